@@ -1,0 +1,45 @@
+"""The oracle pins have teeth: plant one plausible mistake at a time in a
+temporary copy of the oracle (on the CPU) and check that tests/test_oracle.py
+then fails.  The real oracle is never modified."""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+MUTANTS = {
+    "no_max_subtraction": ("w = np.exp(sc - sc.max())", "w = np.exp(sc)"),
+    "exp2_instead_of_exp": ("w = np.exp(sc - sc.max())", "w = np.exp2(sc - sc.max())"),
+    "scale_dropped": ("sc = float(scale) * (Kd @ qrow.astype(np.float64))\n    w =",
+                      "sc = (Kd @ qrow.astype(np.float64))\n    w ="),
+    "head_mapping_h_mod_hk": ("for h in range(g * G, (g + 1) * G):", "for h in range(g, H, Hk):"),
+    "int8_scale_group_index": ("s = np.repeat(scales.astype(np.float64), 64, axis=-1)",
+                               "s = np.tile(scales.astype(np.float64), 64)"),
+    "causal_off_by_one": ("Lt = int(seq_len) - (T - 1 - t)", "Lt = int(seq_len) - (T - t)"),
+    "budget_width_ignores_window": ("width = min(Lt, ids_row.shape[0])", "width = ids_row.shape[0]"),
+    "merge_weight_sign": ("np.exp(np.where(np.isfinite(m), m - M, 0.0))",
+                          "np.exp(np.where(np.isfinite(m), M - m, 0.0))"),
+    "merge_denominator_without_l": ("return num / float((e * l).sum())", "return num / float(e.sum())"),
+    "k_operand_reversed": ("sc = float(scale) * (Kd @ qrow.astype(np.float64))\n    w =",
+                           "sc = float(scale) * (Kd[:, ::-1] @ qrow.astype(np.float64))\n    w ="),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path):
+    before, after = MUTANTS[name]
+    src = open(os.path.join(ROOT, "oracle", "decode_ref.py")).read()
+    assert before in src, f"mutation site for {name} no longer exists"
+    shutil.copytree(os.path.join(ROOT, "oracle"), tmp_path / "oracle")
+    shutil.copytree(os.path.join(ROOT, "workloads"), tmp_path / "workloads")
+    (tmp_path / "tests").mkdir()
+    for f in ("conftest.py", "test_oracle.py"):
+        shutil.copy(os.path.join(ROOT, "tests", f), tmp_path / "tests" / f)
+    (tmp_path / "oracle" / "decode_ref.py").write_text(src.replace(before, after, 1))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        "tests/test_oracle.py"], cwd=tmp_path, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 1, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"

@@ -1,0 +1,206 @@
+"""Seeded synthetic inputs for split-KV GQA decode attention.
+
+This module only draws random tensors of the right shapes and value
+distributions; it holds none of the attention arithmetic.  Both the fp64
+oracle's tests and the GPU path's tests/bench take their inputs from here, so
+the two sides always see bit-identical data.
+
+Layouts (all C-contiguous numpy arrays):
+  q          [S][T][H][D]        float32
+  k, v       [S][Lmax][Hk][D]    float16  (kv="f16")  or  int8 (kv="i8")
+  k_scales,  [S][Lmax][Hk][D/64] float16  (kv="i8" only: one scale per 64
+  v_scales                                  consecutive elements of a row)
+  ids        [S][T][B]           int32    (optional budget of cell ids)
+  seq_lens   [S]                 int32    cells visible to the LAST query
+                                          token of each sequence
+
+The named workloads follow the decode shapes the source pages run their
+kernels on: the f16 GQA decode of the cera shaders (group 4, head_dim 64 and
+128), the int8 QSA decode of qsa2.metal (12 query heads per KV head,
+head_dim 256, one f16 scale per 64 elements, scale 1/16, a budget of 2048
+cell ids), and the causal multi-query window of flash_attention_tq.metal.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+
+__all__ = ["Workload", "WORKLOADS", "WORKLOAD_ORDER", "make_inputs", "make_case",
+           "Inputs", "kv_bytes"]
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    index: int            # position in the canonical list; seeds SeedSequence(1000 + index)
+    S: int
+    T: int
+    H: int
+    Hk: int
+    D: int
+    Lmax: int
+    kv: str               # "f16" or "i8"
+    scale: float
+    chunk: int            # cells per split; 0 = library's automatic choice
+    lens: str             # "full" (every sequence at Lmax) or "uniform:lo:hi" (inclusive)
+    budget: int = 0       # B; 0 = dense (no ids)
+    description: str = ""
+
+
+WORKLOADS = {
+    w.name: w for w in [
+        Workload("tiny_f16", 0, S=1, T=1, H=8, Hk=2, D=64, Lmax=256, kv="f16",
+                 scale=1.0 / 8.0, chunk=32, lens="full",
+                 description="tiny f16 decode: 1 seq, 8 heads / 2 KV heads, hd 64, 256 cells, 32-cell chunks"),
+        Workload("f16_batch", 1, S=32, T=1, H=32, Hk=8, D=128, Lmax=4096, kv="f16",
+                 scale=1.0 / math.sqrt(128.0), chunk=0, lens="uniform:512:4096",
+                 description="f16 GQA decode batch: 32 seqs, lengths U[512,4096], 32/8 heads, hd 128"),
+        Workload("i8_32k", 2, S=8, T=1, H=24, Hk=2, D=256, Lmax=32768, kv="i8",
+                 scale=1.0 / 16.0, chunk=0, lens="full",
+                 description="int8 KV decode: 8 seqs at context 32768, 24/2 heads (group 12), hd 256"),
+        Workload("i8_budget", 3, S=8, T=1, H=24, Hk=2, D=256, Lmax=65536, kv="i8",
+                 scale=1.0 / 16.0, chunk=32, lens="full", budget=2048,
+                 description="budgeted sparse int8 decode: context 65536, 2048 distinct ids per token, 32-cell chunks"),
+        Workload("f16_mq_causal", 4, S=4, T=8, H=32, Hk=8, D=128, Lmax=131072, kv="f16",
+                 scale=1.0 / math.sqrt(128.0), chunk=0, lens="full",
+                 description="multi-query causal chunk: 4 seqs x 8 tokens at start 131064, context 131072, 32/8 heads, hd 128"),
+    ]
+}
+WORKLOAD_ORDER = sorted(WORKLOADS, key=lambda n: WORKLOADS[n].index)
+
+
+@dataclasses.dataclass
+class Inputs:
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    seq_lens: np.ndarray
+    scale: float
+    k_scales: Optional[np.ndarray] = None
+    v_scales: Optional[np.ndarray] = None
+    ids: Optional[np.ndarray] = None
+
+    @property
+    def kv(self) -> str:
+        return "i8" if self.k.dtype == np.int8 else "f16"
+
+    @property
+    def shape(self):
+        S, T, H, D = self.q.shape
+        _, Lmax, Hk, _ = self.k.shape
+        B = 0 if self.ids is None else self.ids.shape[2]
+        return dict(S=S, T=T, H=H, Hk=Hk, D=D, Lmax=Lmax, B=B)
+
+
+def _normal_f16(rng: np.random.Generator, shape) -> np.ndarray:
+    # Draw fp32 N(0,1), then round to binary16 (round-to-nearest-even).
+    out = np.empty(shape, dtype=np.float16)
+    flat = out.reshape(-1)
+    step = 1 << 24
+    for i in range(0, flat.size, step):
+        n = min(step, flat.size - i)
+        flat[i:i + n] = rng.standard_normal(n, dtype=np.float32).astype(np.float16)
+    return out
+
+
+def _int8_uniform(rng: np.random.Generator, shape) -> np.ndarray:
+    # Uniform integers in [-127, 127] inclusive (the symmetric int8 code range).
+    return rng.integers(-127, 128, size=shape, dtype=np.int8)
+
+
+def _scales_f16(rng: np.random.Generator, shape) -> np.ndarray:
+    return rng.uniform(0.005, 0.02, size=shape).astype(np.float16)
+
+
+def make_case(S: int, T: int, H: int, Hk: int, D: int, Lmax: int, seq_lens,
+              kv: str = "f16", scale: Optional[float] = None, budget: int = 0,
+              seed: int = 0, sort_ids: bool = True) -> Inputs:
+    """Seeded inputs for an arbitrary shape.
+
+    `seq_lens` is a sequence of S ints (cells visible to the last query token).
+    With `budget` B > 0, token t of sequence s gets min(L_t, B) distinct ids
+    drawn uniformly without replacement from [0, L_t) (L_t is the causal
+    window of that token, clamped to [0, Lmax]); the remaining entries are
+    padded with 0 and never read.
+    """
+    if kv not in ("f16", "i8"):
+        raise ValueError("kv must be 'f16' or 'i8'")
+    if kv == "i8" and D % 64:
+        raise ValueError("int8 rows need head_dim % 64 == 0")
+    seq_lens = np.asarray(seq_lens, dtype=np.int32).reshape(S)
+    ss = np.random.SeedSequence(seed)
+    rq, rk, rv, rks, rvs, rid = [np.random.default_rng(c) for c in ss.spawn(6)]
+    q = rq.standard_normal((S, T, H, D), dtype=np.float32)
+    if kv == "f16":
+        k = _normal_f16(rk, (S, Lmax, Hk, D))
+        v = _normal_f16(rv, (S, Lmax, Hk, D))
+        ks = vs = None
+    else:
+        k = _int8_uniform(rk, (S, Lmax, Hk, D))
+        v = _int8_uniform(rv, (S, Lmax, Hk, D))
+        ks = _scales_f16(rks, (S, Lmax, Hk, D // 64))
+        vs = _scales_f16(rvs, (S, Lmax, Hk, D // 64))
+    ids = None
+    if budget > 0:
+        ids = np.zeros((S, T, budget), dtype=np.int32)
+        for s in range(S):
+            for t in range(T):
+                Lt = int(seq_lens[s]) - (T - 1 - t)
+                Lt = max(0, min(Lt, Lmax))
+                w = min(Lt, budget)
+                if w == 0:
+                    continue
+                sel = rid.choice(Lt, size=w, replace=False).astype(np.int32)
+                if sort_ids:
+                    sel.sort()
+                ids[s, t, :w] = sel
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    return Inputs(q=q, k=k, v=v, seq_lens=seq_lens, scale=float(scale),
+                  k_scales=ks, v_scales=vs, ids=ids)
+
+
+def workload_seq_lens(w: Workload, seed_seq: np.random.SeedSequence) -> np.ndarray:
+    if w.lens == "full":
+        return np.full(w.S, w.Lmax, dtype=np.int32)
+    kind, lo, hi = w.lens.split(":")
+    assert kind == "uniform"
+    rng = np.random.default_rng(seed_seq)
+    return rng.integers(int(lo), int(hi) + 1, size=w.S).astype(np.int32)
+
+
+def make_inputs(name: str, sort_ids: bool = True) -> Inputs:
+    """Full-size seeded inputs of a named workload (SeedSequence(1000 + index))."""
+    w = WORKLOADS[name]
+    root = np.random.SeedSequence(1000 + w.index)
+    c_lens, c_rest = root.spawn(2)
+    lens = workload_seq_lens(w, c_lens)
+    seed = int(c_rest.generate_state(1)[0])
+    return make_case(w.S, w.T, w.H, w.Hk, w.D, w.Lmax, lens, kv=w.kv, scale=w.scale,
+                     budget=w.budget, seed=seed, sort_ids=sort_ids)
+
+
+def kv_bytes(inp: Inputs) -> int:
+    """Algorithmic bytes one decode step must read: K + V (+ int8 scales) rows of
+    every visible cell, once per KV head and sequence (shared by all query
+    heads of the group and all query tokens of a dense window), plus the ids.
+    q, the output and the split partials are not counted."""
+    sh = inp.shape
+    S, T, Hk, D, Lmax, B = sh["S"], sh["T"], sh["Hk"], sh["D"], sh["Lmax"], sh["B"]
+    row = D * inp.k.itemsize
+    if inp.kv == "i8":
+        row += (D // 64) * 2
+    total = 0
+    for s in range(S):
+        if B == 0:
+            cells = max(0, min(int(inp.seq_lens[s]), Lmax))
+            total += 2 * row * Hk * cells
+        else:
+            for t in range(T):
+                Lt = max(0, min(int(inp.seq_lens[s]) - (T - 1 - t), Lmax))
+                w = min(Lt, B)
+                total += 2 * row * Hk * w + 4 * w
+    return total
