@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--chunk C]
+
+A step is one decode step of the whole path: the chunk kernel
+(gqa_decode_attn_*) and the merge kernel (gqa_decode_merge) over one batch of
+seeded synthetic inputs already resident in HBM.  The default workload is the
+int8 decode at context 32768 (8 sequences, 24 query / 2 KV heads, head_dim
+256), the configuration the >= 70 % HBM-roofline goal is set on.
+
+Reported (one JSON line on stdout):
+  value        effective KV GB/s of the whole step = algorithmic KV bytes per
+               step / wall-clock seconds per step (K steps back to back,
+               bracketed by device synchronisation)
+  ms_per_step  wall-clock milliseconds per step
+  roofline     the chunk kernel alone: algorithmic bytes per launch / its
+               mean duration from HIP events on its stream, against the
+               8 TB/s HBM peak; `traffic` is HBM bytes per launch measured
+               with rocprofv3 counters (from profiles/, null when the kernel
+               source changed since they were taken)
+  cpu_baseline the fp64 oracle on the host cores over a bounded sample
+To keep back-to-back steps from hitting the 256 MB last-level cache, the
+inputs are replicated and the steps rotate through the copies, so every step
+reads K/V that were last touched several hundred MB earlier.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+LLC_BYTES = 256 << 20
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "decode_attention_kv_gqa_amd", "csrc")
+    for fn in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, fn), "rb") as f:
+            h.update(fn.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM bytes per chunk-kernel launch measured with rocprofv3 counters,
+    if they were taken on the current kernel source."""
+    path = os.path.join(PROFILES, f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, budget_s: float = 12.0):
+    """The fp64 oracle, as it stands, on the host cores: whole decode steps of
+    the workload, or the first sequences of one when a step would take too
+    long, repeated until about `budget_s` seconds of work."""
+    import numpy as np
+    from oracle.decode_ref import gqa_decode_ref
+    from workloads import Inputs, kv_bytes
+    threads = os.cpu_count()
+    try:
+        from threadpoolctl import threadpool_info
+        info = [x for x in threadpool_info() if x.get("user_api") == "blas"]
+        if info:
+            threads = int(info[0]["num_threads"])
+    except Exception:
+        pass
+
+    def sub(nseq):
+        sl = slice(0, nseq)
+        f = lambda x: None if x is None else x[sl]
+        return Inputs(q=inp.q[sl], k=inp.k[sl], v=inp.v[sl], seq_lens=inp.seq_lens[sl],
+                      scale=inp.scale, k_scales=f(inp.k_scales), v_scales=f(inp.v_scales),
+                      ids=f(inp.ids))
+
+    def run(x):
+        t0 = time.perf_counter()
+        gqa_decode_ref(x.q, x.k, x.v, x.seq_lens, x.scale, x.k_scales, x.v_scales, x.ids)
+        return time.perf_counter() - t0
+
+    S = inp.q.shape[0]
+    one = sub(1)
+    t1 = run(one)
+    nseq = max(1, min(S, int(budget_s / max(t1, 1e-6))))
+    x = sub(nseq)
+    total_t, total_b, reps = 0.0, 0, 0
+    while total_t < budget_s or reps == 0:
+        total_t += run(x)
+        total_b += kv_bytes(x)
+        reps += 1
+        if total_t > 3 * budget_s:
+            break
+    return {"value": round(total_b / total_t / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{reps} run(s) of the fp64 oracle over the first {nseq} of {S} sequences "
+                      f"({total_b} KV bytes, {total_t:.1f} s); numpy + OpenBLAS"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="i8_32k")
+    ap.add_argument("--chunk", type=int, default=-1, help="cells per split (-1: the workload's)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copies", type=int, default=0, help="input replicas to rotate through")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the decode-attention path here is a single-GPU "
+              "kernel pair (multi-GPU sharding is a design note, not built); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import decode_attention_kv_gqa_amd as gq
+    from workloads import WORKLOADS, make_inputs, kv_bytes
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    w = WORKLOADS[args.workload]
+    chunk = w.chunk if args.chunk < 0 else args.chunk
+    t_gen = time.perf_counter()
+    inp = make_inputs(args.workload)
+    step_bytes = kv_bytes(inp)
+    sh = inp.shape
+    print(f"[bench] {args.workload}: inputs drawn in {time.perf_counter() - t_gen:.1f} s, "
+          f"{step_bytes} KV bytes/step", file=sys.stderr, flush=True)
+
+    # resident footprint of one copy of the inputs
+    foot = sum(x.nbytes for x in (inp.q, inp.k, inp.v, inp.k_scales, inp.v_scales, inp.ids)
+               if x is not None)
+    copies = args.copies or max(2, min(8, math.ceil(3 * LLC_BYTES / foot) + 1))
+    dev = torch.device("cuda:0")
+    d = lambda x: None if x is None else torch.from_numpy(x).to(dev)
+    sets = []
+    for _ in range(copies):
+        sets.append(dict(q=d(inp.q), k=d(inp.k), v=d(inp.v), seq_lens=d(inp.seq_lens),
+                         k_scales=d(inp.k_scales), v_scales=d(inp.v_scales), ids=d(inp.ids)))
+    step = gq.DecodeAttention(sh["S"], sh["T"], sh["H"], sh["Hk"], sh["D"], sh["Lmax"], inp.kv,
+                              B=sh["B"], chunk=chunk, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def one(i, ev=None):
+        x = sets[i % copies]
+        if ev is not None:
+            ev[0].record(stream)
+        step.attn(x["q"], x["k"], x["v"], x["seq_lens"], inp.scale, x["k_scales"], x["v_scales"],
+                  x["ids"])
+        if ev is not None:
+            ev[1].record(stream)
+        step.merge(x["seq_lens"], x["ids"])
+
+    for i in range(args.warmup):
+        one(i)
+    torch.cuda.synchronize()
+
+    # timed region: K steps back to back, wall clock bracketed by synchronisation
+    K = args.steps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        one(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / K * 1e3
+
+    # chunk-kernel duration from HIP events on the launch stream (separate pass
+    # so the events do not perturb the wall-clock run)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        one(i, evs[i])
+    torch.cuda.synchronize()
+    attn_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    attn_mean_s = float(attn_ms.mean()) / 1e3
+
+    achieved = step_bytes / attn_mean_s / 1e9
+    traffic = load_traffic(args.workload)
+    res = {
+        "metric": "decode-attention effective KV HBM GB/s (% of peak) and us/step, 1 MI355X",
+        "value": round(step_bytes / (wall / K) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "pct_of_hbm_peak": round(100 * step_bytes / (wall / K) / 1e9 / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8" if inp.kv == "i8" else "f16",
+        "data": "synthetic (seeded numpy: q N(0,1) fp32; " +
+                ("K/V int8 U[-127,127], f16 scales U[0.005,0.02])" if inp.kv == "i8"
+                 else "K/V f16 N(0,1))"),
+        "config": {"workload": args.workload, "S": sh["S"], "T": sh["T"], "H": sh["H"],
+                   "Hk": sh["Hk"], "D": sh["D"], "Lmax": sh["Lmax"], "budget": sh["B"],
+                   "kv": inp.kv, "chunk": step.chunk, "kv_bytes_per_step": step_bytes,
+                   "input_copies_rotated": copies, "description": w.description},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "kernel": "attn_chunk",
+                     "kernel_us_mean": round(attn_mean_s * 1e6, 3),
+                     "kernel_us_p10_p90": [round(float(np.percentile(attn_ms, 10)) * 1e3, 3),
+                                           round(float(np.percentile(attn_ms, 90)) * 1e3, 3)]},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the fp64 oracle on the host", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

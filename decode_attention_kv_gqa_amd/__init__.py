@@ -1,0 +1,126 @@
+"""Split-KV flash-decoding of grouped-query attention for MI355X (gfx950).
+
+`decode_attention` runs one decode step through the HIP library
+(libgqa_decode.so): the chunk kernel writes per-split partials and the merge
+kernel combines them.  PyTorch is used only for device memory and the
+current stream; there is no CPU or PyTorch fallback: without the built
+library (or without a GPU) the call raises.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+from . import _lib
+from ._lib import (GqaDecodeError, gqa_decode_attn_f16, gqa_decode_attn_i8, gqa_decode_merge,
+                   gqa_decode_part_bytes, gqa_decode_auto_chunk, strerror)
+
+__all__ = ["decode_attention", "DecodeAttention", "GqaDecodeError", "gqa_decode_attn_f16",
+           "gqa_decode_attn_i8", "gqa_decode_merge", "gqa_decode_part_bytes",
+           "gqa_decode_auto_chunk", "strerror"]
+
+
+def _check(fn, code):
+    if code != 0:
+        raise GqaDecodeError(fn, code)
+
+
+class DecodeAttention:
+    """A planned decode step for fixed shapes: resolves the split size once,
+    owns the partial workspace and output, and enqueues the two kernels on
+    the current torch stream at each call."""
+
+    def __init__(self, S, T, H, Hk, D, Lmax, kv: str, B: int = 0, chunk: int = 0, device="cuda"):
+        import torch
+        self.S, self.T, self.H, self.Hk, self.D, self.Lmax, self.B = S, T, H, Hk, D, Lmax, B
+        self.kv = kv
+        if chunk <= 0:
+            chunk = gqa_decode_auto_chunk(S, T, Lmax, B, H, Hk, D, kv == "i8")
+            if chunk <= 0:
+                raise GqaDecodeError("gqa_decode_auto_chunk", chunk)
+        self.chunk = int(chunk)
+        self.part_bytes = gqa_decode_part_bytes(S, T, Lmax, B, H, D, self.chunk)
+        if self.part_bytes == 0 and Lmax > 0:
+            raise GqaDecodeError("gqa_decode_part_bytes", _lib.GQA_ERR_SHAPE)
+        n = max(1, (self.part_bytes + 3) // 4)
+        self.part = torch.empty(n, dtype=torch.float32, device=device)
+        self.out = torch.empty((S, T, H, D), dtype=torch.float32, device=device)
+
+    def attn(self, q, k, v, seq_lens, scale, k_scales=None, v_scales=None, ids=None, stream=None):
+        import torch
+        st = torch.cuda.current_stream().cuda_stream if stream is None else stream
+        B = self.B if ids is not None else 0
+        if self.kv == "i8":
+            rc = gqa_decode_attn_i8(q.data_ptr(), k.data_ptr(), v.data_ptr(), k_scales.data_ptr(),
+                                    v_scales.data_ptr(), None if ids is None else ids.data_ptr(),
+                                    seq_lens.data_ptr(), self.part.data_ptr(), self.part_bytes,
+                                    self.S, self.T, self.Lmax, B, self.H, self.Hk, self.D,
+                                    float(scale), self.chunk, st)
+            _check("gqa_decode_attn_i8", rc)
+        else:
+            rc = gqa_decode_attn_f16(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                     None if ids is None else ids.data_ptr(), seq_lens.data_ptr(),
+                                     self.part.data_ptr(), self.part_bytes, self.S, self.T,
+                                     self.Lmax, B, self.H, self.Hk, self.D, float(scale),
+                                     self.chunk, st)
+            _check("gqa_decode_attn_f16", rc)
+
+    def merge(self, seq_lens, ids=None, stream=None):
+        import torch
+        st = torch.cuda.current_stream().cuda_stream if stream is None else stream
+        rc = gqa_decode_merge(self.part.data_ptr(), seq_lens.data_ptr(),
+                              None if ids is None else ids.data_ptr(), self.out.data_ptr(),
+                              self.S, self.T, self.Lmax, self.B if ids is not None else 0,
+                              self.H, self.D, self.chunk, st)
+        _check("gqa_decode_merge", rc)
+
+    def __call__(self, q, k, v, seq_lens, scale, k_scales=None, v_scales=None, ids=None):
+        self.attn(q, k, v, seq_lens, scale, k_scales, v_scales, ids)
+        self.merge(seq_lens, ids)
+        return self.out
+
+
+def _validate(q, k, v, seq_lens, k_scales, v_scales, ids):
+    import torch
+    tensors = [("q", q), ("k", k), ("v", v), ("seq_lens", seq_lens)]
+    if k_scales is not None:
+        tensors += [("k_scales", k_scales), ("v_scales", v_scales)]
+    if ids is not None:
+        tensors.append(("ids", ids))
+    for name, t in tensors:
+        if t is None:
+            raise ValueError(f"{name} is required")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor (there is no CPU path)")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if q.dtype != torch.float32:
+        raise ValueError("q must be float32 [S][T][H][D]")
+    if seq_lens.dtype != torch.int32 or (ids is not None and ids.dtype != torch.int32):
+        raise ValueError("seq_lens and ids must be int32")
+    if k.dtype == torch.int8:
+        if k_scales is None or v_scales is None or k_scales.dtype != torch.float16 \
+                or v_scales.dtype != torch.float16:
+            raise ValueError("int8 K/V need float16 k_scales and v_scales [S][Lmax][Hk][D/64]")
+    elif k.dtype != torch.float16:
+        raise ValueError("K/V must be float16 or int8")
+    if v.dtype != k.dtype or v.shape != k.shape:
+        raise ValueError("K and V must share dtype and shape")
+
+
+def decode_attention(q, k, v, seq_lens, scale: Optional[float] = None, *, k_scales=None,
+                     v_scales=None, ids=None, chunk: int = 0):
+    """One decode step.  q [S][T][H][D] float32; k, v [S][Lmax][Hk][D]
+    float16, or int8 with k_scales / v_scales [S][Lmax][Hk][D/64] float16;
+    seq_lens [S] int32 (cells visible to each sequence's last query token);
+    ids None or [S][T][B] int32.  Returns out [S][T][H][D] float32."""
+    _validate(q, k, v, seq_lens, k_scales, v_scales, ids)
+    S, T, H, D = q.shape
+    _, Lmax, Hk, Dk = k.shape
+    if Dk != D or k.shape[0] != S or seq_lens.shape != (S,):
+        raise ValueError("shape mismatch between q, k/v and seq_lens")
+    B = 0 if ids is None else ids.shape[2]
+    if scale is None:
+        scale = D ** -0.5
+    kv = "i8" if str(k.dtype) == "torch.int8" else "f16"
+    step = DecodeAttention(S, T, H, Hk, D, Lmax, kv, B=B, chunk=chunk, device=q.device)
+    return step(q, k, v, seq_lens, scale, k_scales, v_scales, ids).clone()

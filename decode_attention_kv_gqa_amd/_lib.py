@@ -1,0 +1,94 @@
+"""ctypes binding of libgqa_decode.so (include/gqa_decode.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+library.  The functions carry the C names and take raw device pointers
+(ints), sizes and a hipStream_t handle (int, 0 = null stream).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgqa_decode.so")
+
+GQA_OK = 0
+GQA_ERR_NULL = -1
+GQA_ERR_SHAPE = -2
+GQA_ERR_GROUP = -3
+GQA_ERR_HEAD_DIM = -4
+GQA_ERR_BUDGET = -5
+GQA_ERR_CHUNK = -6
+GQA_ERR_WORKSPACE = -7
+
+EXPORTED = ["gqa_decode_attn_f16", "gqa_decode_attn_i8", "gqa_decode_merge",
+            "gqa_decode_part_bytes", "gqa_decode_auto_chunk", "gqa_decode_strerror"]
+
+_lib = None
+
+
+class GqaDecodeError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        self.code = code
+        super().__init__(f"{fn} failed with {code}: {strerror(code)}")
+
+
+def load() -> ctypes.CDLL:
+    """Load the built library; raise if it was never built (there is no
+    fallback implementation)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m decode_attention_kv_gqa_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
+    lib.gqa_decode_attn_f16.argtypes = [vp, vp, vp, vp, vp, vp, sz] + [i32] * 7 + [f32, i32, vp]
+    lib.gqa_decode_attn_f16.restype = i32
+    lib.gqa_decode_attn_i8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz] + [i32] * 7 + [f32, i32, vp]
+    lib.gqa_decode_attn_i8.restype = i32
+    lib.gqa_decode_merge.argtypes = [vp, vp, vp, vp] + [i32] * 7 + [vp]
+    lib.gqa_decode_merge.restype = i32
+    lib.gqa_decode_part_bytes.argtypes = [i32] * 7
+    lib.gqa_decode_part_bytes.restype = sz
+    lib.gqa_decode_auto_chunk.argtypes = [i32] * 8
+    lib.gqa_decode_auto_chunk.restype = i32
+    lib.gqa_decode_strerror.argtypes = [i32]
+    lib.gqa_decode_strerror.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def strerror(code: int) -> str:
+    return load().gqa_decode_strerror(int(code)).decode()
+
+
+def _p(x) -> int | None:
+    return None if x is None or x == 0 else int(x)
+
+
+def gqa_decode_attn_f16(q, k, v, ids, seq_lens, part, part_bytes, S, T, Lmax, B, H, Hk, D,
+                        scale, chunk, stream=0) -> int:
+    return load().gqa_decode_attn_f16(_p(q), _p(k), _p(v), _p(ids), _p(seq_lens), _p(part),
+                                      part_bytes, S, T, Lmax, B, H, Hk, D, scale, chunk, _p(stream))
+
+
+def gqa_decode_attn_i8(q, k, v, k_scales, v_scales, ids, seq_lens, part, part_bytes, S, T, Lmax,
+                       B, H, Hk, D, scale, chunk, stream=0) -> int:
+    return load().gqa_decode_attn_i8(_p(q), _p(k), _p(v), _p(k_scales), _p(v_scales), _p(ids),
+                                     _p(seq_lens), _p(part), part_bytes, S, T, Lmax, B, H, Hk, D,
+                                     scale, chunk, _p(stream))
+
+
+def gqa_decode_merge(part, seq_lens, ids_or_null, out, S, T, Lmax, B, H, D, chunk, stream=0) -> int:
+    return load().gqa_decode_merge(_p(part), _p(seq_lens), _p(ids_or_null), _p(out), S, T, Lmax, B,
+                                   H, D, chunk, _p(stream))
+
+
+def gqa_decode_part_bytes(S, T, Lmax, B, H, D, chunk) -> int:
+    return load().gqa_decode_part_bytes(S, T, Lmax, B, H, D, chunk)
+
+
+def gqa_decode_auto_chunk(S, T, Lmax, B, H, Hk, D, kv_is_i8) -> int:
+    return load().gqa_decode_auto_chunk(S, T, Lmax, B, H, Hk, D, int(bool(kv_is_i8)))

@@ -1,0 +1,75 @@
+// Host-side argument checks and launch planning (no HIP calls).
+#include "plan.h"
+
+namespace gqa {
+
+int check_shape(const Shape& s) {
+  if (s.S < 1 || s.T < 1 || s.H < 1 || s.Hk < 1 || s.Lmax < 0) return GQA_ERR_SHAPE;
+  if (s.H % s.Hk != 0) return GQA_ERR_GROUP;
+  if (s.D != 64 && s.D != 128 && s.D != 256) return GQA_ERR_HEAD_DIM;
+  if (s.ids && s.B < 1) return GQA_ERR_BUDGET;
+  // Grid limits: y = Hk * row blocks * (T when gathering), z = S.
+  int64_t y = (int64_t)s.Hk * row_blocks(s) * (s.ids ? s.T : 1);
+  if (y > 65535 || s.S > 65535) return GQA_ERR_SHAPE;
+  return GQA_OK;
+}
+
+// Cells per split.  The grid is S * Hk * row-blocks (* T with ids) units
+// times the split count; aim for about four workgroups per compute unit
+// (256 CUs) so every CU gets equal, overlapping work, with splits of at
+// least 64 cells so the partials (D + 2 floats per query row and split,
+// written once and read once by the merge) stay small next to the K/V
+// rows each split streams.
+int auto_chunk(const Shape& s) {
+  int rc = check_shape(s);
+  if (rc != GQA_OK) return rc;
+  const int64_t kTargetWorkgroups = 1024;
+  const int64_t kMinChunk = 64;
+  int64_t W = width_cap(s);
+  if (W <= 0) return (int)kMinChunk;
+  int64_t units = (int64_t)s.S * s.Hk * row_blocks(s) * (s.ids ? s.T : 1);
+  int64_t chunk = (W * units + kTargetWorkgroups - 1) / kTargetWorkgroups;
+  if (chunk < kMinChunk) chunk = kMinChunk;
+  chunk = (chunk + 63) / 64 * 64;
+  int64_t Wr = (W + 63) / 64 * 64;
+  if (chunk > Wr) chunk = Wr;
+  if (chunk > (1 << 30)) chunk = 1 << 30;
+  return (int)chunk;
+}
+
+size_t part_bytes(const Shape& s, int chunk) {
+  if (chunk < 1 || check_shape(s) != GQA_OK) return 0;
+  int64_t P = num_splits(s, chunk);
+  return (size_t)s.S * s.T * s.H * (size_t)P * (size_t)(s.D + 2) * sizeof(float);
+}
+
+}  // namespace gqa
+
+extern "C" {
+
+size_t gqa_decode_part_bytes(int S, int T, int Lmax, int B, int H, int D, int chunk) {
+  // Hk does not change the workspace size; H is a valid stand-in here.
+  gqa::Shape s{S, T, Lmax, B, H, H, D, B > 0, false};
+  return gqa::part_bytes(s, chunk);
+}
+
+int gqa_decode_auto_chunk(int S, int T, int Lmax, int B, int H, int Hk, int D, int kv_is_i8) {
+  gqa::Shape s{S, T, Lmax, B, H, Hk, D, B > 0, kv_is_i8 != 0};
+  return gqa::auto_chunk(s);
+}
+
+const char* gqa_decode_strerror(int code) {
+  switch (code) {
+    case GQA_OK: return "ok";
+    case GQA_ERR_NULL: return "a required pointer is NULL";
+    case GQA_ERR_SHAPE: return "invalid shape (S, T, H, Hk >= 1, Lmax >= 0, grid within limits)";
+    case GQA_ERR_GROUP: return "n_heads must be a multiple of n_kv_heads";
+    case GQA_ERR_HEAD_DIM: return "head_dim must be 64, 128 or 256";
+    case GQA_ERR_BUDGET: return "ids given with a budget B < 1";
+    case GQA_ERR_CHUNK: return "chunk must be >= 1 (pass the resolved chunk to the merge)";
+    case GQA_ERR_WORKSPACE: return "partial workspace smaller than gqa_decode_part_bytes()";
+    default: return code > 0 ? "HIP launch error (hipError_t)" : "unknown error";
+  }
+}
+
+}  // extern "C"

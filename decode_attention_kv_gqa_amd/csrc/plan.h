@@ -1,0 +1,67 @@
+// Host-side argument checks and launch planning for the decode-attention
+// kernels.  Pure C++ (no HIP calls), so it can be exercised without a GPU.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "gqa_decode.h"
+
+namespace gqa {
+
+// Largest number of query rows one workgroup holds.  A workgroup serves the
+// query rows of one KV head (all G heads of the group, times the T tokens of
+// a dense window), so K/V rows are streamed once for all of them; groups
+// with more rows than this are cut into row blocks that each stream K/V.
+constexpr int kMaxRowsPerBlock = 32;
+
+struct Shape {
+  int S, T, Lmax, B, H, Hk, D;
+  bool ids;   // gather through a budget of cell ids
+  bool i8;    // int8 rows with f16 group scales
+};
+
+// Positions a split can cover: min(B, Lmax) with ids, else Lmax.
+inline int64_t width_cap(const Shape& s) {
+  if (s.ids) return s.B < s.Lmax ? s.B : s.Lmax;
+  return s.Lmax;
+}
+
+inline int64_t num_splits(const Shape& s, int chunk) {
+  int64_t w = width_cap(s);
+  return w <= 0 ? 0 : (w + chunk - 1) / chunk;
+}
+
+// Query rows served by one (sequence, KV head[, token]) unit.
+inline int rows_per_unit(const Shape& s) {
+  int G = s.H / s.Hk;
+  return s.ids ? G : G * s.T;
+}
+
+inline int row_blocks(const Shape& s) {
+  int R = rows_per_unit(s);
+  return (R + kMaxRowsPerBlock - 1) / kMaxRowsPerBlock;
+}
+
+// Rows per block rounded up to the kernel instance (4, 8, 16 or 32).
+inline int block_rows(const Shape& s) {
+  int R = rows_per_unit(s);
+  if (R > kMaxRowsPerBlock) R = kMaxRowsPerBlock;
+  if (R <= 4) return 4;
+  if (R <= 8) return 8;
+  if (R <= 16) return 16;
+  return 32;
+}
+
+int check_shape(const Shape& s);               // GQA_OK or GQA_ERR_*
+int auto_chunk(const Shape& s);                // > 0, or GQA_ERR_*
+size_t part_bytes(const Shape& s, int chunk);  // 0 on bad arguments
+
+// Offsets (in floats) of the two regions of the partial workspace:
+//   o  [S][T][H][P][D]   unnormalised outputs
+//   ml [S][T][H][P][2]   running max (base-2 domain) and running sum
+inline size_t part_o_floats(const Shape& s, int64_t P) {
+  return (size_t)s.S * s.T * s.H * (size_t)P * s.D;
+}
+
+}  // namespace gqa

@@ -1,0 +1,131 @@
+/*
+ * gqa_decode.h — C ABI of libgqa_decode.so: split-KV flash-decoding of
+ * grouped-query attention over a KV cache on AMD Instinct MI355X (gfx950).
+ *
+ * One decode step is two calls on the same stream:
+ *
+ *   gqa_decode_attn_f16 / gqa_decode_attn_i8   chunk partials (o, m, l)
+ *   gqa_decode_merge                            log-sum-exp merge -> out
+ *
+ * What is computed, for sequence s, query token t and query head h
+ * (G = H / Hk query heads share KV head g = h / G):
+ *
+ *   L_t   = clamp(seq_lens[s] - (T - 1 - t), 0, Lmax)
+ *   cells = [0, L_t)                      when ids == NULL
+ *         = ids[s][t][0 .. min(L_t, B))   otherwise
+ *   K[c]  = k[s][c][g][:]                 (f16)
+ *         = int8 k[s][c][g][d] * f16 k_scales[s][c][g][d / 64]   (int8)
+ *   out[s][t][h][:] = sum_c softmax_c(scale * q[s][t][h][:] . K[c]) V[c]
+ *   out[s][t][h][:] = 0 when `cells` is empty.
+ *
+ * Sources: the GQA head mapping and the whole-group workgroup that reads
+ * K/V once come from cera's attention_gqa.metal (header and Phase 1); the
+ * chunk partials with a chunk-local softmax and their log-sum-exp merge from
+ * qsa2.metal (qsa_attn2, qsa_merge2); the int8 row format with one f16
+ * scale per 64 elements and the budget of cell ids (width = min(n_kv,
+ * budget)) from qsa2.metal (qsa_attn2, qsa_attn3); the per-token causal
+ * window that bad parameters can only truncate from cera's
+ * flash_attention_tq.metal (flash_attention_tq); the online softmax and
+ * the zero output of an empty window from cera's flash_attention.metal
+ * (flash_attention_impl).
+ *
+ * Conventions for every call:
+ *  - Array arguments are DEVICE pointers to C-contiguous arrays owned by the
+ *    caller; the library never frees, keeps or allocates memory on these
+ *    paths and holds no state between calls.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream);
+ *    the library never synchronises.  The merge must be enqueued after the
+ *    attention call whose workspace it reads (same stream, or an event).
+ *  - Return 0 on success; a negative GQA_ERR_* code when the arguments are
+ *    rejected on the host, in which case nothing was enqueued; a positive
+ *    hipError_t when a launch failed.  gqa_decode_strerror() names codes.
+ *  - Device-side preconditions that are not checked: seq_lens[s] >= 0 is not
+ *    required (negative counts clamp to an empty window); ids must be
+ *    distinct cells of the token's window [0, L_t).  An id outside [0, Lmax)
+ *    is clamped into range, so a bad id yields a wrong row, never an
+ *    out-of-bounds read.
+ */
+#ifndef GQA_DECODE_H
+#define GQA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  GQA_OK = 0,
+  GQA_ERR_NULL = -1,       /* a required pointer is NULL                         */
+  GQA_ERR_SHAPE = -2,      /* S, T, H, Hk < 1, Lmax < 0, or sizes overflow       */
+  GQA_ERR_GROUP = -3,      /* H % Hk != 0                                        */
+  GQA_ERR_HEAD_DIM = -4,   /* D not in {64, 128, 256}                            */
+  GQA_ERR_BUDGET = -5,     /* ids given with B < 1                               */
+  GQA_ERR_CHUNK = -6,      /* merge called with chunk < 1 (pass the resolved one)*/
+  GQA_ERR_WORKSPACE = -7   /* part_bytes < gqa_decode_part_bytes(...)            */
+};
+
+/* Partial workspace size in bytes for one attention call: one partial
+ * (D unnormalised output floats + running max + running sum) per query row
+ * and split, splits = ceil(min(B or Lmax, Lmax) / chunk).  `B` is the budget
+ * (0 when no ids are used); `chunk` is the resolved cells-per-split (> 0).
+ * Returns 0 for invalid arguments.  Pure host function. */
+size_t gqa_decode_part_bytes(int S, int T, int Lmax, int B, int H, int D, int chunk);
+
+/* The split size the attention calls use when passed chunk <= 0.  A pure,
+ * deterministic host function of the shapes: it picks the cells per split so
+ * that the grid gives every one of the 256 compute units several
+ * workgroups, while the partials stay a small fraction of the KV bytes.
+ * `kv_is_i8` selects the int8 row size.  Returns a positive chunk, or a
+ * negative GQA_ERR_* code. */
+int gqa_decode_auto_chunk(int S, int T, int Lmax, int B, int H, int Hk, int D, int kv_is_i8);
+
+/* Chunk partials over an f16 cache.
+ *   q         [S][T][H][D]       float32
+ *   k, v      [S][Lmax][Hk][D]   IEEE binary16 bit patterns
+ *   ids       NULL (dense causal windows) or [S][T][B] int32 cell ids
+ *   seq_lens  [S] int32: cells visible to the LAST query token of sequence s
+ *   part      workspace of part_bytes >= gqa_decode_part_bytes(S,T,Lmax,B,H,D,chunk')
+ *             where chunk' is the resolved chunk; contents are overwritten
+ *   scale     score scale (typically 1/sqrt(D))
+ *   chunk     cells per split; <= 0 selects gqa_decode_auto_chunk(...)
+ * Errors: GQA_ERR_NULL, _SHAPE, _GROUP, _HEAD_DIM, _BUDGET, _WORKSPACE. */
+int gqa_decode_attn_f16(const float *q, const uint16_t *k, const uint16_t *v,
+                        const int32_t *ids, const int32_t *seq_lens,
+                        float *part, size_t part_bytes,
+                        int S, int T, int Lmax, int B, int H, int Hk, int D,
+                        float scale, int chunk, void *stream);
+
+/* Chunk partials over an int8 cache with one f16 scale per 64 elements.
+ *   k, v                [S][Lmax][Hk][D]      int8 codes
+ *   k_scales, v_scales  [S][Lmax][Hk][D/64]   binary16 bit patterns
+ * Element value = float(int8) * float(scale of its 64-element group), which
+ * is exact in fp32.  Other arguments as gqa_decode_attn_f16. */
+int gqa_decode_attn_i8(const float *q, const int8_t *k, const int8_t *v,
+                       const uint16_t *k_scales, const uint16_t *v_scales,
+                       const int32_t *ids, const int32_t *seq_lens,
+                       float *part, size_t part_bytes,
+                       int S, int T, int Lmax, int B, int H, int Hk, int D,
+                       float scale, int chunk, void *stream);
+
+/* Log-sum-exp merge of the partials written by the attention call with the
+ * same S, T, Lmax, B, H, D and the same RESOLVED chunk (> 0).
+ *   part          workspace written by gqa_decode_attn_*
+ *   seq_lens      [S] int32, as passed to the attention call
+ *   ids_or_null   the attention call's ids pointer (only its NULL-ness is
+ *                 used: it selects the width rule min(L_t, B))
+ *   out           [S][T][H][D] float32; rows with an empty window get zeros
+ * Errors: GQA_ERR_NULL, _SHAPE, _HEAD_DIM, _BUDGET, _CHUNK. */
+int gqa_decode_merge(const float *part, const int32_t *seq_lens, const int32_t *ids_or_null,
+                     float *out, int S, int T, int Lmax, int B, int H, int D, int chunk,
+                     void *stream);
+
+/* Static text for a return code. */
+const char *gqa_decode_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_DECODE_H */

@@ -1,0 +1,119 @@
+"""The C-ABI library loads, exports every function include/gqa_decode.h
+declares, and rejects bad arguments on the host before any HIP call (CPU
+only: no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import decode_attention_kv_gqa_amd as gq
+from decode_attention_kv_gqa_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", fn)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names += re.findall(r"\b(gqa_\w+)\s*\(", src)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    names = declared_functions()
+    assert set(_lib.EXPORTED) <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+def test_strerror_covers_codes():
+    for c in range(0, -8, -1):
+        assert gq.strerror(c) not in ("", "unknown error")
+    assert gq.strerror(-99) == "unknown error"
+    assert "HIP" in gq.strerror(98)
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def attn_f16(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, ids=None, seq_lens=FAKE, part=FAKE, part_bytes=1 << 40,
+             S=1, T=1, Lmax=16, B=0, H=8, Hk=2, D=64, scale=0.125, chunk=0, stream=0)
+    a.update(kw)
+    return gq.gqa_decode_attn_f16(a["q"], a["k"], a["v"], a["ids"], a["seq_lens"], a["part"],
+                                  a["part_bytes"], a["S"], a["T"], a["Lmax"], a["B"], a["H"],
+                                  a["Hk"], a["D"], a["scale"], a["chunk"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), _lib.GQA_ERR_NULL),
+    (dict(k=None), _lib.GQA_ERR_NULL),
+    (dict(seq_lens=None), _lib.GQA_ERR_NULL),
+    (dict(part=None), _lib.GQA_ERR_NULL),
+    (dict(S=0), _lib.GQA_ERR_SHAPE),
+    (dict(T=0), _lib.GQA_ERR_SHAPE),
+    (dict(H=0), _lib.GQA_ERR_SHAPE),
+    (dict(Lmax=-1), _lib.GQA_ERR_SHAPE),
+    (dict(S=70000), _lib.GQA_ERR_SHAPE),
+    (dict(H=9), _lib.GQA_ERR_GROUP),
+    (dict(D=96), _lib.GQA_ERR_HEAD_DIM),
+    (dict(D=32), _lib.GQA_ERR_HEAD_DIM),
+    (dict(ids=FAKE, B=0), _lib.GQA_ERR_BUDGET),
+    (dict(part_bytes=16), _lib.GQA_ERR_WORKSPACE),
+    (dict(chunk=1, part_bytes=8 * 16 * 66 * 4 - 1), _lib.GQA_ERR_WORKSPACE),
+])
+def test_attn_f16_rejects(kw, code):
+    assert attn_f16(**kw) == code
+
+
+def test_attn_i8_needs_scales():
+    rc = gq.gqa_decode_attn_i8(FAKE, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, 1 << 40,
+                               1, 1, 16, 0, 8, 2, 64, 0.125, 0, 0)
+    assert rc == _lib.GQA_ERR_NULL
+
+
+def test_merge_rejects():
+    m = gq.gqa_decode_merge
+    assert m(None, FAKE, None, FAKE, 1, 1, 16, 0, 8, 64, 32, 0) == _lib.GQA_ERR_NULL
+    assert m(FAKE, FAKE, None, FAKE, 1, 1, 16, 0, 8, 64, 0, 0) == _lib.GQA_ERR_CHUNK
+    assert m(FAKE, FAKE, None, FAKE, 1, 1, 16, 0, 8, 96, 32, 0) == _lib.GQA_ERR_HEAD_DIM
+    assert m(FAKE, FAKE, FAKE, FAKE, 1, 1, 16, 0, 8, 64, 32, 0) == _lib.GQA_ERR_BUDGET
+
+
+def test_part_bytes_formula():
+    # splits = ceil(width / chunk); one (D + 2)-float partial per query row and split
+    assert gq.gqa_decode_part_bytes(8, 1, 32768, 0, 24, 256, 512) == 8 * 24 * 64 * 258 * 4
+    assert gq.gqa_decode_part_bytes(8, 1, 65536, 2048, 24, 256, 32) == 8 * 24 * 64 * 258 * 4
+    assert gq.gqa_decode_part_bytes(1, 1, 100, 0, 8, 64, 32) == 8 * 4 * 66 * 4
+    assert gq.gqa_decode_part_bytes(1, 1, 0, 0, 8, 64, 32) == 0
+    assert gq.gqa_decode_part_bytes(1, 1, 100, 0, 8, 64, 0) == 0
+
+
+def test_auto_chunk_plan():
+    ac = gq.gqa_decode_auto_chunk
+    # deterministic, positive, multiple of 64, never wider than the (rounded) window
+    for args in [(8, 1, 32768, 0, 24, 2, 256, 1), (4, 8, 131072, 0, 32, 8, 128, 0),
+                 (32, 1, 4096, 0, 32, 8, 128, 0), (1, 1, 256, 0, 8, 2, 64, 0),
+                 (8, 1, 65536, 2048, 24, 2, 256, 1), (1, 1, 0, 0, 8, 2, 64, 0)]:
+        c = ac(*args)
+        assert c > 0 and c % 64 == 0 and c == ac(*args)
+        S, T, Lmax, B = args[:4]
+        w = min(B, Lmax) if B else Lmax
+        assert c <= max(64, (w + 63) // 64 * 64)
+    # the 32K int8 decode gets ~1024 workgroups: 8 seqs x 2 KV heads x 64 splits
+    assert ac(8, 1, 32768, 0, 24, 2, 256, 1) == 512
+    assert ac(8, 1, 32768, 0, 25, 2, 256, 1) == _lib.GQA_ERR_GROUP
+
+
+def test_python_wrapper_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 8, 64)
+    k = torch.zeros(1, 4, 2, 64, dtype=torch.float16)
+    with pytest.raises(ValueError, match="GPU"):
+        gq.decode_attention(q, k, k, torch.ones(1, dtype=torch.int32))

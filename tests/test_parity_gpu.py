@@ -1,0 +1,193 @@
+"""GPU parity: the HIP library (through the C ABI) against the fp64 oracle on
+identical seeded inputs.  Bar: max |gpu - oracle| <= 2e-3 and row-relative
+max error <= 1e-3 (tests/conftest.py).  Small cases compare every output
+element; the full-size workloads run in the same launch configuration the
+bench times and compare sampled output rows (or whole KV-head slabs) that
+the oracle computes one by one."""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+from conftest import assert_parity
+from oracle import decode_ref as R
+from workloads import make_case, make_inputs, WORKLOADS
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import decode_attention_kv_gqa_amd  # noqa: F401  (raises if the library is missing)
+
+
+def to_dev(inp):
+    d = lambda x: None if x is None else torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    return dict(q=d(inp.q), k=d(inp.k), v=d(inp.v), seq_lens=d(inp.seq_lens),
+                k_scales=d(inp.k_scales), v_scales=d(inp.v_scales), ids=d(inp.ids))
+
+
+def run_gpu(inp, chunk=0, dev=None):
+    import decode_attention_kv_gqa_amd as gq
+    dev = dev or to_dev(inp)
+    print(f"[gpu] shape={inp.shape} kv={inp.kv} chunk={chunk}", flush=True)
+    out = gq.decode_attention(dev["q"], dev["k"], dev["v"], dev["seq_lens"], inp.scale,
+                              k_scales=dev["k_scales"], v_scales=dev["v_scales"], ids=dev["ids"],
+                              chunk=chunk)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def oracle(inp):
+    return R.gqa_decode_ref(inp.q, inp.k, inp.v, inp.seq_lens, inp.scale, inp.k_scales,
+                            inp.v_scales, inp.ids)
+
+
+# ---------------------------------------------------------------- golden files
+def test_tiny_workload_matches_golden_and_oracle():
+    from test_golden import load_golden
+    inp = make_inputs("tiny_f16")
+    got = run_gpu(inp, chunk=WORKLOADS["tiny_f16"].chunk)
+    assert_parity(got, load_golden("tiny_f16.txt"), "tiny_f16 vs golden")
+    assert_parity(got, oracle(inp), "tiny_f16 vs oracle")
+
+
+def test_small_i8_ids_causal_matches_golden():
+    from test_golden import load_golden, golden_small_i8_inputs
+    inp = golden_small_i8_inputs()
+    for chunk in (0, 5, 24):
+        got = run_gpu(inp, chunk=chunk)
+        assert_parity(got, load_golden("small_i8_ids_causal.txt"), f"small i8 ids chunk={chunk}")
+        assert not got[1, 0].any()
+
+
+# ---------------------------------------------------------------- edge cases
+@pytest.mark.parametrize("L", [0, 1, 31, 32, 33, 64, 65, 200])
+@pytest.mark.parametrize("kv", ["f16", "i8"])
+def test_lengths_around_chunk_boundaries(L, kv):
+    inp = make_case(2, 1, 8, 2, 128, 256, [L, max(0, L - 1)], kv=kv, seed=100 + L)
+    ref = oracle(inp)
+    for chunk in (32, 0):
+        got = run_gpu(inp, chunk=chunk)
+        assert_parity(got, ref, f"L={L} kv={kv} chunk={chunk}")
+        if L == 0:
+            assert not got[0].any()
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("G", [1, 4, 6, 12])
+@pytest.mark.parametrize("kv", ["f16", "i8"])
+def test_head_dims_and_groups(D, G, kv):
+    Hk = 2
+    inp = make_case(2, 1, G * Hk, Hk, D, 300, [300, 137], kv=kv, seed=D * 31 + G)
+    ref = oracle(inp)
+    got = run_gpu(inp, chunk=0)
+    assert_parity(got, ref, f"D={D} G={G} kv={kv}")
+
+
+@pytest.mark.parametrize("chunk", [1, 7, 32, 64, 100, 0])
+def test_chunk_sizes(chunk):
+    inp = make_case(3, 1, 12, 1, 256, 150, [150, 77, 3], kv="i8", seed=7)
+    assert_parity(run_gpu(inp, chunk=chunk), oracle(inp), f"chunk={chunk}")
+
+
+@pytest.mark.parametrize("kv", ["f16", "i8"])
+@pytest.mark.parametrize("T", [2, 8])
+def test_multi_query_causal(kv, T):
+    # seq 1 is shorter than the window: its first tokens see nothing
+    inp = make_case(3, T, 16, 4, 128, 400, [400, 3, 129], kv=kv, seed=T)
+    ref = oracle(inp)
+    for chunk in (32, 0):
+        got = run_gpu(inp, chunk=chunk)
+        assert_parity(got, ref, f"T={T} kv={kv} chunk={chunk}")
+        for t in range(T):
+            # sequence 1 holds 3 cells: token t sees 3 - (T - 1 - t) of them
+            assert got[1, t].any() == (3 - (T - 1 - t) > 0)
+
+
+def test_rows_beyond_one_block():
+    # G * T = 64 query rows per KV head: two row blocks, each streams K/V
+    inp = make_case(2, 8, 16, 2, 128, 300, [300, 190], kv="f16", seed=5)
+    assert_parity(run_gpu(inp, chunk=0), oracle(inp), "64 rows per KV head")
+
+
+@pytest.mark.parametrize("kv", ["f16", "i8"])
+@pytest.mark.parametrize("B,lens", [(64, [500, 40]), (16, [500, 16]), (300, [300, 299])])
+def test_budgeted_ids(kv, B, lens):
+    inp = make_case(2, 1, 12, 2, 128 if kv == "f16" else 256, 512, lens, kv=kv, budget=B, seed=B)
+    ref = oracle(inp)
+    for chunk in (32, 7, 0):
+        assert_parity(run_gpu(inp, chunk=chunk), ref, f"ids B={B} kv={kv} chunk={chunk}")
+
+
+def test_unsorted_ids_and_multi_token_ids():
+    inp = make_case(2, 3, 8, 2, 64, 256, [256, 100], kv="i8", budget=40, seed=9, sort_ids=False)
+    assert_parity(run_gpu(inp, chunk=16), oracle(inp), "unsorted ids, 3 tokens")
+
+
+def test_large_scores_stay_finite():
+    inp = make_case(1, 1, 8, 2, 128, 500, [500], kv="f16", seed=3, scale=4.0)
+    got = run_gpu(inp, chunk=64)
+    assert np.isfinite(got).all()
+    assert_parity(got, oracle(inp), "scale 4")
+
+
+def test_empty_cache_capacity():
+    inp = make_case(2, 2, 8, 2, 64, 0, [0, 5], kv="f16", seed=1)
+    got = run_gpu(inp, chunk=0)
+    assert not got.any()
+
+
+def test_deterministic_and_on_side_stream():
+    import decode_attention_kv_gqa_amd as gq
+    inp = make_case(2, 1, 24, 2, 256, 2000, [2000, 1500], kv="i8", seed=4)
+    dev = to_dev(inp)
+    a = run_gpu(inp, dev=dev)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        b = gq.decode_attention(dev["q"], dev["k"], dev["v"], dev["seq_lens"], inp.scale,
+                                k_scales=dev["k_scales"], v_scales=dev["v_scales"])
+    s.synchronize()
+    assert np.array_equal(a, b.cpu().numpy())
+
+
+def test_errors_do_not_launch():
+    import decode_attention_kv_gqa_amd as gq
+    from decode_attention_kv_gqa_amd import _lib
+    inp = make_case(1, 1, 8, 2, 64, 64, [64], kv="f16", seed=1)
+    dev = to_dev(inp)
+    part = torch.empty(16, device="cuda")
+    rc = gq.gqa_decode_attn_f16(dev["q"].data_ptr(), dev["k"].data_ptr(), dev["v"].data_ptr(), None,
+                                dev["seq_lens"].data_ptr(), part.data_ptr(), 64, 1, 1, 64, 0, 8, 2,
+                                64, 0.125, 32, 0)
+    assert rc == _lib.GQA_ERR_WORKSPACE
+
+
+# ---------------------------------------------------------------- full sizes
+def _sampled_rows(inp, n, seed):
+    S, T, H, _ = inp.q.shape
+    rng = np.random.default_rng(seed)
+    rows = {(int(rng.integers(S)), int(rng.integers(T)), int(rng.integers(H))) for _ in range(n)}
+    rows |= {(S - 1, T - 1, H - 1), (0, 0, 0)}
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("name", ["f16_batch", "i8_32k", "i8_budget", "f16_mq_causal"])
+def test_full_size_workload(name):
+    w = WORKLOADS[name]
+    inp = make_inputs(name)
+    print(f"[gpu] full-size workload {name}", flush=True)
+    chunks = [w.chunk] + ([0] if w.chunk else [])
+    for chunk in chunks:
+        got = run_gpu(inp, chunk=chunk)
+        assert np.isfinite(got).all()
+        rows = _sampled_rows(inp, 24, w.index)
+        ref = R.gqa_decode_ref_rows(inp.q, inp.k, inp.v, inp.seq_lens, inp.scale, rows,
+                                    inp.k_scales, inp.v_scales, inp.ids)
+        g = np.stack([got[s, t, h] for (s, t, h) in rows])
+        assert_parity(g, ref, f"{name} chunk={chunk} sampled rows")
