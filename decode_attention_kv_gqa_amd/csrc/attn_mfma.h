@@ -1,0 +1,531 @@
+// Chunk kernel on the gfx950 matrix cores (v_mfma_f32_16x16x32_f16).
+//
+// One workgroup = one (split, KV head [, row block] [, token], sequence): it
+// holds every query row that reads this KV head (the G heads of the group,
+// times the T tokens of a dense causal window, up to 32 rows), so each K/V
+// row is fetched from HBM exactly once per split (cera, attention_gqa.metal:
+// one threadgroup per KV head for all Q heads of the group).
+//
+// The four waves of the workgroup stream 32-cell tiles independently (wave w
+// takes tiles w, w+4, ...) with their own online-softmax state, and combine
+// at the end through LDS into ONE partial (o unnormalised, m, l) per query
+// row — the chunk partial of qsa2.metal (qsa_attn2), merged later by the
+// log-sum-exp merge (qsa_merge2).
+//
+// Per 32-cell tile and wave:
+//   QK   S^T[cell][row] = K[cell][:] . Q[row][:]   MFMA with A = K straight
+//        from HBM into registers (lane: one cell, 8 dims per k-step), B = the
+//        query rows (registers, loaded once).  q is fp32; it is split into
+//        f16 hi + lo (hi = f16(q), lo = f16(q - hi)) and both halves are
+//        multiplied, so the product keeps ~22 bits of q.  f16 K and int8 K
+//        are exact in f16.  int8 K: one accumulator per 64-element group,
+//        multiplied by that group's f16 scale after the dot (qsa2.metal,
+//        qsa_attn3: raw int8 dot per group, then the scale).
+//   softmax  online, per query row, base 2 (q carries scale * log2 e): the
+//        running max/sum update with a zero correction before the first
+//        visible cell (cera, flash_attention.metal, flash_attention_impl).
+//   PV   O[row][dim] += P[row][cell] V[cell][dim]  MFMA with A = P taken
+//        directly from the QK accumulators (no shuffle: the QK output layout
+//        is the PV input layout up to a fixed permutation of the 32 cells),
+//        B = V read from LDS with ds_read_b64_tr_b16 / _b8, which deliver the
+//        cell-major fragments out of the row-major tile.  P is split hi + lo
+//        like q.  int8 V: the per-(cell, group) scale is folded into P.
+//
+// V tiles are staged per wave in LDS with 16-byte chunks XOR-swizzled per
+// row so that both the row-major writes and the transposed reads are free of
+// bank conflicts.  K, V and the int8 scales of the next tile are loaded into
+// registers while the current tile is computed.
+#pragma once
+
+#include "common.h"
+
+namespace gqa_kern {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+#define GQA_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+// Four int8 (one dword) -> four f16 (two dwords), exact: bias each byte to
+// unsigned (x ^ 0x80 = x + 128), place it as the low mantissa byte of
+// f16 1024 (0x6400 | u = 1024 + u), then subtract 1152.
+__device__ __forceinline__ void i8x4_to_f16(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  const uint32_t u = w ^ 0x80808080u;
+  const half2v bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+  const uint32_t a = __builtin_amdgcn_perm(0x64646464u, u, 0x05010400u);
+  const uint32_t b = __builtin_amdgcn_perm(0x64646464u, u, 0x07030602u);
+  lo = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, a) - bias);
+  hi = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, b) - bias);
+}
+
+__device__ __forceinline__ half8 i8x8_to_half8(uint32_t w0, uint32_t w1) {
+  uint32_t r0, r1, r2, r3;
+  i8x4_to_f16(w0, r0, r1);
+  i8x4_to_f16(w1, r2, r3);
+  const u32x4 r = {r0, r1, r2, r3};
+  return __builtin_bit_cast(half8, r);
+}
+
+__device__ __forceinline__ void split_hi_lo(const float (&x)[8], half8& hi, half8& lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const _Float16 h = (_Float16)x[e];
+    hi[e] = h;
+    lo[e] = (_Float16)(x[e] - (float)h);
+  }
+}
+
+__device__ __forceinline__ f32x4 mfma16(half8 a, half8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+template <int D, bool I8>
+struct TileGeom {
+  static constexpr int ES = I8 ? 1 : 2;      // bytes per element
+  static constexpr int RBY = D * ES;         // bytes per K/V row
+  static constexpr int CH = RBY / 16;        // 16-byte chunks per row
+  static constexpr int NG = D / 64;          // int8 scale groups per row
+  static constexpr int KS = D / 32;          // MFMA k-steps over head_dim
+  static constexpr int NB = D / 16;          // 16-dim output blocks
+  static constexpr int KLD = RBY / 64;       // 16-byte K loads per lane per 16-cell block
+  static constexpr int TC = 32;              // cells per wave tile
+  static constexpr int VLD = TC * RBY / 1024;  // 16-byte V loads per lane per tile
+  static constexpr int RPI = 1024 / RBY;     // V rows per wave-wide load
+  // log2(16 / CH) for CH <= 16 (0 above): aligns the row key with the bank
+  // group of a chunk when rows are narrower than the 256-byte bank period.
+  static constexpr int SH = CH >= 16 ? 0 : (CH == 8 ? 1 : 2);
+  static_assert(RBY >= 64 && RBY <= 512, "row size");
+  // chunk swizzle of row r (bank-conflict-free writes and transposed reads)
+  __device__ static int swz(int r) {
+    if constexpr (I8) {
+      const int key = (r & 7) | (((r >> 4) & 1) << 3);
+      return (key >> SH) & (CH - 1);
+    } else {
+      return ((2 * (r & 7)) >> SH) & (CH - 1);
+    }
+  }
+  __device__ static int lds_off(int r, int c) { return r * RBY + ((c ^ swz(r)) << 4); }
+};
+
+// Dynamic LDS bytes of one workgroup.
+template <int D, bool I8, int NRB>
+struct AttnLds {
+  using G = TileGeom<D, I8>;
+  static constexpr int RB = 16 * NRB;
+  static constexpr int VT = 4 * G::TC * G::RBY;          // per-wave V tiles
+  static constexpr int BUF = 2 * RB * D * 4;             // cross-wave merge buffers
+  static constexpr int MAIN = VT > BUF ? VT : BUF;
+  static constexpr int SC = I8 ? 4 * 2 * G::TC * G::NG * 2 : 0;  // per-wave K/V scales
+  static constexpr int ML = 4 * RB * 2 * 4;              // per-wave (m, l)
+  static constexpr int BYTES = MAIN + SC + ML;
+};
+
+template <int D, bool I8, bool IDS, int NRB>
+__global__ __launch_bounds__(256, 1) void attn_mfma(AttnArgs a) {
+  using G = TileGeom<D, I8>;
+  using L = AttnLds<D, I8, NRB>;
+  constexpr int RB = 16 * NRB;
+  constexpr int TC = G::TC;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int lr = lane & 15, lb = lane >> 4;
+
+  const int p = blockIdx.x;
+  int y = blockIdx.y;
+  const int g = y % a.Hk;
+  y /= a.Hk;
+  const int rbl = y % a.nrb;
+  const int tq = y / a.nrb;
+  const int s = blockIdx.z;
+  const int seq_len = a.seq_lens[s];
+
+  auto width_of = [&](int r) -> int {   // r: row index within the unit
+    if (r >= a.R) return 0;
+    const int t = IDS ? tq : r / a.G;
+    int Lt = seq_len - (a.T - 1 - t);
+    Lt = Lt < 0 ? 0 : (Lt > a.Lmax ? a.Lmax : Lt);
+    if (IDS) Lt = Lt < a.B ? Lt : a.B;
+    return Lt;
+  };
+  auto row_t = [&](int r) -> int { return IDS ? tq : r / a.G; };
+  auto row_h = [&](int r) -> int { return g * a.G + (IDS ? r : r % a.G); };
+
+  const int r0 = rbl * RB;                       // first unit row of this block
+  const int rlast = (a.R - 1 < r0 + RB - 1) ? a.R - 1 : r0 + RB - 1;
+  const int wmax = width_of(rlast);
+  const int64_t c0l = (int64_t)p * a.chunk;
+  if (c0l >= wmax) return;                       // nothing visible here; the merge skips it
+  const int c0 = (int)c0l;
+  const int cend = (int)((c0l + a.chunk < wmax) ? c0l + a.chunk : wmax);
+
+  // ---- query rows as MFMA B operands (hi/lo), loaded once ----
+  half8 qhi[NRB][G::KS], qlo[NRB][G::KS];
+  int lim[NRB];                                  // visible limit of this lane's row
+#pragma unroll
+  for (int k = 0; k < NRB; ++k) {
+    const int r = r0 + 16 * k + lr;
+    const int wr = width_of(r);
+    lim[k] = wr < cend ? wr : cend;
+    const float* qrow = a.q + ((size_t)(s * a.T + row_t(r < a.R ? r : 0)) * a.H +
+                               row_h(r < a.R ? r : 0)) * D;
+#pragma unroll
+    for (int ks = 0; ks < G::KS; ++ks) {
+      // dims of k-step ks held by lane group lb (must match the K loads)
+      const int d0 = I8 ? (64 * (ks >> 1) + 16 * lb + 8 * (ks & 1)) : (32 * ks + 8 * lb);
+      float x[8];
+      if (r < a.R) {
+        const float4 u0 = *reinterpret_cast<const float4*>(qrow + d0);
+        const float4 u1 = *reinterpret_cast<const float4*>(qrow + d0 + 4);
+        x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w;
+        x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] *= a.qscale;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = 0.f;
+      }
+      split_hi_lo(x, qhi[k][ks], qlo[k][ks]);
+    }
+  }
+
+  uint8_t* vt = smem + wave * TC * G::RBY;                       // this wave's V tile
+  uint16_t* scl = reinterpret_cast<uint16_t*>(smem + L::MAIN) + wave * 2 * TC * G::NG;
+  float* mls = reinterpret_cast<float*>(smem + L::MAIN + L::SC);
+
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k);
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v);
+  const size_t seq_row0 = (size_t)s * a.Lmax;
+  const int32_t* idrow = IDS ? a.ids + ((size_t)s * a.T + tq) * a.B : nullptr;
+  auto cell_at = [&](int pos) -> int {          // pos in [c0, cend)
+    int c = pos;
+    if (IDS) {
+      c = idrow[pos];
+      c = c < 0 ? 0 : (c >= a.Lmax ? a.Lmax - 1 : c);
+    }
+    return c;
+  };
+  auto row_index = [&](int cell) -> size_t { return (seq_row0 + cell) * a.Hk + g; };
+
+  struct Regs {
+    u32x4 k[2][G::KLD];
+    u32x4 v[G::VLD];
+    u32x2 sc;
+  };
+
+  auto issue_loads = [&](int ts, Regs& R) {
+    const int last = cend - 1;
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      int pos = ts + 16 * cb + lr;
+      pos = pos < last ? pos : last;
+      const uint8_t* row = kbase + row_index(cell_at(pos)) * G::RBY + 16 * lb;
+#pragma unroll
+      for (int j = 0; j < G::KLD; ++j) R.k[cb][j] = *reinterpret_cast<const u32x4*>(row + 64 * j);
+    }
+#pragma unroll
+    for (int u = 0; u < G::VLD; ++u) {
+      const int rr = u * G::RPI + lane / G::CH;
+      int pos = ts + rr;
+      pos = pos < last ? pos : last;
+      const uint8_t* row = vbase + row_index(cell_at(pos)) * G::RBY;
+      R.v[u] = *reinterpret_cast<const u32x4*>(row + 16 * (lane % G::CH));
+    }
+    if constexpr (I8) {
+      const int rr = lane & 31;
+      int pos = ts + rr;
+      pos = pos < last ? pos : last;
+      const uint16_t* sp = (lane < 32 ? a.ksc : a.vsc) + row_index(cell_at(pos)) * G::NG;
+      if constexpr (G::NG == 4) {
+        R.sc = *reinterpret_cast<const u32x2*>(sp);
+      } else if constexpr (G::NG == 2) {
+        R.sc[0] = *reinterpret_cast<const uint32_t*>(sp);
+      } else {
+        R.sc[0] = *sp;
+      }
+    }
+  };
+
+  auto stage = [&](const Regs& R) {
+#pragma unroll
+    for (int u = 0; u < G::VLD; ++u) {
+      const int rr = u * G::RPI + lane / G::CH;
+      *reinterpret_cast<u32x4*>(vt + G::lds_off(rr, lane % G::CH)) = R.v[u];
+    }
+    if constexpr (I8) {
+      uint16_t* dst = scl + (lane >> 5) * TC * G::NG + (lane & 31) * G::NG;
+      if constexpr (G::NG == 4) {
+        *reinterpret_cast<u32x2*>(dst) = R.sc;
+      } else if constexpr (G::NG == 2) {
+        *reinterpret_cast<uint32_t*>(dst) = R.sc[0];
+      } else {
+        *dst = (uint16_t)R.sc[0];
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  };
+
+  f32x4 O[NRB][G::NB];
+  float m_run[NRB], l_run[NRB];
+#pragma unroll
+  for (int k = 0; k < NRB; ++k) {
+    m_run[k] = -INFINITY;
+    l_run[k] = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < G::NB; ++nb) O[k][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  auto compute = [&](int ts, const Regs& R) {
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // ---- QK: S[cb][k][i] = score of cell ts+16cb+4lb+i for row 16k+lr ----
+    f32x4 S[2][NRB];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+#pragma unroll
+      for (int k = 0; k < NRB; ++k) S[cb][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (!I8) {
+#pragma unroll
+        for (int ks = 0; ks < G::KS; ++ks) {
+          const half8 ka = __builtin_bit_cast(half8, R.k[cb][ks]);
+#pragma unroll
+          for (int k = 0; k < NRB; ++k) {
+            S[cb][k] = mfma16(ka, qhi[k][ks], S[cb][k]);
+            S[cb][k] = mfma16(ka, qlo[k][ks], S[cb][k]);
+          }
+        }
+      } else {
+        // K scales of the four output cells of this lane (cells 16cb+4lb+i)
+        const uint16_t* ks_l = scl + (16 * cb + 4 * lb) * G::NG;
+#pragma unroll
+        for (int gi = 0; gi < G::NG; ++gi) {
+          const half8 k0 = i8x8_to_half8(R.k[cb][gi][0], R.k[cb][gi][1]);
+          const half8 k1 = i8x8_to_half8(R.k[cb][gi][2], R.k[cb][gi][3]);
+#pragma unroll
+          for (int k = 0; k < NRB; ++k) {
+            f32x4 C = f32x4{0.f, 0.f, 0.f, 0.f};
+            C = mfma16(k0, qhi[k][2 * gi], C);
+            C = mfma16(k0, qlo[k][2 * gi], C);
+            C = mfma16(k1, qhi[k][2 * gi + 1], C);
+            C = mfma16(k1, qlo[k][2 * gi + 1], C);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              S[cb][k][i] = fmaf(C[i], h2f(ks_l[i * G::NG + gi]), S[cb][k][i]);
+          }
+        }
+      }
+    }
+
+    // ---- online softmax per query row (this lane: row 16k+lr, 8 cells) ----
+    float pr[NRB][8];
+#pragma unroll
+    for (int k = 0; k < NRB; ++k) {
+      float x[8];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int pos = ts + 16 * cb + 4 * lb + i;
+          const float v = pos < lim[k] ? S[cb][k][i] : -INFINITY;
+          x[4 * cb + i] = v;
+          tmax = fmaxf(tmax, v);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float mold = m_run[k];
+      const float mnew = fmaxf(mold, tmax);
+      const float corr = (mold == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mold - mnew);
+      float psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pe = (x[e] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x[e] - mnew);
+        pr[k][e] = pe;
+        psum += pe;
+      }
+      psum += __shfl_xor(psum, 16, 64);
+      psum += __shfl_xor(psum, 32, 64);
+      l_run[k] = l_run[k] * corr + psum;
+      m_run[k] = mnew;
+      // rescale the accumulator rows 16k+4lb+i by their row's correction
+      if (__any(corr != 1.0f)) {
+        float cf[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cf[i] = __shfl(corr, 4 * lb + i, 64);
+#pragma unroll
+        for (int nb = 0; nb < G::NB; ++nb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) O[k][nb][i] *= cf[i];
+      }
+    }
+
+    // ---- PV ----
+    const int lam = lane & 15;
+    if constexpr (!I8) {
+      half8 phi[NRB], plo[NRB];
+#pragma unroll
+      for (int k = 0; k < NRB; ++k) split_hi_lo(pr[k], phi[k], plo[k]);
+      // ds_read_b64_tr_b16: source lane (j = lam/4, q = lam%4) points at
+      // row cell(j) and dims 16nb + 4q .. +3; result lane i gets 4 cells of dim i.
+      const int j = lam >> 2, q = lam & 3;
+      const int ra = 4 * lb + j, rb2 = 16 + 4 * lb + j;
+#pragma unroll
+      for (int nb = 0; nb < G::NB; ++nb) {
+        const int c = 2 * nb + (q >> 1);
+        const int off = 8 * (q & 1);
+        const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            GQA_LDS(s16x4, vt + G::lds_off(ra, c) + off));
+        const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            GQA_LDS(s16x4, vt + G::lds_off(rb2, c) + off));
+        // whole-vector bit casts only: a bit cast of a single vector element
+        // reads element 0 with this compiler
+        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo4);
+        const u32x2 hi2 = __builtin_bit_cast(u32x2, hi4);
+        const u32x4 w = {lo2[0], lo2[1], hi2[0], hi2[1]};
+        const half8 b = __builtin_bit_cast(half8, w);
+#pragma unroll
+        for (int k = 0; k < NRB; ++k) {
+          O[k][nb] = mfma16(phi[k], b, O[k][nb]);
+          O[k][nb] = mfma16(plo[k], b, O[k][nb]);
+        }
+      }
+    } else {
+      // ds_read_b64_tr_b8: source lane (j = lam/2, h = lam%2) points at row
+      // cell(j) and bytes 16nb + 8h .. +7; result lane i gets 8 cells of dim i.
+      const int j = lam >> 1, h = lam & 1;
+      const int rr = (j < 4) ? 4 * lb + j : 16 + 4 * lb + (j - 4);
+      const uint16_t* vs_l = scl + TC * G::NG;
+#pragma unroll
+      for (int gi = 0; gi < G::NG; ++gi) {
+        half8 phi[NRB], plo[NRB];
+#pragma unroll
+        for (int k = 0; k < NRB; ++k) {
+          float pv[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int cell = (e < 4) ? 4 * lb + e : 16 + 4 * lb + (e - 4);
+            pv[e] = pr[k][e] * h2f(vs_l[cell * G::NG + gi]);
+          }
+          split_hi_lo(pv, phi[k], plo[k]);
+        }
+#pragma unroll
+        for (int nn = 0; nn < 4; ++nn) {
+          const int nb = 4 * gi + nn;
+          const i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              GQA_LDS(i32x2, vt + G::lds_off(rr, nb) + 8 * h));
+          const half8 b = i8x8_to_half8((uint32_t)raw[0], (uint32_t)raw[1]);
+#pragma unroll
+          for (int k = 0; k < NRB; ++k) {
+            O[k][nb] = mfma16(phi[k], b, O[k][nb]);
+            O[k][nb] = mfma16(plo[k], b, O[k][nb]);
+          }
+        }
+      }
+    }
+  };
+
+  // ---- main loop: this wave's tiles, next tile's loads in flight ----
+  {
+    Regs RA, RB2;
+    int ts = c0 + TC * wave;
+    if (ts < cend) issue_loads(ts, RA);
+#pragma unroll 1
+    while (ts < cend) {
+      int tn = ts + 4 * TC;
+      stage(RA);
+      if (tn < cend) issue_loads(tn, RB2);
+      compute(ts, RA);
+      ts = tn;
+      if (ts >= cend) break;
+      tn = ts + 4 * TC;
+      stage(RB2);
+      if (tn < cend) issue_loads(tn, RA);
+      compute(ts, RB2);
+      ts = tn;
+    }
+  }
+
+  // ---- combine the four waves: one partial per query row ----
+  __syncthreads();
+  if (lb == 0) {
+#pragma unroll
+    for (int k = 0; k < NRB; ++k) {
+      mls[(wave * RB + 16 * k + lr) * 2] = m_run[k];
+      mls[(wave * RB + 16 * k + lr) * 2 + 1] = l_run[k];
+    }
+  }
+  __syncthreads();
+  float* buf = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int k = 0; k < NRB; ++k) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * k + 4 * lb + i;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) M = fmaxf(M, mls[(w * RB + row) * 2]);
+      const float ms = mls[(wave * RB + row) * 2];
+      const float f = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+#pragma unroll
+      for (int nb = 0; nb < G::NB; ++nb) O[k][nb][i] *= f;
+    }
+  }
+  if (wave >= 2) {
+    float* b = buf + (wave - 2) * RB * D;
+#pragma unroll
+    for (int k = 0; k < NRB; ++k)
+#pragma unroll
+      for (int nb = 0; nb < G::NB; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) b[(16 * k + 4 * lb + i) * D + 16 * nb + lr] = O[k][nb][i];
+  }
+  __syncthreads();
+  if (wave < 2) {
+    float* b = buf + wave * RB * D;
+#pragma unroll
+    for (int k = 0; k < NRB; ++k)
+#pragma unroll
+      for (int nb = 0; nb < G::NB; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float* x = b + (16 * k + 4 * lb + i) * D + 16 * nb + lr;
+          *x = *x + O[k][nb][i];
+        }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < RB * D / 4; idx += 256) {
+    const int row = idx / (D / 4);
+    const int d4 = idx % (D / 4);
+    const int r = r0 + row;
+    if (r < a.R) {
+      const float4 x0 = *reinterpret_cast<const float4*>(buf + row * D + 4 * d4);
+      const float4 x1 = *reinterpret_cast<const float4*>(buf + RB * D + row * D + 4 * d4);
+      const size_t prow = ((size_t)(s * a.T + row_t(r)) * a.H + row_h(r)) * a.P + p;
+      *reinterpret_cast<float4*>(a.part_o + prow * D + 4 * d4) =
+          make_float4(x0.x + x1.x, x0.y + x1.y, x0.z + x1.z, x0.w + x1.w);
+    }
+  }
+  if (tid < RB && r0 + tid < a.R) {
+    const int row = tid;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, mls[(w * RB + row) * 2]);
+    float Ls = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = mls[(w * RB + row) * 2];
+      if (mw != -INFINITY) Ls += mls[(w * RB + row) * 2 + 1] * __builtin_amdgcn_exp2f(mw - M);
+    }
+    const int r = r0 + row;
+    const size_t prow = ((size_t)(s * a.T + row_t(r)) * a.H + row_h(r)) * a.P + p;
+    a.part_ml[prow * 2] = M;
+    a.part_ml[prow * 2 + 1] = Ls;
+  }
+}
+
+}  // namespace gqa_kern
