@@ -110,6 +110,22 @@ def cpu_baseline(inp, budget_s: float = 12.0):
                       f"({total_b} KV bytes, {total_t:.1f} s); numpy + OpenBLAS"}
 
 
+def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
+    """A plain device-to-device copy of known size: what rocprofv3's
+    FETCH_SIZE / WRITE_SIZE read for it converts their units to bytes."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "reps": reps,
+                      "copy_GBps": round(2 * nbytes / dt / 1e9, 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -119,7 +135,12 @@ def main():
     ap.add_argument("--chunk", type=int, default=-1, help="cells per split (-1: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copies", type=int, default=0, help="input replicas to rotate through")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy 5 times (HBM counter calibration)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the decode-attention path here is a single-GPU "

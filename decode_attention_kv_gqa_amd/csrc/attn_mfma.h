@@ -118,23 +118,32 @@ struct AttnLds {
   using G = TileGeom<D, I8>;
   static constexpr int RB = 16 * NRB;
   static constexpr int VT = 4 * G::TC * G::RBY;          // per-wave V tiles
-  static constexpr int BUF = 2 * RB * D * 4;             // cross-wave merge buffers
+  static constexpr int BUF = 2 * RB * D * 4;             // cross-wave merge buffers (alias VT)
   static constexpr int MAIN = VT > BUF ? VT : BUF;
+  static constexpr int QB = NRB * G::KS * 2 * 64 * 16;   // query B operands, hi and lo
   static constexpr int SC = I8 ? 4 * 2 * G::TC * G::NG * 2 : 0;  // per-wave K/V scales
   static constexpr int ML = 4 * RB * 2 * 4;              // per-wave (m, l)
-  static constexpr int BYTES = MAIN + SC + ML;
+  static constexpr int BYTES = MAIN + QB + SC + ML;
 };
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // raw buffer: stride 0, num_records in bytes; reads past the end return 0
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
 template <int D, bool I8, bool IDS, int NRB>
-__global__ __launch_bounds__(256, 1) void attn_mfma(AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a) {
   using G = TileGeom<D, I8>;
   using L = AttnLds<D, I8, NRB>;
   constexpr int RB = 16 * NRB;
   constexpr int TC = G::TC;
+  constexpr int RBY = G::RBY;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
   const int lr = lane & 15, lb = lane >> 4;
 
   const int p = blockIdx.x;
@@ -164,108 +173,160 @@ __global__ __launch_bounds__(256, 1) void attn_mfma(AttnArgs a) {
   if (c0l >= wmax) return;                       // nothing visible here; the merge skips it
   const int c0 = (int)c0l;
   const int cend = (int)((c0l + a.chunk < wmax) ? c0l + a.chunk : wmax);
+  // Tiles ending at or before lim_lo are fully visible to every real row.
+  const int lim_lo = width_of(r0) < cend ? width_of(r0) : cend;
 
-  // ---- query rows as MFMA B operands (hi/lo), loaded once ----
-  half8 qhi[NRB][G::KS], qlo[NRB][G::KS];
-  int lim[NRB];                                  // visible limit of this lane's row
+  uint8_t* vt = smem + wave * TC * RBY;                       // this wave's V tile
+  u32x4* qlds = reinterpret_cast<u32x4*>(smem + L::MAIN);
+  uint16_t* scl = reinterpret_cast<uint16_t*>(smem + L::MAIN + L::QB) + wave * 2 * TC * G::NG;
+  float* mls = reinterpret_cast<float*>(smem + L::MAIN + L::QB + L::SC);
+
+  // ---- query rows as MFMA B operands (f16 hi + lo), staged once in LDS ----
+  for (int slot = tid; slot < NRB * G::KS * 64; slot += 256) {
+    const int ln = slot & 63, kks = slot >> 6;
+    const int ks = kks % G::KS, k = kks / G::KS;
+    const int lr2 = ln & 15, lb2 = ln >> 4;
+    const int r = r0 + 16 * k + lr2;
+    // dims of k-step ks held by lane group lb2 (must match the K loads)
+    const int d0 = I8 ? (64 * (ks >> 1) + 16 * lb2 + 8 * (ks & 1)) : (32 * ks + 8 * lb2);
+    float x[8];
+    if (r < a.R) {
+      const float* qrow = a.q + ((size_t)(s * a.T + row_t(r)) * a.H + row_h(r)) * D + d0;
+      const float4 u0 = *reinterpret_cast<const float4*>(qrow);
+      const float4 u1 = *reinterpret_cast<const float4*>(qrow + 4);
+      x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w;
+      x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] *= a.qscale;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    }
+    half8 hi, lo;
+    split_hi_lo(x, hi, lo);
+    qlds[(kks * 2 + 0) * 64 + ln] = __builtin_bit_cast(u32x4, hi);
+    qlds[(kks * 2 + 1) * 64 + ln] = __builtin_bit_cast(u32x4, lo);
+  }
+  int lim[NRB];                                  // visible limit of this lane's rows
 #pragma unroll
   for (int k = 0; k < NRB; ++k) {
-    const int r = r0 + 16 * k + lr;
-    const int wr = width_of(r);
+    const int wr = width_of(r0 + 16 * k + lr);
     lim[k] = wr < cend ? wr : cend;
-    const float* qrow = a.q + ((size_t)(s * a.T + row_t(r < a.R ? r : 0)) * a.H +
-                               row_h(r < a.R ? r : 0)) * D;
-#pragma unroll
-    for (int ks = 0; ks < G::KS; ++ks) {
-      // dims of k-step ks held by lane group lb (must match the K loads)
-      const int d0 = I8 ? (64 * (ks >> 1) + 16 * lb + 8 * (ks & 1)) : (32 * ks + 8 * lb);
-      float x[8];
-      if (r < a.R) {
-        const float4 u0 = *reinterpret_cast<const float4*>(qrow + d0);
-        const float4 u1 = *reinterpret_cast<const float4*>(qrow + d0 + 4);
-        x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w;
-        x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] *= a.qscale;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = 0.f;
-      }
-      split_hi_lo(x, qhi[k][ks], qlo[k][ks]);
-    }
   }
 
-  uint8_t* vt = smem + wave * TC * G::RBY;                       // this wave's V tile
-  uint16_t* scl = reinterpret_cast<uint16_t*>(smem + L::MAIN) + wave * 2 * TC * G::NG;
-  float* mls = reinterpret_cast<float*>(smem + L::MAIN + L::SC);
-
-  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k);
-  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v);
-  const size_t seq_row0 = (size_t)s * a.Lmax;
+  // ---- K/V addressing ----
+  // dense: buffer resources based at the first cell of this split, so every
+  // offset is 32-bit and the per-tile offsets are scalars; reads past cend
+  // return zeros (those cells are masked).  ids: per-lane cell rows.
+  const uint32_t rowstride = (uint32_t)a.Hk * RBY;           // bytes between cells of a KV head
+  const size_t first_row = ((size_t)s * a.Lmax + (IDS ? 0 : c0)) * a.Hk + g;
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k) + first_row * RBY;
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v) + first_row * RBY;
+  const uint16_t* ksbase = I8 ? a.ksc + first_row * G::NG : nullptr;
+  const uint16_t* vsbase = I8 ? a.vsc + first_row * G::NG : nullptr;
+  const uint32_t nrec = (uint32_t)(cend - c0) * rowstride;
+  const uint32_t srow = (uint32_t)a.Hk * G::NG * 2;           // scale bytes between cells
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase, nrec);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase, nrec);
+  const __amdgpu_buffer_rsrc_t rks = make_rsrc(ksbase, (uint32_t)(cend - c0) * srow);
+  const __amdgpu_buffer_rsrc_t rvs = make_rsrc(vsbase, (uint32_t)(cend - c0) * srow);
   const int32_t* idrow = IDS ? a.ids + ((size_t)s * a.T + tq) * a.B : nullptr;
-  auto cell_at = [&](int pos) -> int {          // pos in [c0, cend)
-    int c = pos;
-    if (IDS) {
-      c = idrow[pos];
-      c = c < 0 ? 0 : (c >= a.Lmax ? a.Lmax - 1 : c);
-    }
-    return c;
+  auto cell_at = [&](int pos) -> int {          // ids mode; pos clamped into [c0, cend)
+    pos = pos < cend - 1 ? pos : cend - 1;
+    int c = idrow[pos];
+    return c < 0 ? 0 : (c >= a.Lmax ? a.Lmax - 1 : c);
   };
-  auto row_index = [&](int cell) -> size_t { return (seq_row0 + cell) * a.Hk + g; };
 
-  struct Regs {
+  struct KRegs {
     u32x4 k[2][G::KLD];
+  };
+  struct VRegs {
     u32x4 v[G::VLD];
-    u32x2 sc;
+    u32x2 ks, vs;
   };
 
-  auto issue_loads = [&](int ts, Regs& R) {
-    const int last = cend - 1;
+  auto issue_k = [&](int ts, KRegs& R) {
+    if constexpr (!IDS) {
+      const uint32_t t0 = (uint32_t)(ts - c0);
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      int pos = ts + 16 * cb + lr;
-      pos = pos < last ? pos : last;
-      const uint8_t* row = kbase + row_index(cell_at(pos)) * G::RBY + 16 * lb;
+      for (int cb = 0; cb < 2; ++cb) {
+        const uint32_t so = (t0 + 16 * cb) * rowstride;
+        const uint32_t vo = lr * rowstride + 16 * lb;
 #pragma unroll
-      for (int j = 0; j < G::KLD; ++j) R.k[cb][j] = *reinterpret_cast<const u32x4*>(row + 64 * j);
-    }
+        for (int j = 0; j < G::KLD; ++j)
+          R.k[cb][j] = __builtin_amdgcn_raw_buffer_load_b128(rk, vo + 64 * j, so, 0);
+      }
+    } else {
 #pragma unroll
-    for (int u = 0; u < G::VLD; ++u) {
-      const int rr = u * G::RPI + lane / G::CH;
-      int pos = ts + rr;
-      pos = pos < last ? pos : last;
-      const uint8_t* row = vbase + row_index(cell_at(pos)) * G::RBY;
-      R.v[u] = *reinterpret_cast<const u32x4*>(row + 16 * (lane % G::CH));
-    }
-    if constexpr (I8) {
-      const int rr = lane & 31;
-      int pos = ts + rr;
-      pos = pos < last ? pos : last;
-      const uint16_t* sp = (lane < 32 ? a.ksc : a.vsc) + row_index(cell_at(pos)) * G::NG;
-      if constexpr (G::NG == 4) {
-        R.sc = *reinterpret_cast<const u32x2*>(sp);
-      } else if constexpr (G::NG == 2) {
-        R.sc[0] = *reinterpret_cast<const uint32_t*>(sp);
-      } else {
-        R.sc[0] = *sp;
+      for (int cb = 0; cb < 2; ++cb) {
+        const uint8_t* row = kbase + (size_t)cell_at(ts + 16 * cb + lr) * rowstride + 16 * lb;
+#pragma unroll
+        for (int j = 0; j < G::KLD; ++j) R.k[cb][j] = *reinterpret_cast<const u32x4*>(row + 64 * j);
       }
     }
   };
 
-  auto stage = [&](const Regs& R) {
+  auto issue_v = [&](int ts, VRegs& R) {
+    if constexpr (!IDS) {
+      const uint32_t t0 = (uint32_t)(ts - c0);
+#pragma unroll
+      for (int u = 0; u < G::VLD; ++u) {
+        const uint32_t so = (t0 + u * G::RPI) * rowstride;
+        const uint32_t vo = (lane / G::CH) * rowstride + 16 * (lane % G::CH);
+        R.v[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, vo, so, 0);
+      }
+      if constexpr (I8) {
+        const uint32_t so = t0 * srow;
+        const uint32_t vo = (lane & 31) * srow;
+        if constexpr (G::NG == 4) {
+          R.ks = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rks, vo, so, 0));
+          R.vs = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rvs, vo, so, 0));
+        } else if constexpr (G::NG == 2) {
+          R.ks[0] = __builtin_amdgcn_raw_buffer_load_b32(rks, vo, so, 0);
+          R.vs[0] = __builtin_amdgcn_raw_buffer_load_b32(rvs, vo, so, 0);
+        } else {
+          R.ks[0] = __builtin_amdgcn_raw_buffer_load_b16(rks, vo, so, 0);
+          R.vs[0] = __builtin_amdgcn_raw_buffer_load_b16(rvs, vo, so, 0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < G::VLD; ++u) {
+        const uint8_t* row = vbase + (size_t)cell_at(ts + u * G::RPI + lane / G::CH) * rowstride;
+        R.v[u] = *reinterpret_cast<const u32x4*>(row + 16 * (lane % G::CH));
+      }
+      if constexpr (I8) {
+        const size_t c = (size_t)cell_at(ts + (lane & 31)) * (a.Hk * G::NG);
+        if constexpr (G::NG == 4) {
+          R.ks = *reinterpret_cast<const u32x2*>(ksbase + c);
+          R.vs = *reinterpret_cast<const u32x2*>(vsbase + c);
+        } else if constexpr (G::NG == 2) {
+          R.ks[0] = *reinterpret_cast<const uint32_t*>(ksbase + c);
+          R.vs[0] = *reinterpret_cast<const uint32_t*>(vsbase + c);
+        } else {
+          R.ks[0] = ksbase[c];
+          R.vs[0] = vsbase[c];
+        }
+      }
+    }
+  };
+
+  auto stage = [&](const VRegs& R) {
 #pragma unroll
     for (int u = 0; u < G::VLD; ++u) {
       const int rr = u * G::RPI + lane / G::CH;
       *reinterpret_cast<u32x4*>(vt + G::lds_off(rr, lane % G::CH)) = R.v[u];
     }
     if constexpr (I8) {
+      // lanes 0-31 store the K scales of cells 0-31, lanes 32-63 the V scales
       uint16_t* dst = scl + (lane >> 5) * TC * G::NG + (lane & 31) * G::NG;
+      const u32x2 sv = lane < 32 ? R.ks : R.vs;
       if constexpr (G::NG == 4) {
-        *reinterpret_cast<u32x2*>(dst) = R.sc;
+        *reinterpret_cast<u32x2*>(dst) = sv;
       } else if constexpr (G::NG == 2) {
-        *reinterpret_cast<uint32_t*>(dst) = R.sc[0];
+        *reinterpret_cast<uint32_t*>(dst) = sv[0];
       } else {
-        *dst = (uint16_t)R.sc[0];
+        *dst = (uint16_t)sv[0];
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -281,72 +342,105 @@ __global__ __launch_bounds__(256, 1) void attn_mfma(AttnArgs a) {
     for (int nb = 0; nb < G::NB; ++nb) O[k][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  auto compute = [&](int ts, const Regs& R) {
+  // ---- QK: S[cb][k][i] = score of cell ts+16cb+4lb+i for row 16k+lr ----
+  auto qk = [&](const KRegs& R, f32x4 (&S)[2][NRB]) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // ---- QK: S[cb][k][i] = score of cell ts+16cb+4lb+i for row 16k+lr ----
-    f32x4 S[2][NRB];
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
+    for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
       for (int k = 0; k < NRB; ++k) S[cb][k] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (!I8) {
+    if constexpr (!I8) {
 #pragma unroll
-        for (int ks = 0; ks < G::KS; ++ks) {
-          const half8 ka = __builtin_bit_cast(half8, R.k[cb][ks]);
+      for (int ks = 0; ks < G::KS; ++ks) {
 #pragma unroll
-          for (int k = 0; k < NRB; ++k) {
-            S[cb][k] = mfma16(ka, qhi[k][ks], S[cb][k]);
-            S[cb][k] = mfma16(ka, qlo[k][ks], S[cb][k]);
+        for (int k = 0; k < NRB; ++k) {
+          const half8 qh = __builtin_bit_cast(half8, qlds[((k * G::KS + ks) * 2 + 0) * 64 + lane]);
+          const half8 ql = __builtin_bit_cast(half8, qlds[((k * G::KS + ks) * 2 + 1) * 64 + lane]);
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb) {
+            const half8 ka = __builtin_bit_cast(half8, R.k[cb][ks]);
+            S[cb][k] = mfma16(ka, qh, S[cb][k]);
+            S[cb][k] = mfma16(ka, ql, S[cb][k]);
           }
         }
-      } else {
-        // K scales of the four output cells of this lane (cells 16cb+4lb+i)
-        const uint16_t* ks_l = scl + (16 * cb + 4 * lb) * G::NG;
+      }
+    } else {
 #pragma unroll
-        for (int gi = 0; gi < G::NG; ++gi) {
-          const half8 k0 = i8x8_to_half8(R.k[cb][gi][0], R.k[cb][gi][1]);
-          const half8 k1 = i8x8_to_half8(R.k[cb][gi][2], R.k[cb][gi][3]);
+      for (int gi = 0; gi < G::NG; ++gi) {
+        half8 k0[2], k1[2];
 #pragma unroll
-          for (int k = 0; k < NRB; ++k) {
+        for (int cb = 0; cb < 2; ++cb) {
+          k0[cb] = i8x8_to_half8(R.k[cb][gi][0], R.k[cb][gi][1]);
+          k1[cb] = i8x8_to_half8(R.k[cb][gi][2], R.k[cb][gi][3]);
+        }
+#pragma unroll
+        for (int k = 0; k < NRB; ++k) {
+          const int b0 = (k * G::KS + 2 * gi) * 2;
+          const half8 qh0 = __builtin_bit_cast(half8, qlds[(b0 + 0) * 64 + lane]);
+          const half8 ql0 = __builtin_bit_cast(half8, qlds[(b0 + 1) * 64 + lane]);
+          const half8 qh1 = __builtin_bit_cast(half8, qlds[(b0 + 2) * 64 + lane]);
+          const half8 ql1 = __builtin_bit_cast(half8, qlds[(b0 + 3) * 64 + lane]);
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb) {
             f32x4 C = f32x4{0.f, 0.f, 0.f, 0.f};
-            C = mfma16(k0, qhi[k][2 * gi], C);
-            C = mfma16(k0, qlo[k][2 * gi], C);
-            C = mfma16(k1, qhi[k][2 * gi + 1], C);
-            C = mfma16(k1, qlo[k][2 * gi + 1], C);
+            C = mfma16(k0[cb], qh0, C);
+            C = mfma16(k0[cb], ql0, C);
+            C = mfma16(k1[cb], qh1, C);
+            C = mfma16(k1[cb], ql1, C);
+            // K scales of this lane's four output cells 16cb+4lb+i, group gi
+            const uint16_t* ks_l = scl + (16 * cb + 4 * lb) * G::NG + gi;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              S[cb][k][i] = fmaf(C[i], h2f(ks_l[i * G::NG + gi]), S[cb][k][i]);
+              S[cb][k][i] = __builtin_fmaf(C[i], (float)__builtin_bit_cast(_Float16, ks_l[i * G::NG]),
+                                           S[cb][k][i]);
           }
         }
       }
     }
 
-    // ---- online softmax per query row (this lane: row 16k+lr, 8 cells) ----
+  };
+
+  // ---- online softmax per query row (this lane: row 16k+lr, 8 cells), then PV ----
+  auto softmax_pv = [&](int ts, const f32x4 (&S)[2][NRB]) {
+    const bool edge = ts + TC > lim_lo;          // wave-uniform
     float pr[NRB][8];
 #pragma unroll
     for (int k = 0; k < NRB; ++k) {
       float x[8];
-      float tmax = -INFINITY;
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int pos = ts + 16 * cb + 4 * lb + i;
-          const float v = pos < lim[k] ? S[cb][k][i] : -INFINITY;
-          x[4 * cb + i] = v;
-          tmax = fmaxf(tmax, v);
-        }
+        for (int i = 0; i < 4; ++i) x[4 * cb + i] = S[cb][k][i];
+      if (edge) {
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (ts + 16 * cb + 4 * lb + i >= lim[k]) x[4 * cb + i] = -INFINITY;
+      }
+      float tmax = x[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) tmax = fmaxf(tmax, x[e]);
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
       const float mold = m_run[k];
       const float mnew = fmaxf(mold, tmax);
       const float corr = (mold == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mold - mnew);
       float psum = 0.f;
+      if (edge) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float pe = (x[e] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x[e] - mnew);
-        pr[k][e] = pe;
-        psum += pe;
+        for (int e = 0; e < 8; ++e) {
+          const float pe = (x[e] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x[e] - mnew);
+          pr[k][e] = pe;
+          psum += pe;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pe = __builtin_amdgcn_exp2f(x[e] - mnew);
+          pr[k][e] = pe;
+          psum += pe;
+        }
       }
       psum += __shfl_xor(psum, 16, 64);
       psum += __shfl_xor(psum, 32, 64);
@@ -409,7 +503,7 @@ __global__ __launch_bounds__(256, 1) void attn_mfma(AttnArgs a) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int cell = (e < 4) ? 4 * lb + e : 16 + 4 * lb + (e - 4);
-            pv[e] = pr[k][e] * h2f(vs_l[cell * G::NG + gi]);
+            pv[e] = pr[k][e] * (float)__builtin_bit_cast(_Float16, vs_l[cell * G::NG + gi]);
           }
           split_hi_lo(pv, phi[k], plo[k]);
         }
@@ -429,23 +523,29 @@ __global__ __launch_bounds__(256, 1) void attn_mfma(AttnArgs a) {
     }
   };
 
-  // ---- main loop: this wave's tiles, next tile's loads in flight ----
+  __syncthreads();   // query operands staged
+
+  // ---- main loop over this wave's tiles.  One register set each for K and
+  // V: V(t+1) is requested as soon as V(t) is in LDS, K(t+1) as soon as QK(t)
+  // has consumed K(t); the second wave on the SIMD covers the rest. ----
   {
-    Regs RA, RB2;
+    KRegs RK;
+    VRegs RV;
     int ts = c0 + TC * wave;
-    if (ts < cend) issue_loads(ts, RA);
+    if (ts < cend) {
+      issue_k(ts, RK);
+      issue_v(ts, RV);
+    }
 #pragma unroll 1
     while (ts < cend) {
-      int tn = ts + 4 * TC;
-      stage(RA);
-      if (tn < cend) issue_loads(tn, RB2);
-      compute(ts, RA);
-      ts = tn;
-      if (ts >= cend) break;
-      tn = ts + 4 * TC;
-      stage(RB2);
-      if (tn < cend) issue_loads(tn, RA);
-      compute(ts, RB2);
+      const int tn = ts + 4 * TC;
+      const bool more = tn < cend;
+      stage(RV);
+      if (more) issue_v(tn, RV);
+      f32x4 S[2][NRB];
+      qk(RK, S);
+      if (more) issue_k(tn, RK);
+      softmax_pv(ts, S);
       ts = tn;
     }
   }

@@ -161,7 +161,7 @@ int attn_common(bool i8, const float* q, const void* k, const void* v, const uin
   int rc = gqa::check_shape(sh);
   if (rc != GQA_OK) return rc;
   if (chunk <= 0) chunk = gqa::auto_chunk(sh);
-  if (chunk <= 0) return GQA_ERR_CHUNK;
+  if (chunk <= 0 || chunk > gqa::max_chunk(sh)) return GQA_ERR_CHUNK;
   const size_t need = gqa::part_bytes(sh, chunk);
   if (part_bytes < need) return GQA_ERR_WORKSPACE;
   const int64_t P = gqa::num_splits(sh, chunk);

@@ -33,7 +33,8 @@ int auto_chunk(const Shape& s) {
   chunk = (chunk + 63) / 64 * 64;
   int64_t Wr = (W + 63) / 64 * 64;
   if (chunk > Wr) chunk = Wr;
-  if (chunk > (1 << 30)) chunk = 1 << 30;
+  const int64_t cap = max_chunk(s) / 64 * 64;
+  if (chunk > cap) chunk = cap;
   return (int)chunk;
 }
 

@@ -53,6 +53,13 @@ inline int block_rows(const Shape& s) {
   return 32;
 }
 
+// Largest split the kernels accept: one split's K (or V) rows of a KV head
+// span chunk * Hk * row bytes, addressed with 31-bit buffer offsets.
+inline int64_t max_chunk(const Shape& s) {
+  const int64_t row = (int64_t)s.Hk * s.D * (s.i8 ? 1 : 2);
+  return ((int64_t)1 << 31) / row - 1;
+}
+
 int check_shape(const Shape& s);               // GQA_OK or GQA_ERR_*
 int auto_chunk(const Shape& s);                // > 0, or GQA_ERR_*
 size_t part_bytes(const Shape& s, int chunk);  // 0 on bad arguments

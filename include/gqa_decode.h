@@ -62,7 +62,8 @@ enum {
   GQA_ERR_GROUP = -3,      /* H % Hk != 0                                        */
   GQA_ERR_HEAD_DIM = -4,   /* D not in {64, 128, 256}                            */
   GQA_ERR_BUDGET = -5,     /* ids given with B < 1                               */
-  GQA_ERR_CHUNK = -6,      /* merge called with chunk < 1 (pass the resolved one)*/
+  GQA_ERR_CHUNK = -6,      /* chunk < 1 in the merge, or a split wider than 2^31
+                              bytes of K rows (chunk * Hk * D * elem >= 2^31)    */
   GQA_ERR_WORKSPACE = -7   /* part_bytes < gqa_decode_part_bytes(...)            */
 };
 
@@ -89,8 +90,9 @@ int gqa_decode_auto_chunk(int S, int T, int Lmax, int B, int H, int Hk, int D, i
  *   part      workspace of part_bytes >= gqa_decode_part_bytes(S,T,Lmax,B,H,D,chunk')
  *             where chunk' is the resolved chunk; contents are overwritten
  *   scale     score scale (typically 1/sqrt(D))
- *   chunk     cells per split; <= 0 selects gqa_decode_auto_chunk(...)
- * Errors: GQA_ERR_NULL, _SHAPE, _GROUP, _HEAD_DIM, _BUDGET, _WORKSPACE. */
+ *   chunk     cells per split; <= 0 selects gqa_decode_auto_chunk(...);
+ *             chunk * Hk * D * (bytes per element) must stay below 2^31
+ * Errors: GQA_ERR_NULL, _SHAPE, _GROUP, _HEAD_DIM, _BUDGET, _CHUNK, _WORKSPACE. */
 int gqa_decode_attn_f16(const float *q, const uint16_t *k, const uint16_t *v,
                         const int32_t *ids, const int32_t *seq_lens,
                         float *part, size_t part_bytes,
