@@ -112,7 +112,10 @@ struct TileGeom {
   __device__ static int lds_off(int r, int c) { return r * RBY + ((c ^ swz(r)) << 4); }
 };
 
-// Dynamic LDS bytes of one workgroup.
+// Largest split (cells) in gather mode: the split's cell ids are staged in LDS.
+constexpr int kMaxIdsChunk = 4096;
+
+// Dynamic LDS bytes of one workgroup (plus AttnLds::IDSB in gather mode).
 template <int D, bool I8, int NRB>
 struct AttnLds {
   using G = TileGeom<D, I8>;
@@ -124,6 +127,7 @@ struct AttnLds {
   static constexpr int SC = I8 ? 4 * 2 * G::TC * G::NG * 2 : 0;  // per-wave K/V scales
   static constexpr int ML = 4 * RB * 2 * 4;              // per-wave (m, l)
   static constexpr int BYTES = MAIN + QB + SC + ML;
+  static constexpr int IDSB = kMaxIdsChunk * 4;          // cell ids of the split (gather mode)
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -214,27 +218,45 @@ __global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a) {
     lim[k] = wr < cend ? wr : cend;
   }
 
-  // ---- K/V addressing ----
-  // dense: buffer resources based at the first cell of this split, so every
-  // offset is 32-bit and the per-tile offsets are scalars; reads past cend
-  // return zeros (those cells are masked).  ids: per-lane cell rows.
+  // ---- K/V addressing through buffer resources: every offset is 32-bit and
+  // a read at or past the resource's size returns zeros without touching
+  // memory.  The whole per-cell offset goes in the per-lane offset, which
+  // the range check covers; the scalar offset is always 0.  dense: the
+  // resource starts at this split's first cell and ends at its last, so the
+  // ragged end of the last tile, and tiles past the split's end, read
+  // zeros.  gather: the resource spans the sequence's rows of this KV head;
+  // a lane adds its cell's row offset (the split's ids are staged in LDS)
+  // and list positions past the split map to kOut, past every resource.
+  // Loads are therefore issued unconditionally, which keeps the compiler's
+  // wait counts exact. ----
   const uint32_t rowstride = (uint32_t)a.Hk * RBY;           // bytes between cells of a KV head
-  const size_t first_row = ((size_t)s * a.Lmax + (IDS ? 0 : c0)) * a.Hk + g;
-  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k) + first_row * RBY;
-  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v) + first_row * RBY;
-  const uint16_t* ksbase = I8 ? a.ksc + first_row * G::NG : nullptr;
-  const uint16_t* vsbase = I8 ? a.vsc + first_row * G::NG : nullptr;
-  const uint32_t nrec = (uint32_t)(cend - c0) * rowstride;
   const uint32_t srow = (uint32_t)a.Hk * G::NG * 2;           // scale bytes between cells
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase, nrec);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase, nrec);
-  const __amdgpu_buffer_rsrc_t rks = make_rsrc(ksbase, (uint32_t)(cend - c0) * srow);
-  const __amdgpu_buffer_rsrc_t rvs = make_rsrc(vsbase, (uint32_t)(cend - c0) * srow);
-  const int32_t* idrow = IDS ? a.ids + ((size_t)s * a.T + tq) * a.B : nullptr;
-  auto cell_at = [&](int pos) -> int {          // ids mode; pos clamped into [c0, cend)
-    pos = pos < cend - 1 ? pos : cend - 1;
-    int c = idrow[pos];
-    return c < 0 ? 0 : (c >= a.Lmax ? a.Lmax - 1 : c);
+  const size_t first_row = ((size_t)s * a.Lmax + (IDS ? 0 : c0)) * a.Hk + g;
+  const uint32_t ncells = IDS ? (uint32_t)a.Lmax : (uint32_t)(cend - c0);
+  const __amdgpu_buffer_rsrc_t rk =
+      make_rsrc(reinterpret_cast<const uint8_t*>(a.k) + first_row * RBY, ncells * rowstride);
+  const __amdgpu_buffer_rsrc_t rv =
+      make_rsrc(reinterpret_cast<const uint8_t*>(a.v) + first_row * RBY, ncells * rowstride);
+  const __amdgpu_buffer_rsrc_t rks = make_rsrc(I8 ? a.ksc + first_row * G::NG : nullptr, ncells * srow);
+  const __amdgpu_buffer_rsrc_t rvs = make_rsrc(I8 ? a.vsc + first_row * G::NG : nullptr, ncells * srow);
+  constexpr uint32_t kOut = 0x80000000u;                     // past every resource (< 2^31 bytes)
+  int32_t* idl = reinterpret_cast<int32_t*>(smem + L::BYTES);  // gather mode: ids of [c0, cend)
+  if constexpr (IDS) {
+    const int32_t* idrow = a.ids + ((size_t)s * a.T + tq) * a.B;
+    for (int i = tid; i < cend - c0; i += 256) {
+      int c = idrow[c0 + i];
+      idl[i] = c < 0 ? 0 : (c >= a.Lmax ? a.Lmax - 1 : c);
+    }
+  }
+  // Byte offset, from the resource base, of the row of list position pos
+  // (pos >= c0; positions at or past cend land out of range).
+  auto cell_off = [&](int pos, uint32_t stride) -> uint32_t {
+    if constexpr (IDS) {
+      const int i = (pos < cend ? pos : cend - 1) - c0;
+      return pos < cend ? (uint32_t)idl[i] * stride : kOut;
+    } else {
+      return (uint32_t)(pos - c0) * stride;
+    }
   };
 
   struct KRegs {
@@ -246,67 +268,33 @@ __global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a) {
   };
 
   auto issue_k = [&](int ts, KRegs& R) {
-    if constexpr (!IDS) {
-      const uint32_t t0 = (uint32_t)(ts - c0);
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        const uint32_t so = (t0 + 16 * cb) * rowstride;
-        const uint32_t vo = lr * rowstride + 16 * lb;
+    for (int cb = 0; cb < 2; ++cb) {
+      const uint32_t vo = cell_off(ts + 16 * cb + lr, rowstride) + 16 * lb;
 #pragma unroll
-        for (int j = 0; j < G::KLD; ++j)
-          R.k[cb][j] = __builtin_amdgcn_raw_buffer_load_b128(rk, vo + 64 * j, so, 0);
-      }
-    } else {
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        const uint8_t* row = kbase + (size_t)cell_at(ts + 16 * cb + lr) * rowstride + 16 * lb;
-#pragma unroll
-        for (int j = 0; j < G::KLD; ++j) R.k[cb][j] = *reinterpret_cast<const u32x4*>(row + 64 * j);
-      }
+      for (int j = 0; j < G::KLD; ++j)
+        R.k[cb][j] = __builtin_amdgcn_raw_buffer_load_b128(rk, vo + 64 * j, 0, 0);
     }
   };
 
   auto issue_v = [&](int ts, VRegs& R) {
-    if constexpr (!IDS) {
-      const uint32_t t0 = (uint32_t)(ts - c0);
 #pragma unroll
-      for (int u = 0; u < G::VLD; ++u) {
-        const uint32_t so = (t0 + u * G::RPI) * rowstride;
-        const uint32_t vo = (lane / G::CH) * rowstride + 16 * (lane % G::CH);
-        R.v[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, vo, so, 0);
-      }
-      if constexpr (I8) {
-        const uint32_t so = t0 * srow;
-        const uint32_t vo = (lane & 31) * srow;
-        if constexpr (G::NG == 4) {
-          R.ks = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rks, vo, so, 0));
-          R.vs = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rvs, vo, so, 0));
-        } else if constexpr (G::NG == 2) {
-          R.ks[0] = __builtin_amdgcn_raw_buffer_load_b32(rks, vo, so, 0);
-          R.vs[0] = __builtin_amdgcn_raw_buffer_load_b32(rvs, vo, so, 0);
-        } else {
-          R.ks[0] = __builtin_amdgcn_raw_buffer_load_b16(rks, vo, so, 0);
-          R.vs[0] = __builtin_amdgcn_raw_buffer_load_b16(rvs, vo, so, 0);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < G::VLD; ++u) {
-        const uint8_t* row = vbase + (size_t)cell_at(ts + u * G::RPI + lane / G::CH) * rowstride;
-        R.v[u] = *reinterpret_cast<const u32x4*>(row + 16 * (lane % G::CH));
-      }
-      if constexpr (I8) {
-        const size_t c = (size_t)cell_at(ts + (lane & 31)) * (a.Hk * G::NG);
-        if constexpr (G::NG == 4) {
-          R.ks = *reinterpret_cast<const u32x2*>(ksbase + c);
-          R.vs = *reinterpret_cast<const u32x2*>(vsbase + c);
-        } else if constexpr (G::NG == 2) {
-          R.ks[0] = *reinterpret_cast<const uint32_t*>(ksbase + c);
-          R.vs[0] = *reinterpret_cast<const uint32_t*>(vsbase + c);
-        } else {
-          R.ks[0] = ksbase[c];
-          R.vs[0] = vsbase[c];
-        }
+    for (int u = 0; u < G::VLD; ++u) {
+      const int rr = u * G::RPI + lane / G::CH;
+      const uint32_t vo = cell_off(ts + rr, rowstride) + 16 * (lane % G::CH);
+      R.v[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, vo, 0, 0);
+    }
+    if constexpr (I8) {
+      const uint32_t vo = cell_off(ts + (lane & 31), srow);
+      if constexpr (G::NG == 4) {
+        R.ks = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rks, vo, 0, 0));
+        R.vs = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rvs, vo, 0, 0));
+      } else if constexpr (G::NG == 2) {
+        R.ks[0] = __builtin_amdgcn_raw_buffer_load_b32(rks, vo, 0, 0);
+        R.vs[0] = __builtin_amdgcn_raw_buffer_load_b32(rvs, vo, 0, 0);
+      } else {
+        R.ks[0] = __builtin_amdgcn_raw_buffer_load_b16(rks, vo, 0, 0);
+        R.vs[0] = __builtin_amdgcn_raw_buffer_load_b16(rvs, vo, 0, 0);
       }
     }
   };
@@ -523,8 +511,6 @@ __global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a) {
     }
   };
 
-  __syncthreads();   // query operands staged
-
   // ---- main loop over this wave's tiles.  One register set each for K and
   // V: V(t+1) is requested as soon as V(t) is in LDS, K(t+1) as soon as QK(t)
   // has consumed K(t); the second wave on the SIMD covers the rest. ----
@@ -532,19 +518,17 @@ __global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a) {
     KRegs RK;
     VRegs RV;
     int ts = c0 + TC * wave;
-    if (ts < cend) {
-      issue_k(ts, RK);
-      issue_v(ts, RV);
-    }
+    __syncthreads();   // query operands (and ids) staged
+    issue_k(ts, RK);
+    issue_v(ts, RV);
 #pragma unroll 1
     while (ts < cend) {
       const int tn = ts + 4 * TC;
-      const bool more = tn < cend;
       stage(RV);
-      if (more) issue_v(tn, RV);
+      issue_v(tn, RV);     // past the split's end: no memory traffic
       f32x4 S[2][NRB];
       qk(RK, S);
-      if (more) issue_k(tn, RK);
+      issue_k(tn, RK);
       softmax_pv(ts, S);
       ts = tn;
     }

@@ -119,7 +119,8 @@ __global__ __launch_bounds__(kThreads) void merge_rows(MergeArgs a) {
 
 template <int D, bool I8, bool IDS, int NRB>
 hipError_t launch_one(const AttnArgs& a, dim3 grid, hipStream_t st) {
-  constexpr int bytes = gqa_kern::AttnLds<D, I8, NRB>::BYTES;
+  constexpr int bytes = gqa_kern::AttnLds<D, I8, NRB>::BYTES +
+                        (IDS ? gqa_kern::AttnLds<D, I8, NRB>::IDSB : 0);
   auto* fn = &gqa_kern::attn_mfma<D, I8, IDS, NRB>;
   if (bytes > 65536) {
     static bool attr_set = false;   // per instance; set before the first launch
@@ -162,6 +163,7 @@ int attn_common(bool i8, const float* q, const void* k, const void* v, const uin
   if (rc != GQA_OK) return rc;
   if (chunk <= 0) chunk = gqa::auto_chunk(sh);
   if (chunk <= 0 || chunk > gqa::max_chunk(sh)) return GQA_ERR_CHUNK;
+  if (ids && (int64_t)Lmax * Hk * D * (i8 ? 1 : 2) >= ((int64_t)1 << 31)) return GQA_ERR_SHAPE;
   const size_t need = gqa::part_bytes(sh, chunk);
   if (part_bytes < need) return GQA_ERR_WORKSPACE;
   const int64_t P = gqa::num_splits(sh, chunk);

@@ -55,9 +55,13 @@ inline int block_rows(const Shape& s) {
 
 // Largest split the kernels accept: one split's K (or V) rows of a KV head
 // span chunk * Hk * row bytes, addressed with 31-bit buffer offsets.
+// In gather mode the split's cell ids are staged in LDS: at most
+// kMaxIdsChunk cells per split.
+constexpr int64_t kMaxIdsChunk = 4096;
 inline int64_t max_chunk(const Shape& s) {
   const int64_t row = (int64_t)s.Hk * s.D * (s.i8 ? 1 : 2);
-  return ((int64_t)1 << 31) / row - 1;
+  const int64_t m = ((int64_t)1 << 31) / row - 1;
+  return s.ids && m > kMaxIdsChunk ? kMaxIdsChunk : m;
 }
 
 int check_shape(const Shape& s);               // GQA_OK or GQA_ERR_*
