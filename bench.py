@@ -15,8 +15,8 @@ Reported (one JSON line on stdout):
                bracketed by device synchronisation)
   ms_per_step  wall-clock milliseconds per step
   roofline     the chunk kernel alone: algorithmic bytes per launch / its
-               mean duration from HIP events on its stream, against the
-               8 TB/s HBM peak; `traffic` is HBM bytes per launch measured
+               mean duration from HIP events on its stream (bursts of
+               back-to-back launches), against the 8 TB/s HBM peak; `traffic` is HBM bytes per launch measured
                with rocprofv3 counters (from profiles/, null when the kernel
                source changed since they were taken)
   cpu_baseline the fp64 oracle on the host cores over a bounded sample
@@ -39,6 +39,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 LLC_BYTES = 256 << 20
+SETTLE_S = 0.05
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -179,19 +180,25 @@ def main():
                               B=sh["B"], chunk=chunk, device=dev)
     stream = torch.cuda.current_stream()
 
-    def one(i, ev=None):
+    def one(i):
         x = sets[i % copies]
-        if ev is not None:
-            ev[0].record(stream)
         step.attn(x["q"], x["k"], x["v"], x["seq_lens"], inp.scale, x["k_scales"], x["v_scales"],
                   x["ids"])
-        if ev is not None:
-            ev[1].record(stream)
         step.merge(x["seq_lens"], x["ids"])
 
     for i in range(args.warmup):
         one(i)
     torch.cuda.synchronize()
+    # The GPU's clocks take a few milliseconds of sustained load to settle; a
+    # short warm-up leaves the first timed steps ~10 % slow.  Keep stepping
+    # (untimed) until at least SETTLE_S of warm-up has run.
+    extra = 0
+    t_w = time.perf_counter()
+    while time.perf_counter() - t_w < SETTLE_S:
+        for i in range(10):
+            one(args.warmup + extra + i)
+        extra += 10
+        torch.cuda.synchronize()
 
     # timed region: K steps back to back, wall clock bracketed by synchronisation
     K = args.steps
@@ -203,15 +210,23 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall / K * 1e3
 
-    # chunk-kernel duration from HIP events on the launch stream (separate pass
-    # so the events do not perturb the wall-clock run)
+    # chunk-kernel duration from HIP events on the launch stream, in a pass of
+    # its own after the timed steps: bursts of back-to-back chunk-kernel
+    # launches (rotating input copies) between two events, so the figure is
+    # the kernel's launch-to-launch time and carries no per-event overhead.
+    bursts, per = 5, max(1, K // 5)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(K)]
+           for _ in range(bursts)]
     torch.cuda.synchronize()
-    for i in range(K):
-        one(i, evs[i])
+    for b in range(bursts):
+        evs[b][0].record(stream)
+        for i in range(per):
+            x = sets[(b * per + i) % copies]
+            step.attn(x["q"], x["k"], x["v"], x["seq_lens"], inp.scale, x["k_scales"],
+                      x["v_scales"], x["ids"])
+        evs[b][1].record(stream)
     torch.cuda.synchronize()
-    attn_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    attn_ms = np.array([a.elapsed_time(b) / per for a, b in evs])
     attn_mean_s = float(attn_ms.mean()) / 1e3
 
     achieved = step_bytes / attn_mean_s / 1e9
@@ -223,6 +238,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "extra_warmup_steps": extra,
         "ms_per_step": round(ms_per_step, 5),
         "us_per_step": round(ms_per_step * 1e3, 2),
         "pct_of_hbm_peak": round(100 * step_bytes / (wall / K) / 1e9 / HBM_PEAK_GBS, 2),
@@ -242,8 +258,8 @@ def main():
                      "traffic": traffic,
                      "kernel": "attn_chunk",
                      "kernel_us_mean": round(attn_mean_s * 1e6, 3),
-                     "kernel_us_p10_p90": [round(float(np.percentile(attn_ms, 10)) * 1e3, 3),
-                                           round(float(np.percentile(attn_ms, 90)) * 1e3, 3)]},
+                     "kernel_us_burst_min_max": [round(float(attn_ms.min()) * 1e3, 3),
+                                                 round(float(attn_ms.max()) * 1e3, 3)]},
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the fp64 oracle on the host", file=sys.stderr, flush=True)

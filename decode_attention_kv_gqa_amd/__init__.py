@@ -19,15 +19,20 @@ __all__ = ["decode_attention", "DecodeAttention", "GqaDecodeError", "gqa_decode_
            "gqa_decode_auto_chunk", "strerror"]
 
 
-def _check(fn, code):
-    if code != 0:
-        raise GqaDecodeError(fn, code)
+def _raw_stream_getter():
+    """Fast lookup of the current torch stream as a raw hipStream_t."""
+    import torch
+    get = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if get is not None:
+        return get
+    return lambda dev: torch.cuda.current_stream(dev).cuda_stream
 
 
 class DecodeAttention:
     """A planned decode step for fixed shapes: resolves the split size once,
     owns the partial workspace and output, and enqueues the two kernels on
-    the current torch stream at each call."""
+    the current torch stream at each call (or on `stream`, a raw
+    hipStream_t).  The per-call path is argument marshalling only."""
 
     def __init__(self, S, T, H, Hk, D, Lmax, kv: str, B: int = 0, chunk: int = 0, device="cuda"):
         import torch
@@ -44,34 +49,38 @@ class DecodeAttention:
         n = max(1, (self.part_bytes + 3) // 4)
         self.part = torch.empty(n, dtype=torch.float32, device=device)
         self.out = torch.empty((S, T, H, D), dtype=torch.float32, device=device)
+        self._dev = self.out.device.index
+        self._stream = _raw_stream_getter()
+        lib = _lib.load()
+        self._f16, self._i8, self._merge = (lib.gqa_decode_attn_f16, lib.gqa_decode_attn_i8,
+                                            lib.gqa_decode_merge)
 
     def attn(self, q, k, v, seq_lens, scale, k_scales=None, v_scales=None, ids=None, stream=None):
-        import torch
-        st = torch.cuda.current_stream().cuda_stream if stream is None else stream
+        st = self._stream(self._dev) if stream is None else stream
+        idp = None if ids is None else ids.data_ptr()
         B = self.B if ids is not None else 0
         if self.kv == "i8":
-            rc = gqa_decode_attn_i8(q.data_ptr(), k.data_ptr(), v.data_ptr(), k_scales.data_ptr(),
-                                    v_scales.data_ptr(), None if ids is None else ids.data_ptr(),
-                                    seq_lens.data_ptr(), self.part.data_ptr(), self.part_bytes,
-                                    self.S, self.T, self.Lmax, B, self.H, self.Hk, self.D,
-                                    float(scale), self.chunk, st)
-            _check("gqa_decode_attn_i8", rc)
+            rc = self._i8(q.data_ptr(), k.data_ptr(), v.data_ptr(), k_scales.data_ptr(),
+                          v_scales.data_ptr(), idp, seq_lens.data_ptr(), self.part.data_ptr(),
+                          self.part_bytes, self.S, self.T, self.Lmax, B, self.H, self.Hk, self.D,
+                          scale, self.chunk, st)
+            if rc:
+                raise GqaDecodeError("gqa_decode_attn_i8", rc)
         else:
-            rc = gqa_decode_attn_f16(q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                                     None if ids is None else ids.data_ptr(), seq_lens.data_ptr(),
-                                     self.part.data_ptr(), self.part_bytes, self.S, self.T,
-                                     self.Lmax, B, self.H, self.Hk, self.D, float(scale),
-                                     self.chunk, st)
-            _check("gqa_decode_attn_f16", rc)
+            rc = self._f16(q.data_ptr(), k.data_ptr(), v.data_ptr(), idp, seq_lens.data_ptr(),
+                           self.part.data_ptr(), self.part_bytes, self.S, self.T, self.Lmax, B,
+                           self.H, self.Hk, self.D, scale, self.chunk, st)
+            if rc:
+                raise GqaDecodeError("gqa_decode_attn_f16", rc)
 
     def merge(self, seq_lens, ids=None, stream=None):
-        import torch
-        st = torch.cuda.current_stream().cuda_stream if stream is None else stream
-        rc = gqa_decode_merge(self.part.data_ptr(), seq_lens.data_ptr(),
-                              None if ids is None else ids.data_ptr(), self.out.data_ptr(),
-                              self.S, self.T, self.Lmax, self.B if ids is not None else 0,
-                              self.H, self.D, self.chunk, st)
-        _check("gqa_decode_merge", rc)
+        st = self._stream(self._dev) if stream is None else stream
+        rc = self._merge(self.part.data_ptr(), seq_lens.data_ptr(),
+                         None if ids is None else ids.data_ptr(), self.out.data_ptr(),
+                         self.S, self.T, self.Lmax, self.B if ids is not None else 0,
+                         self.H, self.D, self.chunk, st)
+        if rc:
+            raise GqaDecodeError("gqa_decode_merge", rc)
 
     def __call__(self, q, k, v, seq_lens, scale, k_scales=None, v_scales=None, ids=None):
         self.attn(q, k, v, seq_lens, scale, k_scales, v_scales, ids)

@@ -6,8 +6,8 @@
 // row is fetched from HBM exactly once per split (cera, attention_gqa.metal:
 // one threadgroup per KV head for all Q heads of the group).
 //
-// The four waves of the workgroup stream 32-cell tiles independently (wave w
-// takes tiles w, w+4, ...) with their own online-softmax state, and combine
+// The NW (4 or 8) waves of the workgroup stream 32-cell tiles independently
+// (wave w takes tiles w, w+NW, ...) with their own online-softmax state, and combine
 // at the end through LDS into ONE partial (o unnormalised, m, l) per query
 // row — the chunk partial of qsa2.metal (qsa_attn2), merged later by the
 // log-sum-exp merge (qsa_merge2).
@@ -22,8 +22,12 @@
 //        multiplied by that group's f16 scale after the dot (qsa2.metal,
 //        qsa_attn3: raw int8 dot per group, then the scale).
 //   softmax  online, per query row, base 2 (q carries scale * log2 e): the
-//        running max/sum update with a zero correction before the first
-//        visible cell (cera, flash_attention.metal, flash_attention_impl).
+//        running max/sum update of cera, flash_attention.metal
+//        (flash_attention_impl), with no correction before the first visible
+//        cell.  The row's reference max moves only when a tile's max exceeds
+//        it by more than 8 (so p <= 256), which skips most accumulator
+//        rescales; any reference gives the same (o, m, l) partial up to
+//        rounding.  Cross-lane max/sum use the gfx950 permlane swaps.
 //   PV   O[row][dim] += P[row][cell] V[cell][dim]  MFMA with A = P taken
 //        directly from the QK accumulators (no shuffle: the QK output layout
 //        is the PV input layout up to a fixed permutation of the 32 cells),
@@ -80,6 +84,42 @@ __device__ __forceinline__ void split_hi_lo(const float (&x)[8], half8& hi, half
   }
 }
 
+// Butterfly steps across lane distance 16 and 32 of a wave64 with the gfx950
+// permlane swaps (VALU, no LDS round trip).  With both operands equal,
+// permlane16_swap returns (rows 0,0,2,2) and (rows 1,1,3,3) of x, and
+// permlane32_swap returns (low, low) and (high, high) halves, so combining
+// the two results gives every lane the reduction over its xor-16 / xor-32
+// partner.  The two results pass through an empty asm statement: without it
+// this compiler folds the second result into the first when both operands
+// are the same value (it emitted r0 + r0 for r0 + r1).
+__device__ __forceinline__ void swap16(float x, float& a, float& b) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  uint32_t r0 = r[0], r1 = r[1];
+  asm volatile("" : "+v"(r0), "+v"(r1));
+  a = __builtin_bit_cast(float, r0);
+  b = __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ void swap32(float x, float& a, float& b) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  uint32_t r0 = r[0], r1 = r[1];
+  asm volatile("" : "+v"(r0), "+v"(r1));
+  a = __builtin_bit_cast(float, r0);
+  b = __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ float max_x16(float x) { float a, b; swap16(x, a, b); return fmaxf(a, b); }
+__device__ __forceinline__ float max_x32(float x) { float a, b; swap32(x, a, b); return fmaxf(a, b); }
+__device__ __forceinline__ float sum_x16(float x) { float a, b; swap16(x, a, b); return a + b; }
+__device__ __forceinline__ float sum_x32(float x) { float a, b; swap32(x, a, b); return a + b; }
+
+// Largest magnitude of the f16 values packed in w exceeds 255 (or is not
+// finite).
+__device__ __forceinline__ bool f16x2_above_255(uint32_t w) {
+  const uint32_t a = w & 0x7fff7fffu;
+  return (a & 0xffffu) > 0x5bf8u || (a >> 16) > 0x5bf8u;   // 0x5bf8 = 255.0
+}
+
 __device__ __forceinline__ f32x4 mfma16(half8 a, half8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
@@ -115,20 +155,25 @@ struct TileGeom {
 // Largest split (cells) in gather mode: the split's cell ids are staged in LDS.
 constexpr int kMaxIdsChunk = 4096;
 
-// Dynamic LDS bytes of one workgroup (plus AttnLds::IDSB in gather mode).
-template <int D, bool I8, int NRB>
+// Dynamic LDS bytes of one workgroup of NW waves (plus AttnLds::IDSB in
+// gather mode).
+template <int D, bool I8, int NRB, int NW>
 struct AttnLds {
   using G = TileGeom<D, I8>;
   static constexpr int RB = 16 * NRB;
-  static constexpr int VT = 4 * G::TC * G::RBY;          // per-wave V tiles
-  static constexpr int BUF = 2 * RB * D * 4;             // cross-wave merge buffers (alias VT)
+  static constexpr int VT = NW * G::TC * G::RBY;         // per-wave V tiles
+  static constexpr int BUF = NW / 2 * RB * D * 4;        // cross-wave merge buffers (alias VT)
   static constexpr int MAIN = VT > BUF ? VT : BUF;
   static constexpr int QB = NRB * G::KS * 2 * 64 * 16;   // query B operands, hi and lo
-  static constexpr int SC = I8 ? 4 * 2 * G::TC * G::NG * 2 : 0;  // per-wave K/V scales
-  static constexpr int ML = 4 * RB * 2 * 4;              // per-wave (m, l)
+  static constexpr int SC = I8 ? NW * 2 * G::TC * G::NG * 2 : 0;  // per-wave K/V scales
+  static constexpr int ML = NW * RB * 2 * 4;             // per-wave (m, l)
   static constexpr int BYTES = MAIN + QB + SC + ML;
   static constexpr int IDSB = kMaxIdsChunk * 4;          // cell ids of the split (gather mode)
 };
+
+// Cache policy of the K/V row loads: non-temporal (each row is read once per
+// split and never again in the step).
+constexpr int kNT = 2;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   // raw buffer: stride 0, num_records in bytes; reads past the end return 0
@@ -136,10 +181,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            0x00020000);
 }
 
-template <int D, bool I8, bool IDS, int NRB>
-__global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a) {
+template <int D, bool I8, bool IDS, int NRB, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void attn_mfma(AttnArgs a) {
   using G = TileGeom<D, I8>;
-  using L = AttnLds<D, I8, NRB>;
+  using L = AttnLds<D, I8, NRB, NW>;
+  constexpr int NT = 64 * NW;                    // threads per workgroup
   constexpr int RB = 16 * NRB;
   constexpr int TC = G::TC;
   constexpr int RBY = G::RBY;
@@ -150,13 +196,21 @@ __global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a) {
   const int lane = tid & 63;
   const int lr = lane & 15, lb = lane >> 4;
 
-  const int p = blockIdx.x;
-  int y = blockIdx.y;
-  const int g = y % a.Hk;
-  y /= a.Hk;
-  const int rbl = y % a.nrb;
-  const int tq = y / a.nrb;
-  const int s = blockIdx.z;
+  // 1-D grid, XCD-aware order.  Consecutive workgroups are dispatched to
+  // different XCDs (8 of them, each with its own L2 and its own share of the
+  // fabric), so the index that varies fastest must carry equal work: the KV
+  // head, then the sequence; the split index varies slowest, because the
+  // last splits of short sequences are empty and would otherwise all land
+  // on the same XCDs.
+  int id = blockIdx.x;
+  const int g = id % a.Hk;
+  id /= a.Hk;
+  const int s = id % a.S;
+  id /= a.S;
+  const int nu = a.nrb * (IDS ? a.T : 1);
+  const int rbl = (id % nu) % a.nrb;
+  const int tq = (id % nu) / a.nrb;
+  const int p = id / nu;
   const int seq_len = a.seq_lens[s];
 
   auto width_of = [&](int r) -> int {   // r: row index within the unit
@@ -174,7 +228,17 @@ __global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a) {
   const int rlast = (a.R - 1 < r0 + RB - 1) ? a.R - 1 : r0 + RB - 1;
   const int wmax = width_of(rlast);
   const int64_t c0l = (int64_t)p * a.chunk;
-  if (c0l >= wmax) return;                       // nothing visible here; the merge skips it
+  if (c0l >= wmax) {
+    // nothing visible in this split for any row of the block: its partials
+    // carry weight 0 (m = -inf, l = 0), and the merge skips their o
+    if (tid < RB && r0 + tid < a.R) {
+      const int r = r0 + tid;
+      const size_t prow = ((size_t)(s * a.T + row_t(r)) * a.H + row_h(r)) * a.P + p;
+      a.part_ml[prow * 2] = -INFINITY;
+      a.part_ml[prow * 2 + 1] = 0.f;
+    }
+    return;
+  }
   const int c0 = (int)c0l;
   const int cend = (int)((c0l + a.chunk < wmax) ? c0l + a.chunk : wmax);
   // Tiles ending at or before lim_lo are fully visible to every real row.
@@ -186,7 +250,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a) {
   float* mls = reinterpret_cast<float*>(smem + L::MAIN + L::QB + L::SC);
 
   // ---- query rows as MFMA B operands (f16 hi + lo), staged once in LDS ----
-  for (int slot = tid; slot < NRB * G::KS * 64; slot += 256) {
+  for (int slot = tid; slot < NRB * G::KS * 64; slot += NT) {
     const int ln = slot & 63, kks = slot >> 6;
     const int ks = kks % G::KS, k = kks / G::KS;
     const int lr2 = ln & 15, lb2 = ln >> 4;
@@ -243,7 +307,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a) {
   int32_t* idl = reinterpret_cast<int32_t*>(smem + L::BYTES);  // gather mode: ids of [c0, cend)
   if constexpr (IDS) {
     const int32_t* idrow = a.ids + ((size_t)s * a.T + tq) * a.B;
-    for (int i = tid; i < cend - c0; i += 256) {
+    for (int i = tid; i < cend - c0; i += NT) {
       int c = idrow[c0 + i];
       idl[i] = c < 0 ? 0 : (c >= a.Lmax ? a.Lmax - 1 : c);
     }
@@ -266,6 +330,12 @@ __global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a) {
     u32x4 v[G::VLD];
     u32x2 ks, vs;
   };
+  // Lazy rescaling: a row's reference max moves only when a tile's max
+  // exceeds it by more than kTau (base-2 units), so p <= 2^kTau.  With int8
+  // V, P' = p * (V scale) must stay in f16 range: a tile holding a V scale
+  // above 255 tracks the exact max instead (tau 0, p <= 1).
+  constexpr float kTau = 8.0f;
+  float tau = kTau;
 
   auto issue_k = [&](int ts, KRegs& R) {
 #pragma unroll
@@ -273,7 +343,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a) {
       const uint32_t vo = cell_off(ts + 16 * cb + lr, rowstride) + 16 * lb;
 #pragma unroll
       for (int j = 0; j < G::KLD; ++j)
-        R.k[cb][j] = __builtin_amdgcn_raw_buffer_load_b128(rk, vo + 64 * j, 0, 0);
+        R.k[cb][j] = __builtin_amdgcn_raw_buffer_load_b128(rk, vo + 64 * j, 0, kNT);
     }
   };
 
@@ -282,7 +352,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a) {
     for (int u = 0; u < G::VLD; ++u) {
       const int rr = u * G::RPI + lane / G::CH;
       const uint32_t vo = cell_off(ts + rr, rowstride) + 16 * (lane % G::CH);
-      R.v[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, vo, 0, 0);
+      R.v[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, vo, 0, kNT);
     }
     if constexpr (I8) {
       const uint32_t vo = cell_off(ts + (lane & 31), srow);
@@ -306,6 +376,9 @@ __global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a) {
       *reinterpret_cast<u32x4*>(vt + G::lds_off(rr, lane % G::CH)) = R.v[u];
     }
     if constexpr (I8) {
+      bool big = f16x2_above_255(R.vs[0]);
+      if constexpr (G::NG == 4) big = big || f16x2_above_255(R.vs[1]);
+      tau = __any(big) ? 0.0f : kTau;
       // lanes 0-31 store the K scales of cells 0-31, lanes 32-63 the V scales
       uint16_t* dst = scl + (lane >> 5) * TC * G::NG + (lane & 31) * G::NG;
       const u32x2 sv = lane < 32 ? R.ks : R.vs;
@@ -409,11 +482,15 @@ __global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a) {
       float tmax = x[0];
 #pragma unroll
       for (int e = 1; e < 8; ++e) tmax = fmaxf(tmax, x[e]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      tmax = max_x32(max_x16(tmax));
+      // The reference max m_run moves only when this tile's max exceeds it
+      // by more than tau (always on a row's first visible cell); the
+      // accumulators are rescaled only then.  exp2 of the reference offset is
+      // exact math: (o, m, l) stays a valid partial for any reference m.
       const float mold = m_run[k];
-      const float mnew = fmaxf(mold, tmax);
-      const float corr = (mold == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mold - mnew);
+      const bool bump = tmax > mold + tau;
+      const float mnew = bump ? tmax : mold;
+      const float corr = bump && mold != -INFINITY ? __builtin_amdgcn_exp2f(mold - mnew) : 1.0f;
       float psum = 0.f;
       if (edge) {
 #pragma unroll
@@ -430,8 +507,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a) {
           psum += pe;
         }
       }
-      psum += __shfl_xor(psum, 16, 64);
-      psum += __shfl_xor(psum, 32, 64);
+      psum = sum_x32(sum_x16(psum));
       l_run[k] = l_run[k] * corr + psum;
       m_run[k] = mnew;
       // rescale the accumulator rows 16k+4lb+i by their row's correction
@@ -519,11 +595,13 @@ __global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a) {
     VRegs RV;
     int ts = c0 + TC * wave;
     __syncthreads();   // query operands (and ids) staged
-    issue_k(ts, RK);
+    // same issue order as inside the loop (V, then K), so the wait counts
+    // at the loop head hold on both paths into it
     issue_v(ts, RV);
+    issue_k(ts, RK);
 #pragma unroll 1
     while (ts < cend) {
-      const int tn = ts + 4 * TC;
+      const int tn = ts + NW * TC;
       stage(RV);
       issue_v(tn, RV);     // past the split's end: no memory traffic
       f32x4 S[2][NRB];
@@ -534,7 +612,11 @@ __global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a) {
     }
   }
 
-  // ---- combine the four waves: one partial per query row ----
+  // ---- combine the NW waves: one partial per query row.  Each wave
+  // rescales its accumulators to the rows' common max, the upper half of the
+  // waves parks them in LDS, the lower half adds theirs, and the NW/2 sums
+  // are added while the partial is written. ----
+  constexpr int HALF = NW / 2;
   __syncthreads();
   if (lb == 0) {
 #pragma unroll
@@ -552,15 +634,15 @@ __global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a) {
       const int row = 16 * k + 4 * lb + i;
       float M = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) M = fmaxf(M, mls[(w * RB + row) * 2]);
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, mls[(w * RB + row) * 2]);
       const float ms = mls[(wave * RB + row) * 2];
       const float f = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
 #pragma unroll
       for (int nb = 0; nb < G::NB; ++nb) O[k][nb][i] *= f;
     }
   }
-  if (wave >= 2) {
-    float* b = buf + (wave - 2) * RB * D;
+  if (wave >= HALF) {
+    float* b = buf + (wave - HALF) * RB * D;
 #pragma unroll
     for (int k = 0; k < NRB; ++k)
 #pragma unroll
@@ -569,7 +651,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a) {
         for (int i = 0; i < 4; ++i) b[(16 * k + 4 * lb + i) * D + 16 * nb + lr] = O[k][nb][i];
   }
   __syncthreads();
-  if (wave < 2) {
+  if (wave < HALF) {
     float* b = buf + wave * RB * D;
 #pragma unroll
     for (int k = 0; k < NRB; ++k)
@@ -582,26 +664,29 @@ __global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a) {
         }
   }
   __syncthreads();
-  for (int idx = tid; idx < RB * D / 4; idx += 256) {
+  for (int idx = tid; idx < RB * D / 4; idx += NT) {
     const int row = idx / (D / 4);
     const int d4 = idx % (D / 4);
     const int r = r0 + row;
     if (r < a.R) {
-      const float4 x0 = *reinterpret_cast<const float4*>(buf + row * D + 4 * d4);
-      const float4 x1 = *reinterpret_cast<const float4*>(buf + RB * D + row * D + 4 * d4);
+      float4 x = *reinterpret_cast<const float4*>(buf + row * D + 4 * d4);
+#pragma unroll
+      for (int w = 1; w < HALF; ++w) {
+        const float4 y = *reinterpret_cast<const float4*>(buf + w * RB * D + row * D + 4 * d4);
+        x.x += y.x; x.y += y.y; x.z += y.z; x.w += y.w;
+      }
       const size_t prow = ((size_t)(s * a.T + row_t(r)) * a.H + row_h(r)) * a.P + p;
-      *reinterpret_cast<float4*>(a.part_o + prow * D + 4 * d4) =
-          make_float4(x0.x + x1.x, x0.y + x1.y, x0.z + x1.z, x0.w + x1.w);
+      *reinterpret_cast<float4*>(a.part_o + prow * D + 4 * d4) = x;
     }
   }
   if (tid < RB && r0 + tid < a.R) {
     const int row = tid;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, mls[(w * RB + row) * 2]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, mls[(w * RB + row) * 2]);
     float Ls = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float mw = mls[(w * RB + row) * 2];
       if (mw != -INFINITY) Ls += mls[(w * RB + row) * 2 + 1] * __builtin_amdgcn_exp2f(mw - M);
     }

@@ -41,13 +41,13 @@ struct AttnArgs {
   float qscale;      // scale * log2(e)
 };
 
+// Arguments of the merge kernel: one output row per workgroup, P partial
+// slots per row, every slot written by the attention call.
 struct MergeArgs {
-  const float* part_o;
-  const float* part_ml;
-  const int32_t* seq_lens;
-  float* out;
-  int S, T, Lmax, B, H, P, chunk;
-  bool ids;
+  const float* part_o;     // [rows][P][D]
+  const float* part_ml;    // [rows][P][2]
+  float* out;              // [rows][D]
+  int P;
 };
 
 }  // namespace gqa_kern

@@ -8,6 +8,8 @@
 //               row and writes one partial (o unnormalised, m, l) per row.
 //   merge_rows  one workgroup per output row: log-sum-exp merge of the
 //               partials of that row's splits.
+// The attention grid is one-dimensional and ordered so that consecutive
+// workgroups, which the hardware hands to different XCDs, carry equal work.
 //
 // Sources: the whole-group workgroup that loads K/V once (cera,
 // attention_gqa.metal, header and Phase 1); the online softmax with a running
@@ -25,6 +27,7 @@
 // in base-2 units; only the merge below reads it.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -37,117 +40,170 @@ namespace {
 
 using gqa_kern::AttnArgs;
 using gqa_kern::MergeArgs;
-using gqa_kern::wave_max;
-using gqa_kern::wave_sum;
 
 constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 
-// One workgroup per output row (s, t, h).
+// One workgroup per output row (s, t, h); its four waves split the row's
+// partials (wave w takes splits w, w+4, ...) and lane l holds dims
+// l*V .. l*V+V-1 (V = D/64), so one split's o is one 16/8/4-byte load per
+// lane, 1 KB / 512 B / 256 B per wave, coalesced.  Each wave merges its
+// splits online (a running max with rescaling, the same update as the
+// attention's softmax but over partials), so every load of the row is issued
+// up front and no wave waits for another before reading o; the four waves'
+// (max, sum, o) are then combined through LDS.
 template <int D>
 __global__ __launch_bounds__(kThreads) void merge_rows(MergeArgs a) {
-  __shared__ float wgt[kThreads];
-  __shared__ float red[kThreads / 64];
-  __shared__ float bcast;
+  constexpr int V = D / 64;
+  constexpr int U = 4;                    // splits per wave whose loads are in flight together
+  __shared__ float red_o[4][D];
+  __shared__ float red_ml[4][2];
   const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
   const int row = blockIdx.x;             // ((s * T) + t) * H + h
-  const int h = row % a.H;
-  const int t = (row / a.H) % a.T;
-  const int s = row / (a.H * a.T);
-  (void)h;
-  int L = a.seq_lens[s] - (a.T - 1 - t);
-  L = L < 0 ? 0 : (L > a.Lmax ? a.Lmax : L);
-  if (a.ids) L = L < a.B ? L : a.B;
-  int nv = (L + a.chunk - 1) / a.chunk;
-  nv = nv < a.P ? nv : a.P;
-  float* out = a.out + (size_t)row * D;
-  if (nv == 0) {
-    for (int d = tid; d < D; d += kThreads) out[d] = 0.f;
-    return;
-  }
+  // The attention call writes every (row, split) slot; a split without a
+  // visible cell of the row carries m = -inf and is skipped, so the row's
+  // window need not be recomputed here and every load is issued at once.
+  const int nv = a.P;
   const float* ml = a.part_ml + (size_t)row * a.P * 2;
-  const float* po = a.part_o + (size_t)row * a.P * D;
+  const float* po = a.part_o + (size_t)row * a.P * D + lane * V;
 
-  // M = max_j m_j
-  float m = -INFINITY;
-  for (int j = tid; j < nv; j += kThreads) m = fmaxf(m, ml[2 * j]);
-  m = wave_max(m);
-  if (tid % 64 == 0) red[tid / 64] = m;
-  __syncthreads();
-  if (tid == 0) {
-    float M = red[0];
-    for (int w = 1; w < kThreads / 64; ++w) M = fmaxf(M, red[w]);
-    bcast = M;
-  }
-  __syncthreads();
-  const float M = bcast;
-  if (M == -INFINITY) {
-    for (int d = tid; d < D; d += kThreads) out[d] = 0.f;
-    return;
-  }
-  // L = sum_j exp2(m_j - M) * l_j ; out = sum_j exp2(m_j - M) * o_j / L
-  float lsum = 0.f;
-  float acc = 0.f;
-  for (int jb = 0; jb < nv; jb += kThreads) {
-    const int j = jb + tid;
-    float e = 0.f;
-    if (j < nv) {
-      const float mj = ml[2 * j];
-      e = (mj == -INFINITY) ? 0.f : exp2f(mj - M);
-      lsum = fmaf(e, ml[2 * j + 1], lsum);
+  float M = -INFINITY, lsum = 0.f;
+  float acc[V];
+#pragma unroll
+  for (int e = 0; e < V; ++e) acc[e] = 0.f;
+  for (int j0 = wave; j0 < nv; j0 += 4 * U) {
+    float mj[U], lj[U], oj[U][V];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + 4 * u;
+      mj[u] = -INFINITY;
+      lj[u] = 0.f;
+#pragma unroll
+      for (int e = 0; e < V; ++e) oj[u][e] = 0.f;
+      if (j < nv) {
+        mj[u] = ml[2 * j];
+        lj[u] = ml[2 * j + 1];
+        const float* src = po + (size_t)j * D;
+        if constexpr (V == 4) {
+          const float4 x = *reinterpret_cast<const float4*>(src);
+          oj[u][0] = x.x; oj[u][1] = x.y; oj[u][2] = x.z; oj[u][3] = x.w;
+        } else if constexpr (V == 2) {
+          const float2 x = *reinterpret_cast<const float2*>(src);
+          oj[u][0] = x.x; oj[u][1] = x.y;
+        } else {
+          oj[u][0] = *src;
+        }
+      }
     }
-    wgt[tid] = e;
-    __syncthreads();
-    const int jn = (nv - jb < kThreads) ? nv - jb : kThreads;
-    if (tid < D) {
-      for (int jj = 0; jj < jn; ++jj) acc = fmaf(wgt[jj], po[(size_t)(jb + jj) * D + tid], acc);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (mj[u] == -INFINITY) continue;   // no visible cell in that split: weight 0
+      if (mj[u] > M) {
+        const float c = (M == -INFINITY) ? 0.f : exp2f(M - mj[u]);
+        lsum *= c;
+#pragma unroll
+        for (int e = 0; e < V; ++e) acc[e] *= c;
+        M = mj[u];
+      }
+      const float w = exp2f(mj[u] - M);
+      lsum = fmaf(w, lj[u], lsum);
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[e] = fmaf(w, oj[u][e], acc[e]);
     }
-    __syncthreads();
   }
-  lsum = wave_sum(lsum);
-  if (tid % 64 == 0) red[tid / 64] = lsum;
-  __syncthreads();
-  if (tid == 0) {
-    float Ls = 0.f;
-    for (int w = 0; w < kThreads / 64; ++w) Ls += red[w];
-    bcast = Ls;
+#pragma unroll
+  for (int e = 0; e < V; ++e) red_o[wave][lane * V + e] = acc[e];
+  if (lane == 0) {
+    red_ml[wave][0] = M;
+    red_ml[wave][1] = lsum;
   }
   __syncthreads();
-  if (tid < D) out[tid] = acc / bcast;
+  if (wave == 0) {
+    float* out = a.out + (size_t)row * D + lane * V;
+    float Mt = red_ml[0][0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) Mt = fmaxf(Mt, red_ml[w][0]);
+    if (Mt == -INFINITY) {                  // no visible cell: zeros
+#pragma unroll
+      for (int e = 0; e < V; ++e) out[e] = 0.f;
+      return;
+    }
+    float f[4], Ls = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = red_ml[w][0];
+      f[w] = (mw == -INFINITY) ? 0.f : exp2f(mw - Mt);
+      Ls = fmaf(f[w], red_ml[w][1], Ls);
+    }
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      float x = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) x = fmaf(f[w], red_o[w][lane * V + e], x);
+      out[e] = x / Ls;
+    }
+  }
 }
 
-
-template <int D, bool I8, bool IDS, int NRB>
+template <int D, bool I8, bool IDS, int NRB, int NW>
 hipError_t launch_one(const AttnArgs& a, dim3 grid, hipStream_t st) {
-  constexpr int bytes = gqa_kern::AttnLds<D, I8, NRB>::BYTES +
-                        (IDS ? gqa_kern::AttnLds<D, I8, NRB>::IDSB : 0);
-  auto* fn = &gqa_kern::attn_mfma<D, I8, IDS, NRB>;
+  constexpr int bytes = gqa_kern::AttnLds<D, I8, NRB, NW>::BYTES +
+                        (IDS ? gqa_kern::AttnLds<D, I8, NRB, NW>::IDSB : 0);
+  auto* fn = &gqa_kern::attn_mfma<D, I8, IDS, NRB, NW>;
   if (bytes > 65536) {
-    static bool attr_set = false;   // per instance; set before the first launch
-    if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    // more than 64 KB of dynamic LDS must be allowed once per device
+    static std::atomic<uint64_t> attr_set{0};   // bit per device, per instance
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
+    if (!(attr_set.load(std::memory_order_acquire) & bit)) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
       if (e != hipSuccess) return e;
-      attr_set = true;
+      attr_set.fetch_or(bit, std::memory_order_acq_rel);
     }
   }
-  hipLaunchKernelGGL(fn, grid, dim3(kThreads), bytes, st, a);
+  hipLaunchKernelGGL(fn, grid, dim3(64 * NW), bytes, st, a);
   return hipGetLastError();
 }
 
+// LDS of one compute unit (gfx950).
+constexpr int kLdsPerCu = 160 * 1024;
+
+template <int D, bool I8, int NRB, int NW>
+constexpr bool fits_lds() {
+  return gqa_kern::AttnLds<D, I8, NRB, NW>::BYTES + gqa_kern::AttnLds<D, I8, NRB, NW>::IDSB <=
+         kLdsPerCu;
+}
+
+// Eight-wave workgroups where their LDS fits, four otherwise.
+template <int D, bool I8, int NRB>
+hipError_t launch_attn_nw(const AttnArgs& a, bool ids, int nw, dim3 grid, hipStream_t st) {
+  static_assert(fits_lds<D, I8, NRB, 4>(), "LDS budget");
+  if constexpr (fits_lds<D, I8, NRB, 8>()) {
+    if (nw == 8)
+      return ids ? launch_one<D, I8, true, NRB, 8>(a, grid, st)
+                 : launch_one<D, I8, false, NRB, 8>(a, grid, st);
+  }
+  return ids ? launch_one<D, I8, true, NRB, 4>(a, grid, st) : launch_one<D, I8, false, NRB, 4>(a, grid, st);
+}
+
 template <int D, bool I8>
-hipError_t launch_attn(const AttnArgs& a, bool ids, int nrows, dim3 grid, hipStream_t st) {
-  if (nrows <= 16)
-    return ids ? launch_one<D, I8, true, 1>(a, grid, st) : launch_one<D, I8, false, 1>(a, grid, st);
-  return ids ? launch_one<D, I8, true, 2>(a, grid, st) : launch_one<D, I8, false, 2>(a, grid, st);
+hipError_t launch_attn(const AttnArgs& a, bool ids, int nrows, int nw, dim3 grid, hipStream_t st) {
+  if (nrows <= 16) return launch_attn_nw<D, I8, 1>(a, ids, nw, grid, st);
+  return launch_attn_nw<D, I8, 2>(a, ids, nw, grid, st);
 }
 
 template <bool I8>
-hipError_t launch_attn_d(const AttnArgs& a, int D, bool ids, int nrows, dim3 grid, hipStream_t st) {
+hipError_t launch_attn_d(const AttnArgs& a, int D, bool ids, int nrows, int nw, dim3 grid,
+                         hipStream_t st) {
   switch (D) {
-    case 64: return launch_attn<64, I8>(a, ids, nrows, grid, st);
-    case 128: return launch_attn<128, I8>(a, ids, nrows, grid, st);
-    default: return launch_attn<256, I8>(a, ids, nrows, grid, st);
+    case 64: return launch_attn<64, I8>(a, ids, nrows, nw, grid, st);
+    case 128: return launch_attn<128, I8>(a, ids, nrows, nw, grid, st);
+    default: return launch_attn<256, I8>(a, ids, nrows, nw, grid, st);
   }
 }
 
@@ -178,10 +234,13 @@ int attn_common(bool i8, const float* q, const void* k, const void* v, const uin
   a.R = gqa::rows_per_unit(sh); a.nrb = gqa::row_blocks(sh); a.P = (int)P; a.chunk = chunk;
   a.qscale = scale * kLog2e;
   const int nrows = gqa::block_rows(sh);
-  dim3 grid((unsigned)P, (unsigned)(Hk * a.nrb * (ids ? T : 1)), (unsigned)S);
+  const int64_t nwg = P * Hk * a.nrb * (ids ? T : 1) * S;
+  if (nwg > 0x7fffffff) return GQA_ERR_SHAPE;
+  dim3 grid((unsigned)nwg);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = i8 ? launch_attn_d<true>(a, D, ids != nullptr, nrows, grid, st)
-                    : launch_attn_d<false>(a, D, ids != nullptr, nrows, grid, st);
+  const int nw = gqa::waves_per_block(sh);
+  hipError_t e = i8 ? launch_attn_d<true>(a, D, ids != nullptr, nrows, nw, grid, st)
+                    : launch_attn_d<false>(a, D, ids != nullptr, nrows, nw, grid, st);
   return e == hipSuccess ? GQA_OK : (int)e;
 }
 
@@ -218,8 +277,8 @@ int gqa_decode_merge(const float* part, const int32_t* seq_lens, const int32_t* 
   MergeArgs a;
   a.part_o = part;
   a.part_ml = part + gqa::part_o_floats(sh, P);
-  a.seq_lens = seq_lens; a.out = out;
-  a.S = S; a.T = T; a.Lmax = Lmax; a.B = sh.B; a.H = H; a.P = (int)P; a.chunk = chunk; a.ids = ids;
+  a.out = out;
+  a.P = (int)P;
   const size_t rows = (size_t)S * T * H;
   if (rows > 0x7fffffffu) return GQA_ERR_SHAPE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);

@@ -8,31 +8,35 @@ int check_shape(const Shape& s) {
   if (s.H % s.Hk != 0) return GQA_ERR_GROUP;
   if (s.D != 64 && s.D != 128 && s.D != 256) return GQA_ERR_HEAD_DIM;
   if (s.ids && s.B < 1) return GQA_ERR_BUDGET;
-  // Grid limits: y = Hk * row blocks * (T when gathering), z = S.
-  int64_t y = (int64_t)s.Hk * row_blocks(s) * (s.ids ? s.T : 1);
-  if (y > 65535 || s.S > 65535) return GQA_ERR_SHAPE;
+  // The attention grid is 1-D: S * Hk * row blocks (* T when gathering)
+  // workgroups per split; the merge grid has one workgroup per output row.
+  const int64_t units = (int64_t)s.S * s.Hk * row_blocks(s) * (s.ids ? s.T : 1);
+  if (units > 0x7fffffff || (int64_t)s.S * s.T * s.H > 0x7fffffff) return GQA_ERR_SHAPE;
   return GQA_OK;
 }
 
-// Cells per split.  The grid is S * Hk * row-blocks (* T with ids) units
-// times the split count; aim for about four workgroups per compute unit
-// (256 CUs) so every CU gets equal, overlapping work, with splits of at
-// least 64 cells so the partials (D + 2 floats per query row and split,
-// written once and read once by the merge) stay small next to the K/V
-// rows each split streams.
+// Cells per split.  The attention grid is S * Hk * row-blocks (* T with ids)
+// units times the split count.  Long splits stream best: one four-wave
+// workgroup per compute unit (256 of them), each running through a long
+// split with its K/V pipeline full, beats more and shorter workgroups that
+// share a compute unit.  So the split is sized for about 256 workgroups
+// when every sequence is full length, but at most an eighth of the window,
+// so that batches of uneven lengths (unknown on the host) still spread over
+// the compute units; and at least 64 cells.
 int auto_chunk(const Shape& s) {
   int rc = check_shape(s);
   if (rc != GQA_OK) return rc;
-  const int64_t kTargetWorkgroups = 1024;
+  const int64_t kTargetWorkgroups = 256;
+  const int64_t kMinSplitsPerUnit = 8;
   const int64_t kMinChunk = 64;
   int64_t W = width_cap(s);
   if (W <= 0) return (int)kMinChunk;
   int64_t units = (int64_t)s.S * s.Hk * row_blocks(s) * (s.ids ? s.T : 1);
   int64_t chunk = (W * units + kTargetWorkgroups - 1) / kTargetWorkgroups;
+  const int64_t eighth = (W + kMinSplitsPerUnit - 1) / kMinSplitsPerUnit;
+  if (chunk > eighth) chunk = eighth;
   if (chunk < kMinChunk) chunk = kMinChunk;
   chunk = (chunk + 63) / 64 * 64;
-  int64_t Wr = (W + 63) / 64 * 64;
-  if (chunk > Wr) chunk = Wr;
   const int64_t cap = max_chunk(s) / 64 * 64;
   if (chunk > cap) chunk = cap;
   return (int)chunk;

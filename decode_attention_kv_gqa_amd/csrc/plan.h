@@ -64,6 +64,14 @@ inline int64_t max_chunk(const Shape& s) {
   return s.ids && m > kMaxIdsChunk ? kMaxIdsChunk : m;
 }
 
+// Waves per attention workgroup (4 or 8).  Each wave streams its own
+// 32-cell tiles of the split; more waves per workgroup put more K/V bytes in
+// flight per compute unit for the same number of workgroups.
+inline int waves_per_block(const Shape& s) {
+  (void)s;
+  return 4;
+}
+
 int check_shape(const Shape& s);               // GQA_OK or GQA_ERR_*
 int auto_chunk(const Shape& s);                // > 0, or GQA_ERR_*
 size_t part_bytes(const Shape& s, int chunk);  // 0 on bad arguments

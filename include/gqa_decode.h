@@ -112,11 +112,16 @@ int gqa_decode_attn_i8(const float *q, const int8_t *k, const int8_t *v,
                        float scale, int chunk, void *stream);
 
 /* Log-sum-exp merge of the partials written by the attention call with the
- * same S, T, Lmax, B, H, D and the same RESOLVED chunk (> 0).
+ * same S, T, Lmax, B, H, D and the same RESOLVED chunk (> 0):
+ *   M = max_j m_j,  out = sum_j e^(m_j - M) o_j / sum_j e^(m_j - M) l_j
+ * (qsa2.metal, qsa_merge2).  The attention call writes every (row, split)
+ * slot of the workspace; a split holding no visible cell of a row carries
+ * m = -inf and weighs 0, so the merge reads only the workspace.
  *   part          workspace written by gqa_decode_attn_*
- *   seq_lens      [S] int32, as passed to the attention call
+ *   seq_lens      [S] int32, as passed to the attention call (must be
+ *                 non-NULL; not dereferenced)
  *   ids_or_null   the attention call's ids pointer (only its NULL-ness is
- *                 used: it selects the width rule min(L_t, B))
+ *                 used: with ids the split count follows min(B, Lmax))
  *   out           [S][T][H][D] float32; rows with an empty window get zeros
  * Errors: GQA_ERR_NULL, _SHAPE, _HEAD_DIM, _BUDGET, _CHUNK. */
 int gqa_decode_merge(const float *part, const int32_t *seq_lens, const int32_t *ids_or_null,

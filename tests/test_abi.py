@@ -60,7 +60,7 @@ def attn_f16(**kw):
     (dict(T=0), _lib.GQA_ERR_SHAPE),
     (dict(H=0), _lib.GQA_ERR_SHAPE),
     (dict(Lmax=-1), _lib.GQA_ERR_SHAPE),
-    (dict(S=70000), _lib.GQA_ERR_SHAPE),
+    (dict(S=1 << 20, H=4096), _lib.GQA_ERR_SHAPE),   # S*T*H output rows beyond 2^31 - 1
     (dict(H=9), _lib.GQA_ERR_GROUP),
     (dict(D=96), _lib.GQA_ERR_HEAD_DIM),
     (dict(D=32), _lib.GQA_ERR_HEAD_DIM),
@@ -106,8 +106,10 @@ def test_auto_chunk_plan():
         S, T, Lmax, B = args[:4]
         w = min(B, Lmax) if B else Lmax
         assert c <= max(64, (w + 63) // 64 * 64)
-    # the 32K int8 decode gets ~1024 workgroups: 8 seqs x 2 KV heads x 64 splits
-    assert ac(8, 1, 32768, 0, 24, 2, 256, 1) == 512
+    # the 32K int8 decode gets one workgroup per compute unit: 8 seqs x 2 KV
+    # heads x 16 splits of 2048 cells; uneven batches get >= 8 splits per window
+    assert ac(8, 1, 32768, 0, 24, 2, 256, 1) == 2048
+    assert ac(32, 1, 4096, 0, 32, 8, 128, 0) == 512
     assert ac(8, 1, 32768, 0, 25, 2, 256, 1) == _lib.GQA_ERR_GROUP
 
 
