@@ -6,7 +6,7 @@
 // row is fetched from HBM exactly once per split (cera, attention_gqa.metal:
 // one threadgroup per KV head for all Q heads of the group).
 //
-// The NW (4 or 8) waves of the workgroup stream 32-cell tiles independently
+// The NW (1 or 4) waves of the workgroup stream 32-cell tiles independently
 // (wave w takes tiles w, w+NW, ...) with their own online-softmax state, and combine
 // at the end through LDS into ONE partial (o unnormalised, m, l) per query
 // row — the chunk partial of qsa2.metal (qsa_attn2), merged later by the
@@ -155,8 +155,8 @@ struct TileGeom {
 // Largest split (cells) in gather mode: the split's cell ids are staged in LDS.
 constexpr int kMaxIdsChunk = 4096;
 
-// Dynamic LDS bytes of one workgroup of NW waves (plus AttnLds::IDSB in
-// gather mode).
+// Dynamic LDS bytes of one workgroup of NW waves (plus the split's cell ids,
+// 4 bytes each, in gather mode).
 template <int D, bool I8, int NRB, int NW>
 struct AttnLds {
   using G = TileGeom<D, I8>;
@@ -168,7 +168,7 @@ struct AttnLds {
   static constexpr int SC = I8 ? NW * 2 * G::TC * G::NG * 2 : 0;  // per-wave K/V scales
   static constexpr int ML = NW * RB * 2 * 4;             // per-wave (m, l)
   static constexpr int BYTES = MAIN + QB + SC + ML;
-  static constexpr int IDSB = kMaxIdsChunk * 4;          // cell ids of the split (gather mode)
+  static constexpr int IDSB = kMaxIdsChunk * 4;          // most the split's cell ids take
 };
 
 // Cache policy of the K/V row loads: non-temporal (each row is read once per
@@ -612,11 +612,35 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma(AttnArgs a) {
     }
   }
 
+  if constexpr (NW == 1) {
+    // ---- a single wave: its state is the partial.  Lane (lr, lb) holds
+    // rows 16k+4lb+i at dims 16nb+lr, and m, l of row 16k+lr. ----
+#pragma unroll
+    for (int k = 0; k < NRB; ++k) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = r0 + 16 * k + 4 * lb + i;
+        if (r < a.R) {
+          float* dst = a.part_o + (((size_t)(s * a.T + row_t(r)) * a.H + row_h(r)) * a.P + p) * D + lr;
+#pragma unroll
+          for (int nb = 0; nb < G::NB; ++nb) dst[16 * nb] = O[k][nb][i];
+        }
+      }
+      const int r = r0 + 16 * k + lr;
+      if (lb == 0 && r < a.R) {
+        const size_t prow = ((size_t)(s * a.T + row_t(r)) * a.H + row_h(r)) * a.P + p;
+        a.part_ml[prow * 2] = m_run[k];
+        a.part_ml[prow * 2 + 1] = l_run[k];
+      }
+    }
+    return;
+  }
+
   // ---- combine the NW waves: one partial per query row.  Each wave
   // rescales its accumulators to the rows' common max, the upper half of the
   // waves parks them in LDS, the lower half adds theirs, and the NW/2 sums
   // are added while the partial is written. ----
-  constexpr int HALF = NW / 2;
+  constexpr int HALF = NW / 2 > 0 ? NW / 2 : 1;
   __syncthreads();
   if (lb == 0) {
 #pragma unroll

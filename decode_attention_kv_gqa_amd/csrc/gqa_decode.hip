@@ -149,10 +149,12 @@ __global__ __launch_bounds__(kThreads) void merge_rows(MergeArgs a) {
 
 template <int D, bool I8, bool IDS, int NRB, int NW>
 hipError_t launch_one(const AttnArgs& a, dim3 grid, hipStream_t st) {
-  constexpr int bytes = gqa_kern::AttnLds<D, I8, NRB, NW>::BYTES +
-                        (IDS ? gqa_kern::AttnLds<D, I8, NRB, NW>::IDSB : 0);
+  using L = gqa_kern::AttnLds<D, I8, NRB, NW>;
+  // gather mode: the split's ids follow the fixed part, 16-byte aligned
+  const int bytes = L::BYTES + (IDS ? (a.chunk * 4 + 15) / 16 * 16 : 0);
+  constexpr int most = L::BYTES + (IDS ? L::IDSB : 0);
   auto* fn = &gqa_kern::attn_mfma<D, I8, IDS, NRB, NW>;
-  if (bytes > 65536) {
+  if constexpr (most > 65536) {
     // more than 64 KB of dynamic LDS must be allowed once per device
     static std::atomic<uint64_t> attr_set{0};   // bit per device, per instance
     int dev = 0;
@@ -161,7 +163,7 @@ hipError_t launch_one(const AttnArgs& a, dim3 grid, hipStream_t st) {
     const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
     if (!(attr_set.load(std::memory_order_acquire) & bit)) {
       e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+                              hipFuncAttributeMaxDynamicSharedMemorySize, most);
       if (e != hipSuccess) return e;
       attr_set.fetch_or(bit, std::memory_order_acq_rel);
     }
@@ -179,15 +181,13 @@ constexpr bool fits_lds() {
          kLdsPerCu;
 }
 
-// Eight-wave workgroups where their LDS fits, four otherwise.
+// One-wave workgroups for splits of at most two tiles, four waves otherwise.
 template <int D, bool I8, int NRB>
 hipError_t launch_attn_nw(const AttnArgs& a, bool ids, int nw, dim3 grid, hipStream_t st) {
-  static_assert(fits_lds<D, I8, NRB, 4>(), "LDS budget");
-  if constexpr (fits_lds<D, I8, NRB, 8>()) {
-    if (nw == 8)
-      return ids ? launch_one<D, I8, true, NRB, 8>(a, grid, st)
-                 : launch_one<D, I8, false, NRB, 8>(a, grid, st);
-  }
+  static_assert(fits_lds<D, I8, NRB, 4>() && fits_lds<D, I8, NRB, 1>(), "LDS budget");
+  if (nw == 1)
+    return ids ? launch_one<D, I8, true, NRB, 1>(a, grid, st)
+               : launch_one<D, I8, false, NRB, 1>(a, grid, st);
   return ids ? launch_one<D, I8, true, NRB, 4>(a, grid, st) : launch_one<D, I8, false, NRB, 4>(a, grid, st);
 }
 
@@ -238,7 +238,7 @@ int attn_common(bool i8, const float* q, const void* k, const void* v, const uin
   if (nwg > 0x7fffffff) return GQA_ERR_SHAPE;
   dim3 grid((unsigned)nwg);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const int nw = gqa::waves_per_block(sh);
+  const int nw = gqa::waves_per_block(sh, chunk);
   hipError_t e = i8 ? launch_attn_d<true>(a, D, ids != nullptr, nrows, nw, grid, st)
                     : launch_attn_d<false>(a, D, ids != nullptr, nrows, nw, grid, st);
   return e == hipSuccess ? GQA_OK : (int)e;

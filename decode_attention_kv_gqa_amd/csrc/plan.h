@@ -64,12 +64,13 @@ inline int64_t max_chunk(const Shape& s) {
   return s.ids && m > kMaxIdsChunk ? kMaxIdsChunk : m;
 }
 
-// Waves per attention workgroup (4 or 8).  Each wave streams its own
-// 32-cell tiles of the split; more waves per workgroup put more K/V bytes in
-// flight per compute unit for the same number of workgroups.
-inline int waves_per_block(const Shape& s) {
+// Waves per attention workgroup.  Each wave streams its own 32-cell tiles
+// of the split (wave w: tiles w, w+NW, ...), so a split of at most two tiles
+// gets a one-wave workgroup (no idle waves, no cross-wave combine); longer
+// splits get four waves, one per SIMD.
+inline int waves_per_block(const Shape& s, int chunk) {
   (void)s;
-  return 4;
+  return chunk <= 64 ? 1 : 4;
 }
 
 int check_shape(const Shape& s);               // GQA_OK or GQA_ERR_*
