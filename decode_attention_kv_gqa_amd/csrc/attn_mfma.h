@@ -150,6 +150,13 @@ struct TileGeom {
     }
   }
   __device__ static int lds_off(int r, int c) { return r * RBY + ((c ^ swz(r)) << 4); }
+  // K tile swizzle: the 16-byte chunks of consecutive rows rotate through the
+  // 16 bank groups of a 256-byte period, so the row-major writes and the
+  // MFMA-operand reads (16 rows x 4 chunks per instruction) are both
+  // conflict-free.
+  static constexpr int SHK = RBY >= 256 ? 0 : (RBY == 128 ? 1 : 2);
+  __device__ static int swzk(int r) { return (r >> SHK) & (CH < 16 ? CH - 1 : 15); }
+  __device__ static int lds_offk(int r, int c) { return r * RBY + ((c ^ swzk(r)) << 4); }
 };
 
 // Largest split (cells) in gather mode: the split's cell ids are staged in LDS.
@@ -161,14 +168,24 @@ template <int D, bool I8, int NRB, int NW>
 struct AttnLds {
   using G = TileGeom<D, I8>;
   static constexpr int RB = 16 * NRB;
-  static constexpr int VT = NW * G::TC * G::RBY;         // per-wave V tiles
-  static constexpr int BUF = NW / 2 * RB * D * 4;        // cross-wave merge buffers (alias VT)
-  static constexpr int MAIN = VT > BUF ? VT : BUF;
+  static constexpr int VT = NW * G::TC * G::RBY;         // per-wave V tiles (and K tiles)
+  static constexpr int BUF = NW / 2 * RB * D * 4;        // cross-wave merge buffers (alias tiles)
   static constexpr int QB = NRB * G::KS * 2 * 64 * 16;   // query B operands, hi and lo
   static constexpr int SC = I8 ? NW * 2 * G::TC * G::NG * 2 : 0;  // per-wave K/V scales
   static constexpr int ML = NW * RB * 2 * 4;             // per-wave (m, l)
-  static constexpr int BYTES = MAIN + QB + SC + ML;
   static constexpr int IDSB = kMaxIdsChunk * 4;          // most the split's cell ids take
+  static constexpr int CAP = 160 * 1024;                 // LDS of one compute unit
+  // f16 K rows are staged through LDS like V when both tiles fit: then K is
+  // read from HBM in whole rows (fully used cache lines) and the next tile's
+  // K and V are both requested as soon as the current ones are staged
+  // (measured: multi-query causal 128K 356 -> 330 us, uneven batch 76 ->
+  // 64 us).  int8 K, whose path is already bound by the vector ALU, and
+  // tiles that do not fit load each lane's K operand fragment straight into
+  // registers (int8 32K: 50 us that way, 55 us through LDS).
+  static constexpr int MAIN_KL = 2 * VT > BUF ? 2 * VT : BUF;
+  static constexpr bool KL = !I8 && MAIN_KL + QB + SC + ML + IDSB <= CAP;
+  static constexpr int MAIN = KL ? MAIN_KL : (VT > BUF ? VT : BUF);
+  static constexpr int BYTES = MAIN + QB + SC + ML;
 };
 
 // Cache policy of the K/V row loads: non-temporal (each row is read once per
@@ -245,6 +262,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma(AttnArgs a) {
   const int lim_lo = width_of(r0) < cend ? width_of(r0) : cend;
 
   uint8_t* vt = smem + wave * TC * RBY;                       // this wave's V tile
+  uint8_t* kt = smem + L::VT + wave * TC * RBY;               // this wave's K tile (L::KL)
   u32x4* qlds = reinterpret_cast<u32x4*>(smem + L::MAIN);
   uint16_t* scl = reinterpret_cast<uint16_t*>(smem + L::MAIN + L::QB) + wave * 2 * TC * G::NG;
   float* mls = reinterpret_cast<float*>(smem + L::MAIN + L::QB + L::SC);
@@ -324,7 +342,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma(AttnArgs a) {
   };
 
   struct KRegs {
-    u32x4 k[2][G::KLD];
+    u32x4 k[L::KL ? G::VLD : 2 * G::KLD];
   };
   struct VRegs {
     u32x4 v[G::VLD];
@@ -338,12 +356,21 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma(AttnArgs a) {
   float tau = kTau;
 
   auto issue_k = [&](int ts, KRegs& R) {
+    if constexpr (L::KL) {       // whole rows, as V
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      const uint32_t vo = cell_off(ts + 16 * cb + lr, rowstride) + 16 * lb;
+      for (int u = 0; u < G::VLD; ++u) {
+        const int rr = u * G::RPI + lane / G::CH;
+        const uint32_t vo = cell_off(ts + rr, rowstride) + 16 * (lane % G::CH);
+        R.k[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, vo, 0, kNT);
+      }
+    } else {                     // the lane's MFMA operand fragments
 #pragma unroll
-      for (int j = 0; j < G::KLD; ++j)
-        R.k[cb][j] = __builtin_amdgcn_raw_buffer_load_b128(rk, vo + 64 * j, 0, kNT);
+      for (int cb = 0; cb < 2; ++cb) {
+        const uint32_t vo = cell_off(ts + 16 * cb + lr, rowstride) + 16 * lb;
+#pragma unroll
+        for (int j = 0; j < G::KLD; ++j)
+          R.k[cb * G::KLD + j] = __builtin_amdgcn_raw_buffer_load_b128(rk, vo + 64 * j, 0, kNT);
+      }
     }
   };
 
@@ -369,11 +396,13 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma(AttnArgs a) {
     }
   };
 
-  auto stage = [&](const VRegs& R) {
+  auto stage = [&](const VRegs& R, const KRegs& RK) {
 #pragma unroll
     for (int u = 0; u < G::VLD; ++u) {
       const int rr = u * G::RPI + lane / G::CH;
       *reinterpret_cast<u32x4*>(vt + G::lds_off(rr, lane % G::CH)) = R.v[u];
+      if constexpr (L::KL)
+        *reinterpret_cast<u32x4*>(kt + G::lds_offk(rr, lane % G::CH)) = RK.k[u];
     }
     if constexpr (I8) {
       bool big = f16x2_above_255(R.vs[0]);
@@ -403,6 +432,15 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma(AttnArgs a) {
     for (int nb = 0; nb < G::NB; ++nb) O[k][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
+  // K operand fragment of lane (lr, lb) for cell block cb, 16-byte chunk
+  // lb + 4j of the row: dims 8lb + 32j .. +7 (f16) or 16lb + 64j .. +15 (int8)
+  auto kfrag = [&](const KRegs& R, int cb, int j) -> u32x4 {
+    if constexpr (L::KL)
+      return *reinterpret_cast<const u32x4*>(kt + G::lds_offk(16 * cb + lr, lb + 4 * j));
+    else
+      return R.k[cb * G::KLD + j];
+  };
+
   // ---- QK: S[cb][k][i] = score of cell ts+16cb+4lb+i for row 16k+lr ----
   auto qk = [&](const KRegs& R, f32x4 (&S)[2][NRB]) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -419,7 +457,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma(AttnArgs a) {
           const half8 ql = __builtin_bit_cast(half8, qlds[((k * G::KS + ks) * 2 + 1) * 64 + lane]);
 #pragma unroll
           for (int cb = 0; cb < 2; ++cb) {
-            const half8 ka = __builtin_bit_cast(half8, R.k[cb][ks]);
+            const half8 ka = __builtin_bit_cast(half8, kfrag(R, cb, ks));
             S[cb][k] = mfma16(ka, qh, S[cb][k]);
             S[cb][k] = mfma16(ka, ql, S[cb][k]);
           }
@@ -431,8 +469,9 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma(AttnArgs a) {
         half8 k0[2], k1[2];
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
-          k0[cb] = i8x8_to_half8(R.k[cb][gi][0], R.k[cb][gi][1]);
-          k1[cb] = i8x8_to_half8(R.k[cb][gi][2], R.k[cb][gi][3]);
+          const u32x4 w = kfrag(R, cb, gi);
+          k0[cb] = i8x8_to_half8(w[0], w[1]);
+          k1[cb] = i8x8_to_half8(w[2], w[3]);
         }
 #pragma unroll
         for (int k = 0; k < NRB; ++k) {
@@ -602,11 +641,16 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma(AttnArgs a) {
 #pragma unroll 1
     while (ts < cend) {
       const int tn = ts + NW * TC;
-      stage(RV);
+      stage(RV, RK);
       issue_v(tn, RV);     // past the split's end: no memory traffic
       f32x4 S[2][NRB];
-      qk(RK, S);
-      issue_k(tn, RK);
+      if constexpr (L::KL) {
+        issue_k(tn, RK);
+        qk(RK, S);
+      } else {
+        qk(RK, S);
+        issue_k(tn, RK);
+      }
       softmax_pv(ts, S);
       ts = tn;
     }
