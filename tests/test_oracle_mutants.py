@@ -28,18 +28,41 @@ MUTANTS = {
 }
 
 
-@pytest.mark.parametrize("name", sorted(MUTANTS))
-def test_pins_catch_mutant(name, tmp_path):
-    before, after = MUTANTS[name]
-    src = open(os.path.join(ROOT, "oracle", "decode_ref.py")).read()
+# Budget-selection oracle (oracle/select_ref.py) against tests/test_oracle_select.py.
+SELECT_MUTANTS = {
+    "okey_ignores_sign": ("return np.where(neg, ~bits, bits | np.uint32(0x80000000))",
+                          "return np.where(neg, bits, bits | np.uint32(0x80000000))"),
+    "ties_to_later_block": ('order = np.argsort(-keys, kind="stable")',
+                            'order = np.argsort(-keys, kind="stable")[::-1][np.argsort(-np.sort(-keys)[::-1], kind="stable")]'),
+    "last_block_counts_four": ("cells_in[-1] = n % 4", "cells_in[-1] = 4"),
+    "budget_off_by_one": ("left = B\n", "left = B - 1\n"),
+    "partial_block_dropped": ("nb = n // 4 + 1\n    keys", "nb = max(1, n // 4)\n    keys"),
+    "ascending_scores": ('order = np.argsort(-keys, kind="stable")', 'order = np.argsort(keys, kind="stable")'),
+}
+
+
+def run_mutant(tmp_path, module, test_file, before, after, name):
+    src = open(os.path.join(ROOT, "oracle", module)).read()
     assert before in src, f"mutation site for {name} no longer exists"
     shutil.copytree(os.path.join(ROOT, "oracle"), tmp_path / "oracle")
     shutil.copytree(os.path.join(ROOT, "workloads"), tmp_path / "workloads")
     (tmp_path / "tests").mkdir()
-    for f in ("conftest.py", "test_oracle.py"):
+    for f in ("conftest.py", test_file):
         shutil.copy(os.path.join(ROOT, "tests", f), tmp_path / "tests" / f)
-    (tmp_path / "oracle" / "decode_ref.py").write_text(src.replace(before, after, 1))
+    (tmp_path / "oracle" / module).write_text(src.replace(before, after, 1))
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
-                        "tests/test_oracle.py"], cwd=tmp_path, capture_output=True, text=True,
+                        "tests/" + test_file], cwd=tmp_path, capture_output=True, text=True,
                        timeout=300)
     assert r.returncode == 1, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path):
+    before, after = MUTANTS[name]
+    run_mutant(tmp_path, "decode_ref.py", "test_oracle.py", before, after, name)
+
+
+@pytest.mark.parametrize("name", sorted(SELECT_MUTANTS))
+def test_select_pins_catch_mutant(name, tmp_path):
+    before, after = SELECT_MUTANTS[name]
+    run_mutant(tmp_path, "select_ref.py", "test_oracle_select.py", before, after, name)

@@ -29,7 +29,7 @@ from typing import Optional
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "WORKLOAD_ORDER", "make_inputs", "make_case",
-           "Inputs", "kv_bytes"]
+           "Inputs", "kv_bytes", "make_block_scores", "SELECT_WORKLOADS"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -204,3 +204,25 @@ def kv_bytes(inp: Inputs) -> int:
                 w = min(Lt, B)
                 total += 2 * row * Hk * w + 4 * w
     return total
+
+
+# ---------------------------------------------------------------------------
+# Block scores for the budget selection (one score per 4-cell block).  How
+# the scores are produced is not on the source pages (qsa2.metal reads them
+# from a buffer), so they are synthetic: fp32 N(0,1), or, for tie-heavy
+# cases, small integers so many blocks share a score.
+
+SELECT_WORKLOADS = {
+    # the selection step of the budgeted int8 decode: 8 sequences at context
+    # 65536, a budget of 2048 cells per token
+    "select_64k": dict(S=8, T=1, Lmax=65536, B=2048, lens="full", index=5),
+}
+
+
+def make_block_scores(S: int, T: int, Lmax: int, seed: int = 0, ties: bool = False) -> np.ndarray:
+    """[S][T][Lmax // 4 + 1] float32 block scores."""
+    rng = np.random.default_rng(np.random.SeedSequence(seed))
+    shape = (S, T, Lmax // 4 + 1)
+    if ties:
+        return rng.integers(-3, 4, size=shape).astype(np.float32)
+    return rng.standard_normal(shape, dtype=np.float32)
