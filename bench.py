@@ -127,6 +127,44 @@ def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
                       "copy_GBps": round(2 * nbytes / dt / 1e9, 1)}), flush=True)
 
 
+def bench_select(args):
+    """Budget-selection kernel alone (gqa_decode_select_ids) on a selection
+    workload: block scores resident in HBM, K launches timed with HIP events
+    after W warm-up launches.  One JSON line."""
+    import numpy as np
+    import torch
+    import decode_attention_kv_gqa_amd as gq
+    from workloads import SELECT_WORKLOADS, make_block_scores
+    w = SELECT_WORKLOADS[args.workload]
+    S, T, Lmax, B = w["S"], w["T"], w["Lmax"], w["B"]
+    dev = torch.device("cuda:0")
+    bs = torch.from_numpy(make_block_scores(S, T, Lmax, seed=1000 + w["index"])).to(dev)
+    lens = torch.full((S,), Lmax, dtype=torch.int32, device=dev)
+    out = torch.full((S, T, B), -1, dtype=torch.int32, device=dev)
+    for _ in range(args.warmup):
+        gq.select_ids(bs, lens, B, out=out)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    a.record(stream)
+    for _ in range(args.steps):
+        gq.select_ids(bs, lens, B, out=out)
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / args.steps * 1e3
+    nbytes = S * T * ((Lmax // 4 + 1) * 4 + B * 4)    # scores read once + ids written
+    print(json.dumps({
+        "metric": "budget selection us per call", "value": round(us, 3), "unit": "us",
+        "higher_is_better": False, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "dtype": "f32 keys", "data": "synthetic (seeded numpy: block scores N(0,1) fp32)",
+        "config": {"workload": args.workload, "S": S, "T": T, "Lmax": Lmax, "budget": B,
+                   "algorithmic_bytes": nbytes},
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / us / 1e3, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 5), "traffic": None,
+                     "note": "one workgroup per token; latency-bound at this size"}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -152,11 +190,14 @@ def main():
     import numpy as np
     import torch
     import decode_attention_kv_gqa_amd as gq
-    from workloads import WORKLOADS, make_inputs, kv_bytes
+    from workloads import WORKLOADS, SELECT_WORKLOADS, make_inputs, kv_bytes
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.workload in SELECT_WORKLOADS:
+        bench_select(args)
+        return
     w = WORKLOADS[args.workload]
     chunk = w.chunk if args.chunk < 0 else args.chunk
     t_gen = time.perf_counter()

@@ -12,10 +12,12 @@ from typing import Optional
 
 from . import _lib
 from ._lib import (GqaDecodeError, gqa_decode_attn_f16, gqa_decode_attn_i8, gqa_decode_merge,
+                   gqa_decode_select_ids,
                    gqa_decode_part_bytes, gqa_decode_auto_chunk, strerror)
 
 __all__ = ["decode_attention", "DecodeAttention", "GqaDecodeError", "gqa_decode_attn_f16",
-           "gqa_decode_attn_i8", "gqa_decode_merge", "gqa_decode_part_bytes",
+           "gqa_decode_attn_i8", "gqa_decode_merge", "gqa_decode_select_ids", "select_ids",
+           "gqa_decode_part_bytes",
            "gqa_decode_auto_chunk", "strerror"]
 
 
@@ -133,3 +135,26 @@ def decode_attention(q, k, v, seq_lens, scale: Optional[float] = None, *, k_scal
     kv = "i8" if str(k.dtype) == "torch.int8" else "f16"
     step = DecodeAttention(S, T, H, Hk, D, Lmax, kv, B=B, chunk=chunk, device=q.device)
     return step(q, k, v, seq_lens, scale, k_scales, v_scales, ids).clone()
+
+
+def select_ids(block_scores, seq_lens, B: int, out=None):
+    """Budget selection on the GPU.  block_scores [S][T][Lmax // 4 + 1]
+    float32, seq_lens [S] int32; returns ids [S][T][B] int32 whose first
+    min(L_t, B) entries per token are defined (the rest keep `out`'s contents,
+    -1 for a fresh output)."""
+    import torch
+    for name, t in (("block_scores", block_scores), ("seq_lens", seq_lens)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if block_scores.dtype != torch.float32 or seq_lens.dtype != torch.int32:
+        raise ValueError("block_scores must be float32 and seq_lens int32")
+    S, T, nbs = block_scores.shape
+    Lmax = 4 * (nbs - 1)
+    if out is None:
+        out = torch.full((S, T, B), -1, dtype=torch.int32, device=block_scores.device)
+    st = torch.cuda.current_stream(block_scores.device).cuda_stream
+    rc = gqa_decode_select_ids(block_scores.data_ptr(), seq_lens.data_ptr(), out.data_ptr(), S, T,
+                               Lmax, B, st)
+    if rc:
+        raise GqaDecodeError("gqa_decode_select_ids", rc)
+    return out

@@ -7,6 +7,9 @@
  *   gqa_decode_attn_f16 / gqa_decode_attn_i8   chunk partials (o, m, l)
  *   gqa_decode_merge                            log-sum-exp merge -> out
  *
+ * preceded, for budgeted attention, by gqa_decode_select_ids (the B cell ids
+ * of every token from per-block scores).
+ *
  * What is computed, for sequence s, query token t and query head h
  * (G = H / Hk query heads share KV head g = h / G):
  *
@@ -127,6 +130,22 @@ int gqa_decode_attn_i8(const float *q, const int8_t *k, const int8_t *v,
 int gqa_decode_merge(const float *part, const int32_t *seq_lens, const int32_t *ids_or_null,
                      float *out, int S, int T, int Lmax, int B, int H, int D, int chunk,
                      void *stream);
+
+/* Budget selection: the ids a budgeted token attends (qsa2.metal, kernel
+ * qsa_topk2).  Cells come in blocks of 4 with one score per block; with
+ * n = L_t visible cells (the causal window of token t, as in the attention
+ * calls), block b < n/4 holds cells 4b..4b+3 and block n/4 the n%4 remaining
+ * ones.  ids[s][t][0..B) = the first B cells ranked by (block score
+ * descending, cell index ascending), in ascending order; when n <= B,
+ * ids[s][t][0..n) = 0..n-1 and the rest of the row is left untouched.
+ * Scores compare as floats (an order-preserving key; -0 below +0).
+ *   block_scores  [S][T][Lmax/4 + 1] float32
+ *   seq_lens      [S] int32, as for the attention calls
+ *   ids           [S][T][B] int32 (written)
+ * The output feeds gqa_decode_attn_* (ids, B).  Errors: GQA_ERR_NULL,
+ * _SHAPE, _BUDGET. */
+int gqa_decode_select_ids(const float *block_scores, const int32_t *seq_lens, int32_t *ids,
+                          int S, int T, int Lmax, int B, void *stream);
 
 /* Static text for a return code. */
 const char *gqa_decode_strerror(int code);

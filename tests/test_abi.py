@@ -119,3 +119,12 @@ def test_python_wrapper_refuses_cpu_tensors():
     k = torch.zeros(1, 4, 2, 64, dtype=torch.float16)
     with pytest.raises(ValueError, match="GPU"):
         gq.decode_attention(q, k, k, torch.ones(1, dtype=torch.int32))
+
+
+def test_select_rejects():
+    f = gq.gqa_decode_select_ids
+    assert f(None, FAKE, FAKE, 1, 1, 64, 8, 0) == _lib.GQA_ERR_NULL
+    assert f(FAKE, FAKE, None, 1, 1, 64, 8, 0) == _lib.GQA_ERR_NULL
+    assert f(FAKE, FAKE, FAKE, 0, 1, 64, 8, 0) == _lib.GQA_ERR_SHAPE
+    assert f(FAKE, FAKE, FAKE, 1, 1, -4, 8, 0) == _lib.GQA_ERR_SHAPE
+    assert f(FAKE, FAKE, FAKE, 1, 1, 64, 0, 0) == _lib.GQA_ERR_BUDGET
