@@ -41,6 +41,18 @@ SELECT_MUTANTS = {
 }
 
 
+# Quantize-on-append oracle (oracle/append_ref.py) against tests/test_oracle_append.py.
+APPEND_MUTANTS = {
+    "round_half_away": ("np.rint(g / d)", "np.trunc(g / d + np.copysign(np.float32(0.5), g))"),
+    "group_of_32": ("g = x.reshape(x.shape[:-1] + (D // 64, 64))",
+                    "g = x.reshape(x.shape[:-1] + (D // 32, 32))[..., ::2, :].repeat(2, axis=-2)"),
+    "clamp_126": ("np.clip(q, -127.0, 127.0)", "np.clip(q, -126.0, 126.0)"),
+    "code_from_f16_scale": ("np.rint(g / d)", "np.rint(g / d.astype(np.float16).astype(np.float32))"),
+    "divide_by_128": ("d = (amax / np.float32(127.0))", "d = (amax / np.float32(128.0))"),
+    "write_off_by_one": ("c = int(pos[s]) + i\n", "c = int(pos[s]) + i + 1\n"),
+}
+
+
 def run_mutant(tmp_path, module, test_file, before, after, name):
     src = open(os.path.join(ROOT, "oracle", module)).read()
     assert before in src, f"mutation site for {name} no longer exists"
@@ -66,3 +78,9 @@ def test_pins_catch_mutant(name, tmp_path):
 def test_select_pins_catch_mutant(name, tmp_path):
     before, after = SELECT_MUTANTS[name]
     run_mutant(tmp_path, "select_ref.py", "test_oracle_select.py", before, after, name)
+
+
+@pytest.mark.parametrize("name", sorted(APPEND_MUTANTS))
+def test_append_pins_catch_mutant(name, tmp_path):
+    before, after = APPEND_MUTANTS[name]
+    run_mutant(tmp_path, "append_ref.py", "test_oracle_append.py", before, after, name)

@@ -29,7 +29,8 @@ from typing import Optional
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "WORKLOAD_ORDER", "make_inputs", "make_case",
-           "Inputs", "kv_bytes", "make_block_scores", "SELECT_WORKLOADS"]
+           "Inputs", "kv_bytes", "make_block_scores", "SELECT_WORKLOADS", "APPEND_WORKLOADS",
+           "make_append_rows"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -226,3 +227,21 @@ def make_block_scores(S: int, T: int, Lmax: int, seed: int = 0, ties: bool = Fal
     if ties:
         return rng.integers(-3, 4, size=shape).astype(np.float32)
     return rng.standard_normal(shape, dtype=np.float32)
+
+
+# ---------------------------------------------------------------------------
+# New fp32 K/V rows for quantize-on-append (fp32 N(0,1), as the projections
+# that produce them would; the source pages do not say).
+
+APPEND_WORKLOADS = {
+    # a 4096-token chunk appended to the int8 32K cache shape
+    "append_i8": dict(S=8, Tn=4096, Hk=2, D=256, Lmax=32768, pos=16384, index=6),
+}
+
+
+def make_append_rows(S: int, Tn: int, Hk: int, D: int, seed: int = 0):
+    """k_new, v_new [S][Tn][Hk][D] float32."""
+    ss = np.random.SeedSequence(seed)
+    rk, rv = [np.random.default_rng(c) for c in ss.spawn(2)]
+    return (rk.standard_normal((S, Tn, Hk, D), dtype=np.float32),
+            rv.standard_normal((S, Tn, Hk, D), dtype=np.float32))
