@@ -165,6 +165,52 @@ def bench_select(args):
                      "note": "one workgroup per token; latency-bound at this size"}}), flush=True)
 
 
+def bench_append(args):
+    """Quantize-on-append kernel alone (gqa_decode_append_i8): new fp32 rows
+    and the int8 cache resident in HBM, K launches timed with HIP events
+    after W warm-up launches.  One JSON line."""
+    import torch
+    import decode_attention_kv_gqa_amd as gq
+    from workloads import APPEND_WORKLOADS, make_append_rows
+    w = APPEND_WORKLOADS[args.workload]
+    S, Tn, Hk, D, Lmax = w["S"], w["Tn"], w["Hk"], w["D"], w["Lmax"]
+    dev = torch.device("cuda:0")
+    rows = make_append_rows(S, Tn, Hk, D, seed=1000 + w["index"])
+    # several copies of the new rows, rotated, so a launch never finds its
+    # input in the 256 MB last-level cache
+    copies = max(2, math.ceil(2 * LLC_BYTES / (2 * rows[0].nbytes)) + 1)
+    sets = [[torch.from_numpy(x).to(dev) for x in rows] for _ in range(copies)]
+    pos = torch.full((S,), w["pos"], dtype=torch.int32, device=dev)
+    k = torch.zeros((S, Lmax, Hk, D), dtype=torch.int8, device=dev)
+    v = torch.zeros_like(k)
+    ks = torch.zeros((S, Lmax, Hk, D // 64), dtype=torch.float16, device=dev)
+    vs = torch.zeros_like(ks)
+    for i in range(args.warmup):
+        gq.append_i8(*sets[i % copies], pos, k, v, ks, vs)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    a.record(stream)
+    for i in range(args.steps):
+        gq.append_i8(*sets[i % copies], pos, k, v, ks, vs)
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / args.steps * 1e3
+    elems = 2 * S * Tn * Hk * D
+    nbytes = elems * 4 + elems + elems // 64 * 2           # fp32 read, codes + scales written
+    achieved = nbytes / us / 1e3
+    print(json.dumps({
+        "metric": "quantize-on-append GB/s", "value": round(achieved, 2), "unit": "GB/s",
+        "higher_is_better": True, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "us_per_call": round(us, 3), "dtype": "f32 -> i8",
+        "data": "synthetic (seeded numpy: new rows N(0,1) fp32)",
+        "config": {"workload": args.workload, "S": S, "Tn": Tn, "Hk": Hk, "D": D, "Lmax": Lmax,
+                   "algorithmic_bytes": nbytes, "input_copies_rotated": copies},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -190,13 +236,16 @@ def main():
     import numpy as np
     import torch
     import decode_attention_kv_gqa_amd as gq
-    from workloads import WORKLOADS, SELECT_WORKLOADS, make_inputs, kv_bytes
+    from workloads import WORKLOADS, SELECT_WORKLOADS, APPEND_WORKLOADS, make_inputs, kv_bytes
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     if args.workload in SELECT_WORKLOADS:
         bench_select(args)
+        return
+    if args.workload in APPEND_WORKLOADS:
+        bench_append(args)
         return
     w = WORKLOADS[args.workload]
     chunk = w.chunk if args.chunk < 0 else args.chunk

@@ -12,11 +12,12 @@ from typing import Optional
 
 from . import _lib
 from ._lib import (GqaDecodeError, gqa_decode_attn_f16, gqa_decode_attn_i8, gqa_decode_merge,
-                   gqa_decode_select_ids,
+                   gqa_decode_select_ids, gqa_decode_append_i8,
                    gqa_decode_part_bytes, gqa_decode_auto_chunk, strerror)
 
 __all__ = ["decode_attention", "DecodeAttention", "GqaDecodeError", "gqa_decode_attn_f16",
            "gqa_decode_attn_i8", "gqa_decode_merge", "gqa_decode_select_ids", "select_ids",
+           "gqa_decode_append_i8", "append_i8",
            "gqa_decode_part_bytes",
            "gqa_decode_auto_chunk", "strerror"]
 
@@ -158,3 +159,28 @@ def select_ids(block_scores, seq_lens, B: int, out=None):
     if rc:
         raise GqaDecodeError("gqa_decode_select_ids", rc)
     return out
+
+
+def append_i8(k_new, v_new, pos, k, v, k_scales, v_scales):
+    """Quantize-on-append in place.  k_new, v_new [S][Tn][Hk][D] float32;
+    pos [S] int32; k, v [S][Lmax][Hk][D] int8; k_scales, v_scales
+    [S][Lmax][Hk][D/64] float16 (all contiguous GPU tensors)."""
+    import torch
+    for name, t in (("k_new", k_new), ("v_new", v_new), ("pos", pos), ("k", k), ("v", v),
+                    ("k_scales", k_scales), ("v_scales", v_scales)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if k_new.dtype != torch.float32 or v_new.dtype != torch.float32 or pos.dtype != torch.int32 \
+            or k.dtype != torch.int8 or v.dtype != torch.int8 \
+            or k_scales.dtype != torch.float16 or v_scales.dtype != torch.float16:
+        raise ValueError("dtypes: k_new/v_new float32, pos int32, k/v int8, scales float16")
+    S, Tn, Hk, D = k_new.shape
+    _, Lmax, Hk2, D2 = k.shape
+    if (Hk2, D2) != (Hk, D) or v_new.shape != k_new.shape or v.shape != k.shape:
+        raise ValueError("shape mismatch between new rows and caches")
+    st = torch.cuda.current_stream(k.device).cuda_stream
+    rc = gqa_decode_append_i8(k_new.data_ptr(), v_new.data_ptr(), pos.data_ptr(), k.data_ptr(),
+                              v.data_ptr(), k_scales.data_ptr(), v_scales.data_ptr(), S, Tn, Lmax,
+                              Hk, D, st)
+    if rc:
+        raise GqaDecodeError("gqa_decode_append_i8", rc)

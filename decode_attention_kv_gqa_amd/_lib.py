@@ -22,7 +22,8 @@ GQA_ERR_CHUNK = -6
 GQA_ERR_WORKSPACE = -7
 
 EXPORTED = ["gqa_decode_attn_f16", "gqa_decode_attn_i8", "gqa_decode_merge",
-            "gqa_decode_select_ids", "gqa_decode_part_bytes", "gqa_decode_auto_chunk",
+            "gqa_decode_select_ids", "gqa_decode_append_i8", "gqa_decode_part_bytes",
+            "gqa_decode_auto_chunk",
             "gqa_decode_strerror"]
 
 _lib = None
@@ -53,6 +54,8 @@ def load() -> ctypes.CDLL:
     lib.gqa_decode_merge.restype = i32
     lib.gqa_decode_select_ids.argtypes = [vp, vp, vp] + [i32] * 4 + [vp]
     lib.gqa_decode_select_ids.restype = i32
+    lib.gqa_decode_append_i8.argtypes = [vp] * 7 + [i32] * 5 + [vp]
+    lib.gqa_decode_append_i8.restype = i32
     lib.gqa_decode_part_bytes.argtypes = [i32] * 7
     lib.gqa_decode_part_bytes.restype = sz
     lib.gqa_decode_auto_chunk.argtypes = [i32] * 8
@@ -100,3 +103,9 @@ def gqa_decode_auto_chunk(S, T, Lmax, B, H, Hk, D, kv_is_i8) -> int:
 def gqa_decode_select_ids(block_scores, seq_lens, ids, S, T, Lmax, B, stream=0) -> int:
     return load().gqa_decode_select_ids(_p(block_scores), _p(seq_lens), _p(ids), S, T, Lmax, B,
                                         _p(stream))
+
+
+def gqa_decode_append_i8(k_new, v_new, pos, k, v, k_scales, v_scales, S, Tn, Lmax, Hk, D,
+                         stream=0) -> int:
+    return load().gqa_decode_append_i8(_p(k_new), _p(v_new), _p(pos), _p(k), _p(v), _p(k_scales),
+                                       _p(v_scales), S, Tn, Lmax, Hk, D, _p(stream))

@@ -8,7 +8,8 @@
  *   gqa_decode_merge                            log-sum-exp merge -> out
  *
  * preceded, for budgeted attention, by gqa_decode_select_ids (the B cell ids
- * of every token from per-block scores).
+ * of every token from per-block scores); gqa_decode_append_i8 writes new K/V
+ * rows into the int8 cache the int8 call reads.
  *
  * What is computed, for sequence s, query token t and query head h
  * (G = H / Hk query heads share KV head g = h / G):
@@ -146,6 +147,23 @@ int gqa_decode_merge(const float *part, const int32_t *seq_lens, const int32_t *
  * _SHAPE, _BUDGET. */
 int gqa_decode_select_ids(const float *block_scores, const int32_t *seq_lens, int32_t *ids,
                           int S, int T, int Lmax, int B, void *stream);
+
+/* Quantize-on-append: new fp32 K and V rows written into the int8 cache
+ * (FORWARD_MSL, kernel kv_append_q8, with 64-element groups as the cache the
+ * attention reads).  For every 64-element group x of a new row, in fp32:
+ *   d = max|x| / 127,  code = clamp(rint(x / d), -127, 127) (0 when d == 0),
+ *   stored scale = f16(d)   (IEEE division, rint rounds halves to even).
+ *   k_new, v_new        [S][Tn][Hk][D] float32, D a multiple of 64
+ *   pos                 [S] int32: cell of the first new row of sequence s;
+ *                       row i goes to cell pos[s] + i, and cells outside
+ *                       [0, Lmax) are skipped (a bad position only truncates)
+ *   k, v                [S][Lmax][Hk][D] int8 caches (rows written in place)
+ *   k_scales, v_scales  [S][Lmax][Hk][D/64] f16 bits (written in place)
+ * Tn == 0 or Lmax == 0 enqueues nothing.  Errors: GQA_ERR_NULL, _SHAPE,
+ * _HEAD_DIM (D not a positive multiple of 64). */
+int gqa_decode_append_i8(const float *k_new, const float *v_new, const int32_t *pos,
+                         int8_t *k, int8_t *v, uint16_t *k_scales, uint16_t *v_scales,
+                         int S, int Tn, int Lmax, int Hk, int D, void *stream);
 
 /* Static text for a return code. */
 const char *gqa_decode_strerror(int code);

@@ -44,7 +44,8 @@ def quantize_groups(x: np.ndarray):
         q = np.where(d > 0, np.rint(g / d), np.float32(0.0)).astype(np.float32)
     q = np.clip(q, -127.0, 127.0)
     codes = q.astype(np.int8).reshape(x.shape)
-    scales = d[..., 0].astype(np.float16)
+    with np.errstate(over="ignore"):         # d past the f16 range stores inf, as f16(d) does
+        scales = d[..., 0].astype(np.float16)
     return codes, scales
 
 

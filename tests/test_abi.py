@@ -128,3 +128,13 @@ def test_select_rejects():
     assert f(FAKE, FAKE, FAKE, 0, 1, 64, 8, 0) == _lib.GQA_ERR_SHAPE
     assert f(FAKE, FAKE, FAKE, 1, 1, -4, 8, 0) == _lib.GQA_ERR_SHAPE
     assert f(FAKE, FAKE, FAKE, 1, 1, 64, 0, 0) == _lib.GQA_ERR_BUDGET
+
+
+def test_append_rejects():
+    f = gq.gqa_decode_append_i8
+    args = [FAKE] * 7
+    assert f(*args, 0, 1, 16, 2, 64, 0) == _lib.GQA_ERR_SHAPE
+    assert f(*args, 1, -1, 16, 2, 64, 0) == _lib.GQA_ERR_SHAPE
+    assert f(*args, 1, 1, 16, 2, 96, 0) == _lib.GQA_ERR_HEAD_DIM
+    assert f(*([None] + [FAKE] * 6), 1, 1, 16, 2, 64, 0) == _lib.GQA_ERR_NULL
+    assert f(*([None] * 7), 1, 0, 16, 2, 64, 0) == _lib.GQA_OK      # nothing to write
