@@ -43,24 +43,33 @@ SETTLE_S = 0.05
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def kernel_source_hash() -> str:
+# the sources each measured kernel is built from: counters taken on one
+# version of a kernel do not describe another
+KERNEL_SOURCES = {
+    "attn": ["attn_mfma.h", "common.h", "gqa_decode.hip", "plan.h", "plan.cpp"],
+    "append": ["append.hip"],
+    "select": ["select.hip"],
+}
+
+
+def kernel_source_hash(kernel: str = "attn") -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "decode_attention_kv_gqa_amd", "csrc")
-    for fn in sorted(os.listdir(csrc)):
+    for fn in KERNEL_SOURCES[kernel]:
         with open(os.path.join(csrc, fn), "rb") as f:
             h.update(fn.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str):
-    """HBM bytes per chunk-kernel launch measured with rocprofv3 counters,
-    if they were taken on the current kernel source."""
+def load_traffic(workload: str, kernel: str = "attn"):
+    """HBM bytes per launch of the workload's measured kernel from rocprofv3
+    counters, if they were taken on the current kernel source."""
     path = os.path.join(PROFILES, f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash(kernel):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -208,7 +217,7 @@ def bench_append(args):
                    "algorithmic_bytes": nbytes, "input_copies_rotated": copies},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None}}), flush=True)
+                     "traffic": load_traffic(args.workload, "append")}}), flush=True)
 
 
 def main():
