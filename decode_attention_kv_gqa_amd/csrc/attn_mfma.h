@@ -198,8 +198,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            0x00020000);
 }
 
+// Waves per SIMD the register budget is sized for: 2, except for the
+// instances whose accumulators and operands do not fit half the register
+// file (head_dim 256 with two row blocks or f16 K, and f16 head_dim 128 with
+// two row blocks), which get the whole file instead of spilling.
+template <int D, bool I8, int NRB>
+constexpr int attn_occupancy() {
+  return ((D == 256 && (NRB == 2 || !I8)) || (D == 128 && NRB == 2 && !I8)) ? 1 : 2;
+}
+
 template <int D, bool I8, bool IDS, int NRB, int NW>
-__global__ __launch_bounds__(64 * NW, 2) void attn_mfma(AttnArgs a) {
+__global__ __launch_bounds__(64 * NW, (attn_occupancy<D, I8, NRB>())) void attn_mfma(AttnArgs a) {
   using G = TileGeom<D, I8>;
   using L = AttnLds<D, I8, NRB, NW>;
   constexpr int NT = 64 * NW;                    // threads per workgroup
@@ -228,6 +237,50 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma(AttnArgs a) {
   const int rbl = (id % nu) % a.nrb;
   const int tq = (id % nu) / a.nrb;
   const int p = id / nu;
+  auto row_t = [&](int r) -> int { return IDS ? tq : r / a.G; };
+  auto row_h = [&](int r) -> int { return g * a.G + (IDS ? r : r % a.G); };
+  const int r0 = rbl * RB;                       // first unit row of this block
+
+  // ---- query rows as MFMA B operands (f16 hi + lo), staged once in LDS.
+  // Slot = (row block k, k-step ks, lane ln) of the operand layout.  Their
+  // loads are issued before anything waits on memory, so their latency
+  // overlaps the sequence-length read and the first tile's K/V requests. ----
+  constexpr int QSLOTS = NRB * G::KS * 64;
+  constexpr int QPT = QSLOTS / NT;                // slots per thread
+  constexpr bool QPRE = QSLOTS % NT == 0 && QPT <= 4;
+  auto q_load = [&](int slot, float4& u0, float4& u1) {
+    const int ln = slot & 63, kks = slot >> 6;
+    const int ks = kks % G::KS, k = kks / G::KS;
+    const int r = r0 + 16 * k + (ln & 15);
+    // dims of k-step ks held by lane group ln / 16 (must match the K loads)
+    const int lb2 = ln >> 4;
+    const int d0 = I8 ? (64 * (ks >> 1) + 16 * lb2 + 8 * (ks & 1)) : (32 * ks + 8 * lb2);
+    // rows past the unit's last read that last row (always valid) and are
+    // zeroed when stored
+    const int rc = r < a.R ? r : a.R - 1;
+    const float* qrow = a.q + ((size_t)(s * a.T + row_t(rc)) * a.H + row_h(rc)) * D + d0;
+    u0 = *reinterpret_cast<const float4*>(qrow);
+    u1 = *reinterpret_cast<const float4*>(qrow + 4);
+  };
+  auto q_store = [&](int slot, const float4& u0, const float4& u1) {
+    const int ln = slot & 63, kks = slot >> 6;
+    const int r = r0 + 16 * (kks / G::KS) + (ln & 15);
+    const bool real = r < a.R;
+    float x[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = real ? x[e] * a.qscale : 0.f;
+    half8 hi, lo;
+    split_hi_lo(x, hi, lo);
+    u32x4* qlds = reinterpret_cast<u32x4*>(smem + L::MAIN);
+    qlds[(kks * 2 + 0) * 64 + ln] = __builtin_bit_cast(u32x4, hi);
+    qlds[(kks * 2 + 1) * 64 + ln] = __builtin_bit_cast(u32x4, lo);
+  };
+  float4 qv[QPRE ? QPT : 1][2];
+  if constexpr (QPRE) {
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) q_load(tid + NT * i, qv[i][0], qv[i][1]);
+  }
+
   const int seq_len = a.seq_lens[s];
 
   auto width_of = [&](int r) -> int {   // r: row index within the unit
@@ -238,10 +291,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma(AttnArgs a) {
     if (IDS) Lt = Lt < a.B ? Lt : a.B;
     return Lt;
   };
-  auto row_t = [&](int r) -> int { return IDS ? tq : r / a.G; };
-  auto row_h = [&](int r) -> int { return g * a.G + (IDS ? r : r % a.G); };
 
-  const int r0 = rbl * RB;                       // first unit row of this block
   const int rlast = (a.R - 1 < r0 + RB - 1) ? a.R - 1 : r0 + RB - 1;
   const int wmax = width_of(rlast);
   const int64_t c0l = (int64_t)p * a.chunk;
@@ -267,32 +317,6 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma(AttnArgs a) {
   uint16_t* scl = reinterpret_cast<uint16_t*>(smem + L::MAIN + L::QB) + wave * 2 * TC * G::NG;
   float* mls = reinterpret_cast<float*>(smem + L::MAIN + L::QB + L::SC);
 
-  // ---- query rows as MFMA B operands (f16 hi + lo), staged once in LDS ----
-  for (int slot = tid; slot < NRB * G::KS * 64; slot += NT) {
-    const int ln = slot & 63, kks = slot >> 6;
-    const int ks = kks % G::KS, k = kks / G::KS;
-    const int lr2 = ln & 15, lb2 = ln >> 4;
-    const int r = r0 + 16 * k + lr2;
-    // dims of k-step ks held by lane group lb2 (must match the K loads)
-    const int d0 = I8 ? (64 * (ks >> 1) + 16 * lb2 + 8 * (ks & 1)) : (32 * ks + 8 * lb2);
-    float x[8];
-    if (r < a.R) {
-      const float* qrow = a.q + ((size_t)(s * a.T + row_t(r)) * a.H + row_h(r)) * D + d0;
-      const float4 u0 = *reinterpret_cast<const float4*>(qrow);
-      const float4 u1 = *reinterpret_cast<const float4*>(qrow + 4);
-      x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w;
-      x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] *= a.qscale;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = 0.f;
-    }
-    half8 hi, lo;
-    split_hi_lo(x, hi, lo);
-    qlds[(kks * 2 + 0) * 64 + ln] = __builtin_bit_cast(u32x4, hi);
-    qlds[(kks * 2 + 1) * 64 + ln] = __builtin_bit_cast(u32x4, lo);
-  }
   int lim[NRB];                                  // visible limit of this lane's rows
 #pragma unroll
   for (int k = 0; k < NRB; ++k) {
@@ -633,11 +657,24 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma(AttnArgs a) {
     KRegs RK;
     VRegs RV;
     int ts = c0 + TC * wave;
-    __syncthreads();   // query operands (and ids) staged
-    // same issue order as inside the loop (V, then K), so the wait counts
-    // at the loop head hold on both paths into it
+    if constexpr (IDS) __syncthreads();   // the split's ids are staged
+    // The first tile is requested before the query operands are staged, so
+    // its latency overlaps that work.  Same issue order as inside the loop
+    // (V, then K), so the wait counts at the loop head hold on both paths
+    // into it.
     issue_v(ts, RV);
     issue_k(ts, RK);
+    if constexpr (QPRE) {
+#pragma unroll
+      for (int i = 0; i < QPT; ++i) q_store(tid + NT * i, qv[i][0], qv[i][1]);
+    } else {
+      for (int slot = tid; slot < QSLOTS; slot += NT) {
+        float4 u0, u1;
+        q_load(slot, u0, u1);
+        q_store(slot, u0, u1);
+      }
+    }
+    __syncthreads();   // query operands staged
 #pragma unroll 1
     while (ts < cend) {
       const int tn = ts + NW * TC;
