@@ -53,6 +53,17 @@ APPEND_MUTANTS = {
 }
 
 
+# Output-gate oracle (oracle/gate_ref.py) against tests/test_oracle_gate.py.
+GATE_MUTANTS = {
+    "exp_sign": ("return 1.0 / (1.0 + np.exp(-x))", "return 1.0 / (1.0 + np.exp(x))"),
+    "tanh_gate": ("return 1.0 / (1.0 + np.exp(-x))", "return 0.5 * (1.0 + np.tanh(x))"),
+    "gate_from_query_half": ("return qfull[..., :D], qfull[..., D:]",
+                             "return qfull[..., :D], qfull[..., :D]"),
+    "gate_added": ("return np.asarray(out, dtype=np.float64) * sigmoid(gate)",
+                   "return np.asarray(out, dtype=np.float64) + sigmoid(gate)"),
+}
+
+
 def run_mutant(tmp_path, module, test_file, before, after, name):
     src = open(os.path.join(ROOT, "oracle", module)).read()
     assert before in src, f"mutation site for {name} no longer exists"
@@ -84,3 +95,9 @@ def test_select_pins_catch_mutant(name, tmp_path):
 def test_append_pins_catch_mutant(name, tmp_path):
     before, after = APPEND_MUTANTS[name]
     run_mutant(tmp_path, "append_ref.py", "test_oracle_append.py", before, after, name)
+
+
+@pytest.mark.parametrize("name", sorted(GATE_MUTANTS))
+def test_gate_pins_catch_mutant(name, tmp_path):
+    before, after = GATE_MUTANTS[name]
+    run_mutant(tmp_path, "gate_ref.py", "test_oracle_gate.py", before, after, name)
