@@ -228,6 +228,8 @@ def main():
     ap.add_argument("--workload", default="i8_32k")
     ap.add_argument("--chunk", type=int, default=-1, help="cells per split (-1: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--gate", action="store_true",
+                    help="merge with the output gate (gate rows interleaved with the query)")
     ap.add_argument("--copies", type=int, default=0, help="input replicas to rotate through")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (HBM counter calibration)")
@@ -272,9 +274,18 @@ def main():
     dev = torch.device("cuda:0")
     d = lambda x: None if x is None else torch.from_numpy(x).to(dev)
     sets = []
+    gate_np = None
+    if args.gate:
+        # the output gate as the second half of [query | gate] rows
+        gate_np = np.random.default_rng(2000 + w.index).standard_normal(inp.q.shape).astype(np.float32)
     for _ in range(copies):
-        sets.append(dict(q=d(inp.q), k=d(inp.k), v=d(inp.v), seq_lens=d(inp.seq_lens),
-                         k_scales=d(inp.k_scales), v_scales=d(inp.v_scales), ids=d(inp.ids)))
+        x = dict(q=d(inp.q), k=d(inp.k), v=d(inp.v), seq_lens=d(inp.seq_lens),
+                 k_scales=d(inp.k_scales), v_scales=d(inp.v_scales), ids=d(inp.ids), gate=None)
+        if args.gate:
+            full = d(np.concatenate([inp.q, gate_np], axis=-1))
+            x["q"] = full[..., :sh["D"]].contiguous()
+            x["gate"] = full[..., sh["D"]:]
+        sets.append(x)
     step = gq.DecodeAttention(sh["S"], sh["T"], sh["H"], sh["Hk"], sh["D"], sh["Lmax"], inp.kv,
                               B=sh["B"], chunk=chunk, device=dev)
     stream = torch.cuda.current_stream()
@@ -283,7 +294,8 @@ def main():
         x = sets[i % copies]
         step.attn(x["q"], x["k"], x["v"], x["seq_lens"], inp.scale, x["k_scales"], x["v_scales"],
                   x["ids"])
-        step.merge(x["seq_lens"], x["ids"])
+        step.merge(x["seq_lens"], x["ids"], gate=x["gate"],
+                   gate_stride=None if x["gate"] is None else 2 * sh["D"])
 
     for i in range(args.warmup):
         one(i)
@@ -351,7 +363,8 @@ def main():
         "config": {"workload": args.workload, "S": sh["S"], "T": sh["T"], "H": sh["H"],
                    "Hk": sh["Hk"], "D": sh["D"], "Lmax": sh["Lmax"], "budget": sh["B"],
                    "kv": inp.kv, "chunk": step.chunk, "kv_bytes_per_step": step_bytes,
-                   "input_copies_rotated": copies, "description": w.description},
+                   "input_copies_rotated": copies, "output_gate": bool(args.gate),
+                   "description": w.description},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,

@@ -12,11 +12,13 @@ from typing import Optional
 
 from . import _lib
 from ._lib import (GqaDecodeError, gqa_decode_attn_f16, gqa_decode_attn_i8, gqa_decode_merge,
+                   gqa_decode_merge_gated,
                    gqa_decode_select_ids, gqa_decode_append_i8,
                    gqa_decode_part_bytes, gqa_decode_auto_chunk, strerror)
 
 __all__ = ["decode_attention", "DecodeAttention", "GqaDecodeError", "gqa_decode_attn_f16",
-           "gqa_decode_attn_i8", "gqa_decode_merge", "gqa_decode_select_ids", "select_ids",
+           "gqa_decode_attn_i8", "gqa_decode_merge", "gqa_decode_merge_gated",
+           "gqa_decode_select_ids", "select_ids",
            "gqa_decode_append_i8", "append_i8",
            "gqa_decode_part_bytes",
            "gqa_decode_auto_chunk", "strerror"]
@@ -57,6 +59,7 @@ class DecodeAttention:
         lib = _lib.load()
         self._f16, self._i8, self._merge = (lib.gqa_decode_attn_f16, lib.gqa_decode_attn_i8,
                                             lib.gqa_decode_merge)
+        self._merge_gated = lib.gqa_decode_merge_gated
 
     def attn(self, q, k, v, seq_lens, scale, k_scales=None, v_scales=None, ids=None, stream=None):
         st = self._stream(self._dev) if stream is None else stream
@@ -76,18 +79,30 @@ class DecodeAttention:
             if rc:
                 raise GqaDecodeError("gqa_decode_attn_f16", rc)
 
-    def merge(self, seq_lens, ids=None, stream=None):
+    def merge(self, seq_lens, ids=None, stream=None, gate=None, gate_stride=None):
+        """The merge into self.out; with `gate` (float32 on the GPU, row r of
+        the S*T*H output rows at element r * gate_stride, default D) each
+        output element is multiplied by sigmoid(gate)."""
         st = self._stream(self._dev) if stream is None else stream
-        rc = self._merge(self.part.data_ptr(), seq_lens.data_ptr(),
-                         None if ids is None else ids.data_ptr(), self.out.data_ptr(),
-                         self.S, self.T, self.Lmax, self.B if ids is not None else 0,
-                         self.H, self.D, self.chunk, st)
-        if rc:
-            raise GqaDecodeError("gqa_decode_merge", rc)
+        idp = None if ids is None else ids.data_ptr()
+        B = self.B if ids is not None else 0
+        if gate is None:
+            rc = self._merge(self.part.data_ptr(), seq_lens.data_ptr(), idp, self.out.data_ptr(),
+                             self.S, self.T, self.Lmax, B, self.H, self.D, self.chunk, st)
+            if rc:
+                raise GqaDecodeError("gqa_decode_merge", rc)
+        else:
+            gs = self.D if gate_stride is None else int(gate_stride)
+            rc = self._merge_gated(self.part.data_ptr(), seq_lens.data_ptr(), idp, gate.data_ptr(),
+                                   gs, self.out.data_ptr(), self.S, self.T, self.Lmax, B, self.H,
+                                   self.D, self.chunk, st)
+            if rc:
+                raise GqaDecodeError("gqa_decode_merge_gated", rc)
 
-    def __call__(self, q, k, v, seq_lens, scale, k_scales=None, v_scales=None, ids=None):
+    def __call__(self, q, k, v, seq_lens, scale, k_scales=None, v_scales=None, ids=None,
+                 gate=None, gate_stride=None):
         self.attn(q, k, v, seq_lens, scale, k_scales, v_scales, ids)
-        self.merge(seq_lens, ids)
+        self.merge(seq_lens, ids, gate=gate, gate_stride=gate_stride)
         return self.out
 
 
@@ -120,12 +135,25 @@ def _validate(q, k, v, seq_lens, k_scales, v_scales, ids):
 
 
 def decode_attention(q, k, v, seq_lens, scale: Optional[float] = None, *, k_scales=None,
-                     v_scales=None, ids=None, chunk: int = 0):
+                     v_scales=None, ids=None, chunk: int = 0, gate=None):
     """One decode step.  q [S][T][H][D] float32; k, v [S][Lmax][Hk][D]
     float16, or int8 with k_scales / v_scales [S][Lmax][Hk][D/64] float16;
     seq_lens [S] int32 (cells visible to each sequence's last query token);
-    ids None or [S][T][B] int32.  Returns out [S][T][H][D] float32."""
+    ids None or [S][T][B] int32; gate None or float32 [S][T][H][D], possibly
+    the gate half of [query | gate] rows (a view whose last dim is contiguous
+    and whose head rows are evenly strided).  Returns out [S][T][H][D]
+    float32, multiplied by sigmoid(gate) when a gate is given."""
     _validate(q, k, v, seq_lens, k_scales, v_scales, ids)
+    gate_stride = None
+    if gate is not None:
+        import torch
+        if not gate.is_cuda or gate.dtype != torch.float32 or tuple(gate.shape) != tuple(q.shape):
+            raise ValueError("gate must be a float32 GPU tensor shaped like q")
+        S_, T_, H_, D_ = gate.shape
+        st = gate.stride()
+        if st[3] != 1 or st[2] < D_ or st[1] != H_ * st[2] or st[0] != T_ * st[1]:
+            raise ValueError("gate rows must be evenly strided with a contiguous last dim")
+        gate_stride = st[2]
     S, T, H, D = q.shape
     _, Lmax, Hk, Dk = k.shape
     if Dk != D or k.shape[0] != S or seq_lens.shape != (S,):
@@ -135,7 +163,8 @@ def decode_attention(q, k, v, seq_lens, scale: Optional[float] = None, *, k_scal
         scale = D ** -0.5
     kv = "i8" if str(k.dtype) == "torch.int8" else "f16"
     step = DecodeAttention(S, T, H, Hk, D, Lmax, kv, B=B, chunk=chunk, device=q.device)
-    return step(q, k, v, seq_lens, scale, k_scales, v_scales, ids).clone()
+    return step(q, k, v, seq_lens, scale, k_scales, v_scales, ids, gate=gate,
+                gate_stride=gate_stride).clone()
 
 
 def select_ids(block_scores, seq_lens, B: int, out=None):

@@ -22,7 +22,7 @@ GQA_ERR_CHUNK = -6
 GQA_ERR_WORKSPACE = -7
 
 EXPORTED = ["gqa_decode_attn_f16", "gqa_decode_attn_i8", "gqa_decode_merge",
-            "gqa_decode_select_ids", "gqa_decode_append_i8", "gqa_decode_part_bytes",
+            "gqa_decode_merge_gated", "gqa_decode_select_ids", "gqa_decode_append_i8", "gqa_decode_part_bytes",
             "gqa_decode_auto_chunk",
             "gqa_decode_strerror"]
 
@@ -52,6 +52,8 @@ def load() -> ctypes.CDLL:
     lib.gqa_decode_attn_i8.restype = i32
     lib.gqa_decode_merge.argtypes = [vp, vp, vp, vp] + [i32] * 7 + [vp]
     lib.gqa_decode_merge.restype = i32
+    lib.gqa_decode_merge_gated.argtypes = [vp, vp, vp, vp, ctypes.c_int64, vp] + [i32] * 7 + [vp]
+    lib.gqa_decode_merge_gated.restype = i32
     lib.gqa_decode_select_ids.argtypes = [vp, vp, vp] + [i32] * 4 + [vp]
     lib.gqa_decode_select_ids.restype = i32
     lib.gqa_decode_append_i8.argtypes = [vp] * 7 + [i32] * 5 + [vp]
@@ -90,6 +92,13 @@ def gqa_decode_attn_i8(q, k, v, k_scales, v_scales, ids, seq_lens, part, part_by
 def gqa_decode_merge(part, seq_lens, ids_or_null, out, S, T, Lmax, B, H, D, chunk, stream=0) -> int:
     return load().gqa_decode_merge(_p(part), _p(seq_lens), _p(ids_or_null), _p(out), S, T, Lmax, B,
                                    H, D, chunk, _p(stream))
+
+
+def gqa_decode_merge_gated(part, seq_lens, ids_or_null, gate, gate_stride, out, S, T, Lmax, B, H,
+                           D, chunk, stream=0) -> int:
+    return load().gqa_decode_merge_gated(_p(part), _p(seq_lens), _p(ids_or_null), _p(gate),
+                                         int(gate_stride), _p(out), S, T, Lmax, B, H, D, chunk,
+                                         _p(stream))
 
 
 def gqa_decode_part_bytes(S, T, Lmax, B, H, D, chunk) -> int:

@@ -47,6 +47,8 @@ struct MergeArgs {
   const float* part_o;     // [rows][P][D]
   const float* part_ml;    // [rows][P][2]
   float* out;              // [rows][D]
+  const float* gate;       // row r's gate at gate + r * gate_stride, or null (no gate)
+  int64_t gate_stride;
   int P;
 };
 

@@ -68,6 +68,16 @@ __global__ __launch_bounds__(kThreads) void merge_rows(MergeArgs a) {
   const int nv = a.P;
   const float* ml = a.part_ml + (size_t)row * a.P * 2;
   const float* po = a.part_o + (size_t)row * a.P * D + lane * V;
+  // output gate (qsa2.metal, qsa_merge2; FORWARD_MSL, attn_combine): the
+  // merged row is multiplied by sigmoid(gate) elementwise.  Wave 0 writes
+  // the row, so it requests its gate elements first.
+  float gt[V];
+  const bool gated = a.gate != nullptr;
+  if (gated && wave == 0) {
+    const float* gsrc = a.gate + (size_t)row * a.gate_stride + lane * V;
+#pragma unroll
+    for (int e = 0; e < V; ++e) gt[e] = gsrc[e];
+  }
 
   float M = -INFINITY, lsum = 0.f;
   float acc[V];
@@ -142,7 +152,9 @@ __global__ __launch_bounds__(kThreads) void merge_rows(MergeArgs a) {
       float x = 0.f;
 #pragma unroll
       for (int w = 0; w < 4; ++w) x = fmaf(f[w], red_o[w][lane * V + e], x);
-      out[e] = x / Ls;
+      x = x / Ls;
+      if (gated) x *= 1.0f / (1.0f + __expf(-gt[e]));
+      out[e] = x;
     }
   }
 }
@@ -264,20 +276,23 @@ int gqa_decode_attn_i8(const float* q, const int8_t* k, const int8_t* v, const u
                      Lmax, B, H, Hk, D, scale, chunk, stream);
 }
 
-int gqa_decode_merge(const float* part, const int32_t* seq_lens, const int32_t* ids_or_null,
-                     float* out, int S, int T, int Lmax, int B, int H, int D, int chunk,
-                     void* stream) {
+static int merge_common(const float* part, const int32_t* seq_lens, const int32_t* ids_or_null,
+                        const float* gate, int64_t gate_stride, float* out, int S, int T,
+                        int Lmax, int B, int H, int D, int chunk, void* stream) {
   if (!part || !seq_lens || !out) return GQA_ERR_NULL;
   const bool ids = ids_or_null != nullptr;
   gqa::Shape sh{S, T, Lmax, ids ? B : 0, H, H, D, ids, false};
   int rc = gqa::check_shape(sh);
   if (rc != GQA_OK) return rc;
   if (chunk < 1) return GQA_ERR_CHUNK;
+  if (gate && gate_stride < D) return GQA_ERR_SHAPE;
   const int64_t P = gqa::num_splits(sh, chunk);
   MergeArgs a;
   a.part_o = part;
   a.part_ml = part + gqa::part_o_floats(sh, P);
   a.out = out;
+  a.gate = gate;
+  a.gate_stride = gate_stride;
   a.P = (int)P;
   const size_t rows = (size_t)S * T * H;
   if (rows > 0x7fffffffu) return GQA_ERR_SHAPE;
@@ -290,6 +305,21 @@ int gqa_decode_merge(const float* part, const int32_t* seq_lens, const int32_t* 
   }
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? GQA_OK : (int)e;
+}
+
+int gqa_decode_merge(const float* part, const int32_t* seq_lens, const int32_t* ids_or_null,
+                     float* out, int S, int T, int Lmax, int B, int H, int D, int chunk,
+                     void* stream) {
+  return merge_common(part, seq_lens, ids_or_null, nullptr, 0, out, S, T, Lmax, B, H, D, chunk,
+                      stream);
+}
+
+int gqa_decode_merge_gated(const float* part, const int32_t* seq_lens, const int32_t* ids_or_null,
+                           const float* gate, int64_t gate_stride, float* out, int S, int T,
+                           int Lmax, int B, int H, int D, int chunk, void* stream) {
+  if (!gate) return GQA_ERR_NULL;
+  return merge_common(part, seq_lens, ids_or_null, gate, gate_stride, out, S, T, Lmax, B, H, D,
+                      chunk, stream);
 }
 
 }  // extern "C"

@@ -6,6 +6,7 @@
  *
  *   gqa_decode_attn_f16 / gqa_decode_attn_i8   chunk partials (o, m, l)
  *   gqa_decode_merge                            log-sum-exp merge -> out
+ *   gqa_decode_merge_gated                      the merge times sigmoid(gate)
  *
  * preceded, for budgeted attention, by gqa_decode_select_ids (the B cell ids
  * of every token from per-block scores); gqa_decode_append_i8 writes new K/V
@@ -131,6 +132,22 @@ int gqa_decode_attn_i8(const float *q, const int8_t *k, const int8_t *v,
 int gqa_decode_merge(const float *part, const int32_t *seq_lens, const int32_t *ids_or_null,
                      float *out, int S, int T, int Lmax, int B, int H, int D, int chunk,
                      void *stream);
+
+/* The merge of gqa_decode_merge followed by the output gate (qsa2.metal,
+ * end of qsa_merge2; FORWARD_MSL, end of attn_combine):
+ *   out[r][d] = merged[r][d] * 1 / (1 + exp(-gate[r][d]))
+ * for every output row r = (s * T + t) * H + h.  The gate is fp32 and row r
+ * starts at gate + r * gate_stride (in floats, gate_stride >= D): a separate
+ * [S][T][H][D] tensor has gate_stride = D; the pages' layout, one
+ * [query | gate] row of 2 * D floats per (token, head), is passed as
+ * gate = qfull + D with gate_stride = 2 * D.  Rows with an empty window stay
+ * zero.  The gate is read only; the caller owns it.  Other arguments and
+ * errors as gqa_decode_merge, plus GQA_ERR_NULL for a NULL gate and
+ * GQA_ERR_SHAPE for gate_stride < D. */
+int gqa_decode_merge_gated(const float *part, const int32_t *seq_lens, const int32_t *ids_or_null,
+                           const float *gate, int64_t gate_stride, float *out,
+                           int S, int T, int Lmax, int B, int H, int D, int chunk,
+                           void *stream);
 
 /* Budget selection: the ids a budgeted token attends (qsa2.metal, kernel
  * qsa_topk2).  Cells come in blocks of 4 with one score per block; with

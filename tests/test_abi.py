@@ -86,6 +86,16 @@ def test_merge_rejects():
     assert m(FAKE, FAKE, FAKE, FAKE, 1, 1, 16, 0, 8, 64, 32, 0) == _lib.GQA_ERR_BUDGET
 
 
+def test_merge_gated_rejects():
+    m = gq.gqa_decode_merge_gated
+    # NULL gate, NULL workspace, gate rows narrower than D, then the merge's own checks
+    assert m(FAKE, FAKE, None, None, 64, FAKE, 1, 1, 16, 0, 8, 64, 32, 0) == _lib.GQA_ERR_NULL
+    assert m(None, FAKE, None, FAKE, 64, FAKE, 1, 1, 16, 0, 8, 64, 32, 0) == _lib.GQA_ERR_NULL
+    assert m(FAKE, FAKE, None, FAKE, 63, FAKE, 1, 1, 16, 0, 8, 64, 32, 0) == _lib.GQA_ERR_SHAPE
+    assert m(FAKE, FAKE, None, FAKE, 64, FAKE, 1, 1, 16, 0, 8, 64, 0, 0) == _lib.GQA_ERR_CHUNK
+    assert m(FAKE, FAKE, None, FAKE, 96, FAKE, 1, 1, 16, 0, 8, 96, 32, 0) == _lib.GQA_ERR_HEAD_DIM
+
+
 def test_part_bytes_formula():
     # splits = ceil(width / chunk); one (D + 2)-float partial per query row and split
     assert gq.gqa_decode_part_bytes(8, 1, 32768, 0, 24, 256, 512) == 8 * 24 * 64 * 258 * 4
