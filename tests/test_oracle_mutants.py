@@ -64,6 +64,26 @@ GATE_MUTANTS = {
 }
 
 
+# TurboQuant decode oracle (oracle/tq_ref.py) against tests/test_oracle_tq.py.
+TQ_MUTANTS = {
+    "jl_sign_flipped": ("signed_sum = 2.0 * pos_sum - q_jl.sum()", "signed_sum = q_jl.sum() - 2.0 * pos_sum"),
+    "jl_factor_two_dropped": ("signed_sum = 2.0 * pos_sum - q_jl.sum()", "signed_sum = pos_sum - q_jl.sum()"),
+    "residual_norm_dropped": ("correction = norm * residual_norm * float(qjl_scale) * signed_sum",
+                              "correction = norm * float(qjl_scale) * signed_sum"),
+    "polar_field_order_reversed": ("idx = (w[..., :, None] >> (np.uint32(2) * k)) & np.uint32(3)",
+                                   "idx = (w[..., :, None] >> (np.uint32(2) * (np.uint32(15) - k))) & np.uint32(3)"),
+    "jl_bit_order_reversed": ("b = (w[..., :, None] >> k) & np.uint32(1)",
+                              "b = (w[..., :, None] >> (np.uint32(31) - k)) & np.uint32(1)"),
+    "rotation_unnormalised": ("(hadamard(D) @ acc) / math.sqrt(D)", "(hadamard(D) @ acc)"),
+    "signs_not_undone": ("return np.asarray(signs, dtype=np.float64) * (hadamard(D) @ acc)",
+                         "return (hadamard(D) @ acc)"),
+    "norm_halves_swapped": ("norm, residual_norm = f16_halves(k_norms)",
+                            "residual_norm, norm = f16_halves(k_norms)"),
+    "polar_term_without_norm": ("return (polar_dot * norm + correction) * float(scale)",
+                                "return (polar_dot + correction) * float(scale)"),
+}
+
+
 def run_mutant(tmp_path, module, test_file, before, after, name):
     src = open(os.path.join(ROOT, "oracle", module)).read()
     assert before in src, f"mutation site for {name} no longer exists"
@@ -101,3 +121,9 @@ def test_append_pins_catch_mutant(name, tmp_path):
 def test_gate_pins_catch_mutant(name, tmp_path):
     before, after = GATE_MUTANTS[name]
     run_mutant(tmp_path, "gate_ref.py", "test_oracle_gate.py", before, after, name)
+
+
+@pytest.mark.parametrize("name", sorted(TQ_MUTANTS))
+def test_tq_pins_catch_mutant(name, tmp_path):
+    before, after = TQ_MUTANTS[name]
+    run_mutant(tmp_path, "tq_ref.py", "test_oracle_tq.py", before, after, name)

@@ -1,0 +1,166 @@
+"""Pins of the TurboQuant decode oracle (oracle/tq_ref.py), CPU only.
+
+The page prints no worked values, so the pins are: the Hadamard matrix
+against scipy's; the whole path against plain softmax attention (the
+separately pinned oracle/decode_ref.py) over keys and values decoded and
+rotated back to the original basis by code written here (a different bit
+unpacking and scipy's Hadamard), which holds exactly when the residual norm
+is zero because the rotation is orthogonal; the QJL correction against the
+unbiasedness of the QJL estimator for Gaussian projections (Monte Carlo);
+the field / bit order and the f16 halves against hand-built words; one cell;
+empty windows."""
+import math
+
+import numpy as np
+import pytest
+import scipy.linalg
+
+from oracle import decode_ref as DR
+from oracle import tq_ref as R
+from workloads import make_tq_case
+
+
+# ------------------------------------------------------------------ helpers
+# (an independent unpacking: numpy's little-endian bit order on the bytes)
+def unpack_fields(words: np.ndarray, D: int) -> np.ndarray:
+    b = np.unpackbits(np.ascontiguousarray(words).view(np.uint8), axis=-1, bitorder="little")
+    b = b.reshape(words.shape[:-1] + (D, 2)).astype(np.int64)
+    return b[..., 0] + 2 * b[..., 1]
+
+
+def unpack_bits(words: np.ndarray, D: int) -> np.ndarray:
+    b = np.unpackbits(np.ascontiguousarray(words).view(np.uint8), axis=-1, bitorder="little")
+    return b.reshape(words.shape[:-1] + (D,)).astype(np.float64)
+
+
+def low_half(words):
+    return (words & 0xFFFF).astype(np.uint16).view(np.float16).astype(np.float64)
+
+
+def to_original_basis(x_rot: np.ndarray, signs: np.ndarray) -> np.ndarray:
+    """Inverse randomized Hadamard rotation of rows: signs * (H x) / sqrt(D)."""
+    D = x_rot.shape[-1]
+    H = scipy.linalg.hadamard(D).astype(np.float64)
+    return (x_rot @ H.T) / math.sqrt(D) * signs.astype(np.float64)
+
+
+# ------------------------------------------------------------------ pins
+@pytest.mark.parametrize("D", [1, 2, 4, 32, 64, 128])
+def test_hadamard_against_scipy(D):
+    H = R.hadamard(D)
+    assert np.array_equal(H, scipy.linalg.hadamard(D).astype(np.float64))
+    np.testing.assert_array_equal(H @ H.T, D * np.eye(D))
+
+
+def test_field_bit_order_and_f16_halves():
+    D = 32
+    polar = np.zeros((1, 2), dtype=np.uint32)
+    polar[0, 0] = np.uint32(3) << np.uint32(10)        # field 5 of word 0 -> dim 5
+    polar[0, 1] = np.uint32(2) << np.uint32(30)        # field 15 of word 1 -> dim 31
+    idx = R.polar_indices(polar, D)[0]
+    expect = np.zeros(D, dtype=np.int64)
+    expect[5], expect[31] = 3, 2
+    assert np.array_equal(idx, expect)
+    jl = np.array([[1 << 7]], dtype=np.uint32)
+    b = R.jl_bits(jl, D)[0]
+    assert b[7] == 1 and b.sum() == 1
+    w = np.array([np.float16(1.5).view(np.uint16) | (np.uint32(np.float16(0.25).view(np.uint16)) << 16)],
+                 dtype=np.uint32)
+    lo, hi = R.f16_halves(w)
+    assert lo[0] == 1.5 and hi[0] == 0.25
+    # against the independent unpacking on random words
+    rng = np.random.default_rng(0)
+    wr = rng.integers(0, 2**32, size=(5, 8), dtype=np.uint64).astype(np.uint32)
+    assert np.array_equal(R.polar_indices(wr, 128), unpack_fields(wr, 128))
+    assert np.array_equal(R.jl_bits(wr[:, :4], 128), unpack_bits(wr[:, :4], 128))
+
+
+@pytest.mark.parametrize("T,lens", [(1, [60, 17, 0]), (3, [60, 2, 1])])
+@pytest.mark.parametrize("D", [32, 64, 128])
+def test_zero_residual_equals_plain_attention_in_original_basis(D, T, lens):
+    S, H, Hk, Lmax = 3, 8, 2, 60
+    inp = make_tq_case(S, T, H, Hk, D, Lmax, lens, seed=D + T)
+    k_norms = inp.k_norms & np.uint32(0xFFFF)           # residual norm 0: no QJL term
+    got = R.tq_decode_ref(inp.q_rot, inp.q_jl, inp.k_polar, inp.k_jl, k_norms, inp.v_polar,
+                          inp.v_norms, inp.seq_lens, inp.signs, inp.centroids, inp.qjl_scale,
+                          inp.scale)
+    c = np.asarray(inp.centroids, dtype=np.float64)
+    k_rot = low_half(k_norms)[..., None] * c[unpack_fields(inp.k_polar, D)]   # [S][Hk][Lmax][D]
+    v_rot = low_half(inp.v_norms)[..., None] * c[unpack_fields(inp.v_polar, D)]
+    k_orig = to_original_basis(k_rot, inp.signs).transpose(0, 2, 1, 3)          # [S][Lmax][Hk][D]
+    v_orig = to_original_basis(v_rot, inp.signs).transpose(0, 2, 1, 3)
+    # q . k is rotation invariant: the original-basis query is the inverse
+    # rotation of q_rot
+    q_orig = to_original_basis(inp.q_rot.astype(np.float64), inp.signs)
+    ref = DR.gqa_decode_ref(q_orig, k_orig, v_orig, inp.seq_lens, inp.scale)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_qjl_correction_is_unbiased():
+    # QJL: for s_i ~ N(0, I), E[(s_i . q) sign(s_i . r)] = sqrt(2/pi) q.r/|r|, so
+    # sqrt(pi/2)/m * |r| * sum_i (S q)_i sign((S r)_i) estimates q . r
+    D, trials = 64, 3000
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal(D)
+    r = rng.standard_normal(D)
+    r /= np.linalg.norm(r)                              # |r| = 1 is exact in f16
+    norms = np.array([np.float16(1.0).view(np.uint16) | (np.uint32(np.float16(1.0).view(np.uint16)) << 16)],
+                     dtype=np.uint32)
+    polar = np.zeros((1, D // 16), dtype=np.uint32)
+    est = np.empty(trials)
+    for i in range(trials):
+        Smat = rng.standard_normal((D, D))
+        bits = (Smat @ r > 0).astype(np.uint8)
+        jl = np.packbits(bits, bitorder="little").view(np.uint32)[None, :]
+        est[i] = R.tq_scores(np.zeros(D), Smat @ q, polar, jl, norms, (0.0, 0.0, 0.0, 0.0),
+                             math.sqrt(math.pi / 2) / D, 1.0, D)[0]
+    mean, sem = est.mean(), est.std(ddof=1) / math.sqrt(trials)
+    assert abs(mean - q @ r) < 4.0 * sem, (mean, q @ r, sem)
+    assert sem < 0.1 * abs(q @ r) + 0.05
+
+
+def test_single_cell_gives_its_decoded_value():
+    D = 64
+    inp = make_tq_case(1, 1, 4, 1, D, 8, [1], seed=3)
+    out = R.tq_decode_ref(inp.q_rot, inp.q_jl, inp.k_polar, inp.k_jl, inp.k_norms, inp.v_polar,
+                          inp.v_norms, inp.seq_lens, inp.signs, inp.centroids, inp.qjl_scale,
+                          inp.scale)
+    # rotate the output forward (H (signs * out) / sqrt(D)): the cell's codes come back
+    H = scipy.linalg.hadamard(D).astype(np.float64)
+    back = (out[0, 0] * inp.signs) @ H.T / math.sqrt(D)
+    c = np.asarray(inp.centroids, dtype=np.float64)
+    expect = low_half(inp.v_norms[0, 0, :1])[0] * c[unpack_fields(inp.v_polar[0, 0, :1], D)[0]]
+    for h in range(4):
+        np.testing.assert_allclose(back[h], expect, rtol=0, atol=1e-12)
+
+
+def test_empty_windows_and_rows_variant():
+    inp = make_tq_case(2, 2, 8, 2, 64, 30, [30, 1], seed=5)
+    full = R.tq_decode_ref(inp.q_rot, inp.q_jl, inp.k_polar, inp.k_jl, inp.k_norms, inp.v_polar,
+                           inp.v_norms, inp.seq_lens, inp.signs, inp.centroids, inp.qjl_scale,
+                           inp.scale)
+    assert not full[1, 0].any() and full[1, 1].any()    # token 0 of sequence 1 sees nothing
+    rows = [(0, 1, 7), (1, 0, 3), (1, 1, 0)]
+    part = R.tq_decode_ref(inp.q_rot, inp.q_jl, inp.k_polar, inp.k_jl, inp.k_norms, inp.v_polar,
+                           inp.v_norms, inp.seq_lens, inp.signs, inp.centroids, inp.qjl_scale,
+                           inp.scale, rows=rows)
+    for i, (s, t, h) in enumerate(rows):
+        assert np.array_equal(part[i], full[s, t, h])
+
+
+def test_residual_term_moves_scores_by_the_formula_scale():
+    # two cells with identical polar codes and norms: only the JL bits differ, so
+    # the softmax weight ratio is exp(score difference), and with one extra set
+    # bit on dim d the difference is 2 * norm * rnorm * qjl_scale * scale * q_jl[d]
+    D = 32
+    inp = make_tq_case(1, 1, 1, 1, D, 2, [2], seed=9)
+    inp.k_polar[0, 0, 1] = inp.k_polar[0, 0, 0]
+    inp.k_norms[0, 0, 1] = inp.k_norms[0, 0, 0]
+    inp.k_jl[0, 0, 0] = 0
+    inp.k_jl[0, 0, 1] = 1 << 11
+    sc = R.tq_scores(inp.q_rot[0, 0, 0], inp.q_jl[0, 0, 0], inp.k_polar[0, 0], inp.k_jl[0, 0],
+                     inp.k_norms[0, 0], inp.centroids, inp.qjl_scale, inp.scale, D)
+    n, rn = float(low_half(inp.k_norms[0, 0, :1])[0]), float(np.float16(
+        (inp.k_norms[0, 0, 0] >> 16).astype(np.uint16).view(np.float16)))
+    expect = 2.0 * n * rn * inp.qjl_scale * inp.scale * float(inp.q_jl[0, 0, 0, 11])
+    assert abs((sc[1] - sc[0]) - expect) <= 1e-12 * (1 + abs(expect))

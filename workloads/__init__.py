@@ -30,7 +30,8 @@ import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "WORKLOAD_ORDER", "make_inputs", "make_case",
            "Inputs", "kv_bytes", "make_block_scores", "SELECT_WORKLOADS", "APPEND_WORKLOADS",
-           "make_append_rows"]
+           "make_append_rows", "TQ_WORKLOADS", "TqInputs", "make_tq_case", "make_tq_inputs",
+           "tq_bytes"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -245,3 +246,91 @@ def make_append_rows(S: int, Tn: int, Hk: int, D: int, seed: int = 0):
     rk, rv = [np.random.default_rng(c) for c in ss.spawn(2)]
     return (rk.standard_normal((S, Tn, Hk, D), dtype=np.float32),
             rv.standard_normal((S, Tn, Hk, D), dtype=np.float32))
+
+
+# ---------------------------------------------------------------------------
+# TurboQuant-compressed caches (the cache format of cera's
+# flash_attention_tq.metal).  The encoder that produces the codes is not on
+# the source page, so the codes themselves are drawn: uniform 2-bit polar
+# indices and JL sign bits, f16 norms, random +-1 rotation signs.  The
+# centroids are the 2-bit Lloyd-Max levels of a standard normal scaled by
+# 1/sqrt(D) (the spread of one coordinate of a rotated unit vector); they are
+# deliberately not f16-exact.  Queries arrive already rotated (q_rot) and
+# JL-projected (q_jl): fp32 N(0,1).
+
+TQ_LLOYD_MAX_2BIT = (-1.5104, -0.4528, 0.4528, 1.5104)
+
+TQ_WORKLOADS = {
+    # 4 sequences at context 131072, 32 query / 8 KV heads, head_dim 128
+    # (the page's largest head_dim)
+    "tq_128k": dict(S=4, T=1, H=32, Hk=8, D=128, Lmax=131072, lens="full", index=7),
+}
+
+
+@dataclasses.dataclass
+class TqInputs:
+    q_rot: np.ndarray      # [S][T][H][D] float32
+    q_jl: np.ndarray       # [S][T][H][D] float32
+    k_polar: np.ndarray    # [S][Hk][Lmax][D/16] uint32
+    k_jl: np.ndarray       # [S][Hk][Lmax][D/32] uint32
+    k_norms: np.ndarray    # [S][Hk][Lmax] uint32: f16 norm | f16 residual norm << 16
+    v_polar: np.ndarray    # [S][Hk][Lmax][D/16] uint32
+    v_norms: np.ndarray    # [S][Hk][Lmax] uint32: f16 norm in the low half
+    seq_lens: np.ndarray   # [S] int32
+    signs: np.ndarray      # [D] float32, +-1
+    centroids: tuple       # 4 floats
+    qjl_scale: float       # sqrt(pi / 2) / D, as the page's header gives it
+    scale: float
+
+    @property
+    def shape(self):
+        S, T, H, D = self.q_rot.shape
+        return dict(S=S, T=T, H=H, Hk=self.k_polar.shape[1], D=D, Lmax=self.k_polar.shape[2])
+
+
+def _f16_bits(x: np.ndarray) -> np.ndarray:
+    return x.astype(np.float16).view(np.uint16).astype(np.uint32)
+
+
+def make_tq_case(S: int, T: int, H: int, Hk: int, D: int, Lmax: int, seq_lens, seed: int = 0,
+                 scale: Optional[float] = None) -> TqInputs:
+    assert D % 32 == 0 and D & (D - 1) == 0 and H % Hk == 0
+    ss = np.random.SeedSequence(seed)
+    r = [np.random.default_rng(c) for c in ss.spawn(10)]
+    q_rot = r[0].standard_normal((S, T, H, D), dtype=np.float32)
+    q_jl = r[1].standard_normal((S, T, H, D), dtype=np.float32)
+    u32 = np.iinfo(np.uint32).max
+    k_polar = r[2].integers(0, u32, size=(S, Hk, Lmax, D // 16), dtype=np.uint32, endpoint=True)
+    k_jl = r[3].integers(0, u32, size=(S, Hk, Lmax, D // 32), dtype=np.uint32, endpoint=True)
+    v_polar = r[4].integers(0, u32, size=(S, Hk, Lmax, D // 16), dtype=np.uint32, endpoint=True)
+    kn = r[5].uniform(0.5, 2.0, size=(S, Hk, Lmax)).astype(np.float32)
+    kr = r[6].uniform(0.0, 0.5, size=(S, Hk, Lmax)).astype(np.float32)
+    vn = r[7].uniform(0.5, 2.0, size=(S, Hk, Lmax)).astype(np.float32)
+    k_norms = (_f16_bits(kn) | (_f16_bits(kr) << np.uint32(16))).astype(np.uint32)
+    v_norms = _f16_bits(vn).astype(np.uint32)
+    signs = np.where(r[8].integers(0, 2, size=D) == 1, 1.0, -1.0).astype(np.float32)
+    c = tuple(float(np.float32(x / math.sqrt(D))) for x in TQ_LLOYD_MAX_2BIT)
+    return TqInputs(q_rot=q_rot, q_jl=q_jl, k_polar=k_polar, k_jl=k_jl, k_norms=k_norms,
+                    v_polar=v_polar, v_norms=v_norms,
+                    seq_lens=np.asarray(seq_lens, dtype=np.int32).reshape(S),
+                    signs=signs, centroids=c,
+                    qjl_scale=float(np.float32(math.sqrt(math.pi / 2.0) / D)),
+                    scale=float(np.float32(1.0 / math.sqrt(D) if scale is None else scale)))
+
+
+def make_tq_inputs(name: str) -> TqInputs:
+    w = TQ_WORKLOADS[name]
+    lens = [w["Lmax"]] * w["S"]
+    return make_tq_case(w["S"], w["T"], w["H"], w["Hk"], w["D"], w["Lmax"], lens,
+                        seed=1000 + w["index"])
+
+
+def tq_bytes(inp: TqInputs) -> int:
+    """Algorithmic cache bytes one decode step reads: every visible cell of
+    every (sequence, KV head) once -- K polar + JL + norms, V polar + norms."""
+    sh = inp.shape
+    per_cell = (sh["D"] // 16 * 4) * 2 + sh["D"] // 32 * 4 + 4 + 4
+    total = 0
+    for s in range(sh["S"]):
+        total += per_cell * sh["Hk"] * max(0, min(int(inp.seq_lens[s]), sh["Lmax"]))
+    return total
