@@ -12,12 +12,13 @@ from typing import Optional
 
 from . import _lib
 from ._lib import (GqaDecodeError, gqa_decode_attn_f16, gqa_decode_attn_i8, gqa_decode_merge,
-                   gqa_decode_merge_gated,
+                   gqa_decode_merge_gated, gqa_decode_attn_tq, gqa_decode_merge_tq,
                    gqa_decode_select_ids, gqa_decode_append_i8,
                    gqa_decode_part_bytes, gqa_decode_auto_chunk, strerror)
 
 __all__ = ["decode_attention", "DecodeAttention", "GqaDecodeError", "gqa_decode_attn_f16",
            "gqa_decode_attn_i8", "gqa_decode_merge", "gqa_decode_merge_gated",
+           "gqa_decode_attn_tq", "gqa_decode_merge_tq", "TqDecodeAttention", "tq_decode_attention",
            "gqa_decode_select_ids", "select_ids",
            "gqa_decode_append_i8", "append_i8",
            "gqa_decode_part_bytes",
@@ -213,3 +214,81 @@ def append_i8(k_new, v_new, pos, k, v, k_scales, v_scales):
                               Hk, D, st)
     if rc:
         raise GqaDecodeError("gqa_decode_append_i8", rc)
+
+
+class TqDecodeAttention:
+    """A decode step over a TurboQuant-compressed cache with its workspace
+    and output preallocated: attn() writes the rotated partials, merge() the
+    merged rows rotated back to the original basis (out [S][T][H][D])."""
+
+    def __init__(self, S, T, H, Hk, D, Lmax, chunk: int = 0, device="cuda"):
+        import torch
+        self.S, self.T, self.H, self.Hk, self.D, self.Lmax = S, T, H, Hk, D, Lmax
+        if chunk <= 0:
+            chunk = gqa_decode_auto_chunk(S, T, Lmax, 0, H, Hk, D, True)
+            if chunk <= 0:
+                raise GqaDecodeError("gqa_decode_auto_chunk", chunk)
+        self.chunk = int(chunk)
+        self.part_bytes = gqa_decode_part_bytes(S, T, Lmax, 0, H, D, self.chunk)
+        if self.part_bytes == 0 and Lmax > 0:
+            raise GqaDecodeError("gqa_decode_part_bytes", _lib.GQA_ERR_SHAPE)
+        self.part = torch.empty(max(1, (self.part_bytes + 3) // 4), dtype=torch.float32,
+                                device=device)
+        self.out = torch.empty((S, T, H, D), dtype=torch.float32, device=device)
+        self._dev = self.out.device.index
+        self._stream = _raw_stream_getter()
+        lib = _lib.load()
+        self._attn, self._merge = lib.gqa_decode_attn_tq, lib.gqa_decode_merge_tq
+
+    def attn(self, q_rot, q_jl, k_polar, k_jl, k_norms, v_polar, v_norms, seq_lens, centroids,
+             qjl_scale, scale, stream=None):
+        st = self._stream(self._dev) if stream is None else stream
+        c = [float(x) for x in centroids]
+        rc = self._attn(q_rot.data_ptr(), q_jl.data_ptr(), k_polar.data_ptr(), k_jl.data_ptr(),
+                        k_norms.data_ptr(), v_polar.data_ptr(), v_norms.data_ptr(),
+                        seq_lens.data_ptr(), self.part.data_ptr(), self.part_bytes, self.S, self.T,
+                        self.Lmax, self.H, self.Hk, self.D, c[0], c[1], c[2], c[3],
+                        float(qjl_scale), float(scale), self.chunk, st)
+        if rc:
+            raise GqaDecodeError("gqa_decode_attn_tq", rc)
+
+    def merge(self, seq_lens, signs, stream=None):
+        st = self._stream(self._dev) if stream is None else stream
+        rc = self._merge(self.part.data_ptr(), seq_lens.data_ptr(), signs.data_ptr(),
+                         self.out.data_ptr(), self.S, self.T, self.Lmax, self.H, self.D,
+                         self.chunk, st)
+        if rc:
+            raise GqaDecodeError("gqa_decode_merge_tq", rc)
+
+
+def tq_decode_attention(q_rot, q_jl, k_polar, k_jl, k_norms, v_polar, v_norms, seq_lens, signs,
+                        centroids, qjl_scale: float, scale: float, *, chunk: int = 0):
+    """One decode step over a TurboQuant-compressed cache.  q_rot, q_jl
+    [S][T][H][D] float32; k_polar, v_polar [S][Hk][Lmax][D/16], k_jl
+    [S][Hk][Lmax][D/32], k_norms, v_norms [S][Hk][Lmax] (int32 or uint32
+    words); seq_lens [S] int32; signs [D] float32; centroids: 4 floats.
+    Returns out [S][T][H][D] float32 in the original basis."""
+    import torch
+    for name, t in (("q_rot", q_rot), ("q_jl", q_jl), ("k_polar", k_polar), ("k_jl", k_jl),
+                    ("k_norms", k_norms), ("v_polar", v_polar), ("v_norms", v_norms),
+                    ("seq_lens", seq_lens), ("signs", signs)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor (there is no CPU path)")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if q_rot.dtype != torch.float32 or q_jl.dtype != torch.float32 or signs.dtype != torch.float32:
+        raise ValueError("q_rot, q_jl and signs must be float32")
+    if q_rot.shape != q_jl.shape:
+        raise ValueError("q_rot and q_jl must share a shape")
+    S, T, H, D = q_rot.shape
+    _, Hk, Lmax, W = k_polar.shape
+    if W * 16 != D or tuple(v_polar.shape) != tuple(k_polar.shape) \
+            or tuple(k_jl.shape) != (S, Hk, Lmax, D // 32) \
+            or tuple(k_norms.shape) != (S, Hk, Lmax) or tuple(v_norms.shape) != (S, Hk, Lmax) \
+            or tuple(signs.shape) != (D,) or tuple(seq_lens.shape) != (S,):
+        raise ValueError("shape mismatch between the query, the compressed cache and signs")
+    step = TqDecodeAttention(S, T, H, Hk, D, Lmax, chunk=chunk, device=q_rot.device)
+    step.attn(q_rot, q_jl, k_polar, k_jl, k_norms, v_polar, v_norms, seq_lens, centroids,
+              qjl_scale, scale)
+    step.merge(seq_lens, signs)
+    return step.out.clone()

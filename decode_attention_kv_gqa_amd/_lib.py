@@ -22,7 +22,8 @@ GQA_ERR_CHUNK = -6
 GQA_ERR_WORKSPACE = -7
 
 EXPORTED = ["gqa_decode_attn_f16", "gqa_decode_attn_i8", "gqa_decode_merge",
-            "gqa_decode_merge_gated", "gqa_decode_select_ids", "gqa_decode_append_i8", "gqa_decode_part_bytes",
+            "gqa_decode_merge_gated", "gqa_decode_attn_tq", "gqa_decode_merge_tq",
+            "gqa_decode_select_ids", "gqa_decode_append_i8", "gqa_decode_part_bytes",
             "gqa_decode_auto_chunk",
             "gqa_decode_strerror"]
 
@@ -54,6 +55,10 @@ def load() -> ctypes.CDLL:
     lib.gqa_decode_merge.restype = i32
     lib.gqa_decode_merge_gated.argtypes = [vp, vp, vp, vp, ctypes.c_int64, vp] + [i32] * 7 + [vp]
     lib.gqa_decode_merge_gated.restype = i32
+    lib.gqa_decode_attn_tq.argtypes = [vp] * 9 + [sz] + [i32] * 6 + [f32] * 6 + [i32, vp]
+    lib.gqa_decode_attn_tq.restype = i32
+    lib.gqa_decode_merge_tq.argtypes = [vp] * 4 + [i32] * 6 + [vp]
+    lib.gqa_decode_merge_tq.restype = i32
     lib.gqa_decode_select_ids.argtypes = [vp, vp, vp] + [i32] * 4 + [vp]
     lib.gqa_decode_select_ids.restype = i32
     lib.gqa_decode_append_i8.argtypes = [vp] * 7 + [i32] * 5 + [vp]
@@ -99,6 +104,20 @@ def gqa_decode_merge_gated(part, seq_lens, ids_or_null, gate, gate_stride, out, 
     return load().gqa_decode_merge_gated(_p(part), _p(seq_lens), _p(ids_or_null), _p(gate),
                                          int(gate_stride), _p(out), S, T, Lmax, B, H, D, chunk,
                                          _p(stream))
+
+
+def gqa_decode_attn_tq(q_rot, q_jl, k_polar, k_jl, k_norms, v_polar, v_norms, seq_lens, part,
+                       part_bytes, S, T, Lmax, H, Hk, D, c0, c1, c2, c3, qjl_scale, scale, chunk,
+                       stream=0) -> int:
+    return load().gqa_decode_attn_tq(_p(q_rot), _p(q_jl), _p(k_polar), _p(k_jl), _p(k_norms),
+                                     _p(v_polar), _p(v_norms), _p(seq_lens), _p(part), part_bytes,
+                                     S, T, Lmax, H, Hk, D, c0, c1, c2, c3, qjl_scale, scale, chunk,
+                                     _p(stream))
+
+
+def gqa_decode_merge_tq(part, seq_lens, signs, out, S, T, Lmax, H, D, chunk, stream=0) -> int:
+    return load().gqa_decode_merge_tq(_p(part), _p(seq_lens), _p(signs), _p(out), S, T, Lmax, H, D,
+                                      chunk, _p(stream))
 
 
 def gqa_decode_part_bytes(S, T, Lmax, B, H, D, chunk) -> int:

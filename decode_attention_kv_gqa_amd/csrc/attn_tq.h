@@ -1,0 +1,539 @@
+// Chunk kernel over a TurboQuant-compressed KV cache (cera 0.4.0,
+// flash_attention_tq.metal) on the gfx950 matrix cores.
+//
+// Per cell c of a KV head the cache holds, as the page lays it out:
+//   K: D/16 words of 2-bit polar indices, D/32 words of QJL sign bits, and one
+//      word holding the f16 key norm (low half) and f16 residual norm (high);
+//   V: D/16 words of 2-bit polar indices and one word with the f16 value norm.
+// The query arrives rotated (q_rot) and JL-projected (q_jl).  Score and value
+// (the page's header):
+//   score = scale * norm * (sum_d q_rot[d] c[idx_k[d]]
+//                           + residual * qjl_scale * sum_d q_jl[d] (2 bit[d] - 1))
+//   acc[d] += p * vnorm * c[idx_v[d]]        (rotated basis; the inverse
+//                                             rotation runs after the merge)
+// Keys and values are never rebuilt in the original basis.
+//
+// Layout of the work is that of the dense attention kernel: one workgroup per
+// (split, KV head, row block, sequence), four waves streaming their own
+// 32-cell tiles with their own online softmax (base 2, lazy rescale),
+// combined into one partial (o in the rotated basis, m, l) per query row.
+//
+// QK on v_mfma_f32_16x16x32_f16: A = decoded key fragments, B = the query
+// rows.  Lane group lb (lanes 16 lb .. 16 lb + 15) owns dims [lb D/4, (lb+1)
+// D/4) of every cell -- D/64 polar words and D/4 sign bits -- and covers
+// 8 of them per k-step; the query operands use the same dim assignment.
+//   polar:  each 2-bit index selects the f16 high and low parts of its
+//           centroid with one byte permute each (the centroid table is two
+//           dwords), so q_rot . c[idx] keeps ~22 bits: hi*hi + hi*lo + lo*hi.
+//   QJL:    sign bits become f16 0 / 1; the MFMA gives sum over set bits,
+//           and the signed sum is 2 * that - sum_d q_jl[d] (page's form).
+// PV on the same MFMA: A = p * vnorm (f16 hi + lo) straight from the score
+// accumulators, B = decoded value fragments: a lane needs one dim of eight
+// cells, so the tile's V index words are staged in LDS transposed
+// ([word][cell]) and each lane extracts its 2-bit field from eight words.
+#pragma once
+
+#include "attn_mfma.h"
+
+namespace gqa_kern {
+
+struct TqArgs {
+  const float* q_rot;        // [S][T][H][D]
+  const float* q_jl;         // [S][T][H][D]
+  const uint32_t* k_polar;   // [S][Hk][Lmax][D/16]
+  const uint32_t* k_jl;      // [S][Hk][Lmax][D/32]
+  const uint32_t* k_norms;   // [S][Hk][Lmax]
+  const uint32_t* v_polar;   // [S][Hk][Lmax][D/16]
+  const uint32_t* v_norms;   // [S][Hk][Lmax]
+  const int32_t* seq_lens;
+  float* part_o;             // [S][T][H][P][D]  (rotated basis)
+  float* part_ml;            // [S][T][H][P][2]
+  uint32_t chi_lo, chi_hi;   // f16 high parts of centroids 0,1 and 2,3 (perm table)
+  uint32_t clo_lo, clo_hi;   // f16 low parts (c - f16(c))
+  float qjl_scale;
+  float qscale;              // scale * log2(e)
+  int S, T, Lmax, H, Hk, G, R, nrb, P, chunk;
+};
+
+// LDS of one TurboQuant workgroup (four waves).
+template <int D, int NRB>
+struct TqLds {
+  static constexpr int NW = 4;
+  static constexpr int TC = 32;
+  static constexpr int RB = 16 * NRB;
+  static constexpr int KS = D / 32;
+  static constexpr int VW = D / 16;                          // V index words per cell
+  static constexpr int VT = NW * VW * TC * 4;                // per-wave transposed V words
+  static constexpr int NM = NW * 2 * TC * 4;                 // per-wave K and V norm words
+  static constexpr int QB = 2 * NRB * KS * 2 * 64 * 16;      // q_rot and q_jl operands, hi + lo
+  static constexpr int QS = RB * 4;                          // per-row sum of q_jl
+  static constexpr int ML = NW * RB * 2 * 4;
+  static constexpr int BUF = NW / 2 * RB * D * 4;            // cross-wave combine (aliases VT, NM, QB)
+  static constexpr int MAIN = VT + NM + QB;
+  static constexpr int BYTES = (MAIN > BUF ? MAIN : BUF) + QS + ML;
+};
+
+// Eight 2-bit indices (bits off .. off+15 of w) -> f16 high and low parts of
+// their centroids.  Pair j (fields 2j, 2j+1 -> a, b): the byte selector
+// [2a, 2a+1, 2b, 2b+1] picks both halves of centroid a and of centroid b out of
+// the 8-byte table.
+__device__ __forceinline__ void tq_polar8(uint32_t w, int off, uint32_t thi_lo, uint32_t thi_hi,
+                                          uint32_t tlo_lo, uint32_t tlo_hi, half8& hi, half8& lo) {
+  u32x4 h, l;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t u = __builtin_amdgcn_ubfe(w, off + 4 * j, 4);
+    const uint32_t x = (u * 0x4001u) & 0x00030003u;          // a at bit 0, b at bit 16
+    const uint32_t sel = x * 0x0202u + 0x01000100u;
+    h[j] = __builtin_amdgcn_perm(thi_hi, thi_lo, sel);
+    l[j] = __builtin_amdgcn_perm(tlo_hi, tlo_lo, sel);
+  }
+  hi = __builtin_bit_cast(half8, h);
+  lo = __builtin_bit_cast(half8, l);
+}
+
+// Eight sign bits (bits off .. off+7 of w) -> f16 1.0 where set, 0 elsewhere.
+__device__ __forceinline__ half8 tq_bits8(uint32_t w, int off) {
+  u32x4 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t t = __builtin_amdgcn_ubfe(w, off + 2 * j, 2);
+    r[j] = ((t * 0x8001u) & 0x00010001u) * 0x3C00u;         // bit 0 -> low f16, bit 1 -> high
+  }
+  return __builtin_bit_cast(half8, r);
+}
+
+__device__ __forceinline__ float f16lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu)); }
+__device__ __forceinline__ float f16hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+
+template <int D, int NRB>
+__global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
+  using L = TqLds<D, NRB>;
+  constexpr int NW = L::NW, NT = 64 * NW, TC = L::TC, RB = L::RB, KS = L::KS, VW = L::VW;
+  constexpr int NB = D / 16;                     // 16-dim output blocks
+  constexpr int KW = D / 64;                     // polar words per lane group and cell
+  static_assert(D == 64 || D == 128, "head_dim");
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int lr = lane & 15, lb = lane >> 4;
+
+  // 1-D grid: KV head fastest, then sequence, then row block, split slowest
+  int id = blockIdx.x;
+  const int g = id % a.Hk;
+  id /= a.Hk;
+  const int s = id % a.S;
+  id /= a.S;
+  const int rbl = id % a.nrb;
+  const int p = id / a.nrb;
+  const int r0 = rbl * RB;
+  auto row_t = [&](int r) -> int { return r / a.G; };
+  auto row_h = [&](int r) -> int { return g * a.G + r % a.G; };
+
+  const int seq_len = a.seq_lens[s];
+  auto width_of = [&](int r) -> int {
+    if (r >= a.R) return 0;
+    int Lt = seq_len - (a.T - 1 - row_t(r));
+    return Lt < 0 ? 0 : (Lt > a.Lmax ? a.Lmax : Lt);
+  };
+  const int rlast = (a.R - 1 < r0 + RB - 1) ? a.R - 1 : r0 + RB - 1;
+  const int wmax = width_of(rlast);
+  const int64_t c0l = (int64_t)p * a.chunk;
+  if (c0l >= wmax) {                             // empty split: weight 0
+    if (tid < RB && r0 + tid < a.R) {
+      const int r = r0 + tid;
+      const size_t prow = ((size_t)(s * a.T + row_t(r)) * a.H + row_h(r)) * a.P + p;
+      a.part_ml[prow * 2] = -INFINITY;
+      a.part_ml[prow * 2 + 1] = 0.f;
+    }
+    return;
+  }
+  const int c0 = (int)c0l;
+  const int cend = (int)((c0l + a.chunk < wmax) ? c0l + a.chunk : wmax);
+  const int lim_lo = width_of(r0) < cend ? width_of(r0) : cend;
+
+  uint32_t* vtw = reinterpret_cast<uint32_t*>(smem) + wave * VW * TC;          // [VW][TC]
+  uint32_t* nrm = reinterpret_cast<uint32_t*>(smem + L::VT) + wave * 2 * TC;   // K norms, V norms
+  u32x4* qlds = reinterpret_cast<u32x4*>(smem + L::VT + L::NM);
+  const int tail = L::MAIN > L::BUF ? L::MAIN : L::BUF;
+  float* qsum = reinterpret_cast<float*>(smem + tail);
+  float* mls = reinterpret_cast<float*>(smem + tail + L::QS);
+
+  // ---- query operands: q_rot and q_jl rows as f16 hi + lo, and each row's
+  // sum of q_jl (fp32) ----
+  for (int slot = tid; slot < 2 * NRB * KS * 64; slot += NT) {
+    const int which = slot / (NRB * KS * 64);    // 0: q_rot, 1: q_jl
+    const int sl = slot % (NRB * KS * 64);
+    const int ln = sl & 63, kks = sl >> 6;
+    const int ks = kks % KS, k = kks / KS;
+    const int r = r0 + 16 * k + (ln & 15);
+    const int d0 = (ln >> 4) * (D / 4) + 8 * ks;
+    float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (r < a.R) {
+      const float* src = (which ? a.q_jl : a.q_rot) +
+                         ((size_t)(s * a.T + row_t(r)) * a.H + row_h(r)) * D + d0;
+      const float4 u0 = *reinterpret_cast<const float4*>(src);
+      const float4 u1 = *reinterpret_cast<const float4*>(src + 4);
+      x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w;
+      x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
+    }
+    half8 hi, lo;
+    split_hi_lo(x, hi, lo);
+    const int base = ((which * NRB * KS + kks) * 2) * 64;
+    qlds[base + ln] = __builtin_bit_cast(u32x4, hi);
+    qlds[base + 64 + ln] = __builtin_bit_cast(u32x4, lo);
+  }
+  if (tid < RB) {
+    const int r = r0 + tid;
+    float t = 0.f;
+    if (r < a.R) {
+      const float* src = a.q_jl + ((size_t)(s * a.T + row_t(r)) * a.H + row_h(r)) * D;
+#pragma unroll 8
+      for (int d = 0; d < D; d += 4) {
+        const float4 u = *reinterpret_cast<const float4*>(src + d);
+        t += (u.x + u.y) + (u.z + u.w);
+      }
+    }
+    qsum[tid] = t;
+  }
+
+  int lim[NRB];
+#pragma unroll
+  for (int k = 0; k < NRB; ++k) {
+    const int wr = width_of(r0 + 16 * k + lr);
+    lim[k] = wr < cend ? wr : cend;
+  }
+
+  // ---- compressed rows of this split through range-checked buffer
+  // resources: reads past the split's last cell return zeros ----
+  const size_t first = ((size_t)s * a.Hk + g) * a.Lmax + c0;
+  const uint32_t ncells = (uint32_t)(cend - c0);
+  const __amdgpu_buffer_rsrc_t rkp = make_rsrc(a.k_polar + first * VW, ncells * VW * 4);
+  const __amdgpu_buffer_rsrc_t rkj = make_rsrc(a.k_jl + first * (D / 32), ncells * (D / 32) * 4);
+  const __amdgpu_buffer_rsrc_t rkn = make_rsrc(a.k_norms + first, ncells * 4);
+  const __amdgpu_buffer_rsrc_t rvp = make_rsrc(a.v_polar + first * VW, ncells * VW * 4);
+  const __amdgpu_buffer_rsrc_t rvn = make_rsrc(a.v_norms + first, ncells * 4);
+
+  struct KRegs {
+    uint32_t pol[2][KW];       // this lane's polar words of cells 16 cb + lr
+    uint32_t jl[2];            // the sign-bit word holding this lane group's dims
+  };
+  struct VRegs {
+    uint32_t pol[VW / 2];      // lane l: cell l / 2, words (l % 2) * VW/2 ..
+    uint32_t nrm;              // lanes 0-31: K norm word of cell l; 32-63: V norm word of cell l - 32
+  };
+
+  auto issue_k = [&](int ts, KRegs& R) {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const uint32_t cell = (uint32_t)(ts + 16 * cb + lr - c0);
+      if constexpr (KW == 2) {
+        const u32x2 w = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_raw_buffer_load_b64(rkp, (cell * VW + 2 * lb) * 4, 0, kNT));
+        R.pol[cb][0] = w[0];
+        R.pol[cb][1] = w[1];
+      } else {
+        R.pol[cb][0] = __builtin_amdgcn_raw_buffer_load_b32(rkp, (cell * VW + lb) * 4, 0, kNT);
+      }
+      R.jl[cb] = __builtin_amdgcn_raw_buffer_load_b32(
+          rkj, (cell * (D / 32) + (lb * (D / 4)) / 32) * 4, 0, kNT);
+    }
+  };
+  auto issue_v = [&](int ts, VRegs& R) {
+    const uint32_t cell = (uint32_t)(ts + (lane >> 1) - c0);
+    const uint32_t off = (cell * VW + (lane & 1) * (VW / 2)) * 4;
+    if constexpr (VW == 8) {
+      const u32x4 w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rvp, off, 0, kNT));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) R.pol[j] = w[j];
+    } else {
+      const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rvp, off, 0, kNT));
+      R.pol[0] = w[0];
+      R.pol[1] = w[1];
+    }
+    const uint32_t nc = (uint32_t)(ts + (lane & 31) - c0);
+    R.nrm = lane < 32 ? __builtin_amdgcn_raw_buffer_load_b32(rkn, nc * 4, 0, 0)
+                      : __builtin_amdgcn_raw_buffer_load_b32(rvn, nc * 4, 0, 0);
+  };
+
+  constexpr float kTau = 8.0f;
+  float tau = kTau;
+  auto stage = [&](const VRegs& R) {
+    const int cell = lane >> 1;
+#pragma unroll
+    for (int j = 0; j < VW / 2; ++j) vtw[((lane & 1) * (VW / 2) + j) * TC + cell] = R.pol[j];
+    nrm[lane] = R.nrm;
+    // p * vnorm must stay in f16 range: a tile with a value norm above 255
+    // tracks the exact max (tau 0, p <= 1)
+    const bool big = lane >= 32 && (R.nrm & 0x7fffu) > 0x5bf8u;
+    tau = __any(big) ? 0.0f : kTau;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  };
+
+  f32x4 O[NRB][NB];
+  float m_run[NRB], l_run[NRB];
+#pragma unroll
+  for (int k = 0; k < NRB; ++k) {
+    m_run[k] = -INFINITY;
+    l_run[k] = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) O[k][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  float qs[NRB];                                 // sum of q_jl of this lane's rows 16k + lr
+
+  // ---- QK: S[cb][k][i] = score (base 2) of cell ts+16cb+4lb+i for row 16k+lr ----
+  auto qk = [&](const KRegs& R, f32x4 (&S)[2][NRB]) {
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    f32x4 Sp[2][NRB], Sj[2][NRB];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int k = 0; k < NRB; ++k) {
+        Sp[cb][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+        Sj[cb][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      half8 ch[2], cl[2], jb[2];
+      const int dl = 8 * ks;                     // dim offset inside the lane group's span
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        tq_polar8(R.pol[cb][dl / 16], 2 * (dl % 16), a.chi_lo, a.chi_hi, a.clo_lo, a.clo_hi,
+                  ch[cb], cl[cb]);
+        jb[cb] = tq_bits8(R.jl[cb], (lb * (D / 4) + dl) % 32);
+      }
+#pragma unroll
+      for (int k = 0; k < NRB; ++k) {
+        const int br = ((0 * NRB * KS + k * KS + ks) * 2) * 64;
+        const int bj = ((1 * NRB * KS + k * KS + ks) * 2) * 64;
+        const half8 qh = __builtin_bit_cast(half8, qlds[br + lane]);
+        const half8 ql = __builtin_bit_cast(half8, qlds[br + 64 + lane]);
+        const half8 jh = __builtin_bit_cast(half8, qlds[bj + lane]);
+        const half8 jl = __builtin_bit_cast(half8, qlds[bj + 64 + lane]);
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+          Sp[cb][k] = mfma16(ch[cb], qh, Sp[cb][k]);
+          Sp[cb][k] = mfma16(ch[cb], ql, Sp[cb][k]);
+          Sp[cb][k] = mfma16(cl[cb], qh, Sp[cb][k]);
+          Sj[cb][k] = mfma16(jb[cb], jh, Sj[cb][k]);
+          Sj[cb][k] = mfma16(jb[cb], jl, Sj[cb][k]);
+        }
+      }
+    }
+    // score = qscale * norm * (polar + residual * qjl_scale * (2 pos - sum q_jl))
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const u32x4 kn = *reinterpret_cast<const u32x4*>(nrm + 16 * cb + 4 * lb);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float n = f16lo(kn[i]) * a.qscale;
+        const float rq = f16hi(kn[i]) * a.qjl_scale;
+#pragma unroll
+        for (int k = 0; k < NRB; ++k)
+          S[cb][k][i] = n * __builtin_fmaf(rq, __builtin_fmaf(2.f, Sj[cb][k][i], -qs[k]), Sp[cb][k][i]);
+      }
+    }
+  };
+
+  // ---- online softmax per row, then PV in the rotated basis ----
+  auto softmax_pv = [&](int ts, const f32x4 (&S)[2][NRB]) {
+    const bool edge = ts + TC > lim_lo;
+    float pr[NRB][8];
+#pragma unroll
+    for (int k = 0; k < NRB; ++k) {
+      float x[8];
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[4 * cb + i] = S[cb][k][i];
+      if (edge) {
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (ts + 16 * cb + 4 * lb + i >= lim[k]) x[4 * cb + i] = -INFINITY;
+      }
+      float tmax = x[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) tmax = fmaxf(tmax, x[e]);
+      tmax = max_x32(max_x16(tmax));
+      const float mold = m_run[k];
+      const bool bump = tmax > mold + tau;
+      const float mnew = bump ? tmax : mold;
+      const float corr = bump && mold != -INFINITY ? __builtin_amdgcn_exp2f(mold - mnew) : 1.0f;
+      float psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pe = (x[e] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x[e] - mnew);
+        pr[k][e] = pe;
+        psum += pe;
+      }
+      psum = sum_x32(sum_x16(psum));
+      l_run[k] = l_run[k] * corr + psum;
+      m_run[k] = mnew;
+      if (__any(corr != 1.0f)) {
+        float cf[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cf[i] = __shfl(corr, 4 * lb + i, 64);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) O[k][nb][i] *= cf[i];
+      }
+    }
+    // P' = p * vnorm of each of this lane's eight cells (A operand k = 8 lb + e)
+    half8 phi[NRB], plo[NRB];
+    {
+      const u32x4 va = *reinterpret_cast<const u32x4*>(nrm + TC + 4 * lb);
+      const u32x4 vb = *reinterpret_cast<const u32x4*>(nrm + TC + 16 + 4 * lb);
+      float vn[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        vn[i] = f16lo(va[i]);
+        vn[4 + i] = f16lo(vb[i]);
+      }
+#pragma unroll
+      for (int k = 0; k < NRB; ++k) {
+        float pv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv[e] = pr[k][e] * vn[e];
+        split_hi_lo(pv, phi[k], plo[k]);
+      }
+    }
+    // value fragments: lane (dim 16 nb + lr, k-group lb) takes field lr of the
+    // index words of cells 4lb .. 4lb+3 and 16+4lb .. 16+4lb+3
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const u32x4 wa = *reinterpret_cast<const u32x4*>(vtw + nb * TC + 4 * lb);
+      const u32x4 wb = *reinterpret_cast<const u32x4*>(vtw + nb * TC + 16 + 4 * lb);
+      const uint32_t w[8] = {wa[0], wa[1], wa[2], wa[3], wb[0], wb[1], wb[2], wb[3]};
+      u32x4 h, l;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t ia = __builtin_amdgcn_ubfe(w[2 * j], 2 * lr, 2);
+        const uint32_t ib = __builtin_amdgcn_ubfe(w[2 * j + 1], 2 * lr, 2);
+        const uint32_t sel = (ia | (ib << 16)) * 0x0202u + 0x01000100u;
+        h[j] = __builtin_amdgcn_perm(a.chi_hi, a.chi_lo, sel);
+        l[j] = __builtin_amdgcn_perm(a.clo_hi, a.clo_lo, sel);
+      }
+      const half8 vh = __builtin_bit_cast(half8, h);
+      const half8 vl = __builtin_bit_cast(half8, l);
+#pragma unroll
+      for (int k = 0; k < NRB; ++k) {
+        O[k][nb] = mfma16(phi[k], vh, O[k][nb]);
+        O[k][nb] = mfma16(plo[k], vh, O[k][nb]);
+        O[k][nb] = mfma16(phi[k], vl, O[k][nb]);
+      }
+    }
+  };
+
+  // ---- main loop: the first tile is requested before the query operands are
+  // staged; then K and V of tile t+1 are in flight while tile t computes ----
+  {
+    KRegs RK;
+    VRegs RV;
+    int ts = c0 + TC * wave;
+    issue_v(ts, RV);
+    issue_k(ts, RK);
+    __syncthreads();                             // query operands and sums staged
+#pragma unroll
+    for (int k = 0; k < NRB; ++k) qs[k] = qsum[16 * k + lr];
+#pragma unroll 1
+    while (ts < cend) {
+      const int tn = ts + NW * TC;
+      stage(RV);
+      issue_v(tn, RV);
+      f32x4 S[2][NRB];
+      qk(RK, S);
+      issue_k(tn, RK);
+      softmax_pv(ts, S);
+      ts = tn;
+    }
+  }
+
+  // ---- combine the four waves into one partial per query row (as the
+  // dense kernel) ----
+  __syncthreads();
+  if (lb == 0) {
+#pragma unroll
+    for (int k = 0; k < NRB; ++k) {
+      mls[(wave * RB + 16 * k + lr) * 2] = m_run[k];
+      mls[(wave * RB + 16 * k + lr) * 2 + 1] = l_run[k];
+    }
+  }
+  __syncthreads();
+  float* buf = reinterpret_cast<float*>(smem);
+  constexpr int HALF = NW / 2;
+#pragma unroll
+  for (int k = 0; k < NRB; ++k) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * k + 4 * lb + i;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, mls[(w * RB + row) * 2]);
+      const float ms = mls[(wave * RB + row) * 2];
+      const float f = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) O[k][nb][i] *= f;
+    }
+  }
+  if (wave >= HALF) {
+    float* b = buf + (wave - HALF) * RB * D;
+#pragma unroll
+    for (int k = 0; k < NRB; ++k)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) b[(16 * k + 4 * lb + i) * D + 16 * nb + lr] = O[k][nb][i];
+  }
+  __syncthreads();
+  if (wave < HALF) {
+    float* b = buf + wave * RB * D;
+#pragma unroll
+    for (int k = 0; k < NRB; ++k)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float* x = b + (16 * k + 4 * lb + i) * D + 16 * nb + lr;
+          *x = *x + O[k][nb][i];
+        }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < RB * D / 4; idx += NT) {
+    const int row = idx / (D / 4);
+    const int d4 = idx % (D / 4);
+    const int r = r0 + row;
+    if (r < a.R) {
+      float4 x = *reinterpret_cast<const float4*>(buf + row * D + 4 * d4);
+#pragma unroll
+      for (int w = 1; w < HALF; ++w) {
+        const float4 y = *reinterpret_cast<const float4*>(buf + w * RB * D + row * D + 4 * d4);
+        x.x += y.x; x.y += y.y; x.z += y.z; x.w += y.w;
+      }
+      const size_t prow = ((size_t)(s * a.T + row_t(r)) * a.H + row_h(r)) * a.P + p;
+      *reinterpret_cast<float4*>(a.part_o + prow * D + 4 * d4) = x;
+    }
+  }
+  if (tid < RB && r0 + tid < a.R) {
+    const int row = tid;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, mls[(w * RB + row) * 2]);
+    float Ls = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float mw = mls[(w * RB + row) * 2];
+      if (mw != -INFINITY) Ls += mls[(w * RB + row) * 2 + 1] * __builtin_amdgcn_exp2f(mw - M);
+    }
+    const int r = r0 + row;
+    const size_t prow = ((size_t)(s * a.T + row_t(r)) * a.H + row_h(r)) * a.P + p;
+    a.part_ml[prow * 2] = M;
+    a.part_ml[prow * 2 + 1] = Ls;
+  }
+}
+
+}  // namespace gqa_kern

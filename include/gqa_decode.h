@@ -7,6 +7,8 @@
  *   gqa_decode_attn_f16 / gqa_decode_attn_i8   chunk partials (o, m, l)
  *   gqa_decode_merge                            log-sum-exp merge -> out
  *   gqa_decode_merge_gated                      the merge times sigmoid(gate)
+ *   gqa_decode_attn_tq / gqa_decode_merge_tq     the same step over a
+ *                                               TurboQuant-compressed cache
  *
  * preceded, for budgeted attention, by gqa_decode_select_ids (the B cell ids
  * of every token from per-block scores); gqa_decode_append_i8 writes new K/V
@@ -148,6 +150,52 @@ int gqa_decode_merge_gated(const float *part, const int32_t *seq_lens, const int
                            const float *gate, int64_t gate_stride, float *out,
                            int S, int T, int Lmax, int B, int H, int D, int chunk,
                            void *stream);
+
+/* Chunk partials over a TurboQuant-compressed cache (cera 0.4.0,
+ * flash_attention_tq.metal: header formulas, kernel flash_attention_tq).
+ * Keys and values are never rebuilt; for cell c of KV head g, in the page's
+ * notation:
+ *   polar_dot  = sum_d q_rot[d] * centroid[idx_k[d]]
+ *   signed_sum = 2 * sum_{d: jl_bit[d] = 1} q_jl[d] - sum_d q_jl[d]
+ *   score      = scale * (norm * polar_dot
+ *                         + norm * residual_norm * qjl_scale * signed_sum)
+ * softmax over the causal window (L_t as for the other attention calls), and
+ * the value accumulator stays in the rotated basis:
+ *   o[d] = sum_c p_c * vnorm_c * centroid[idx_v[c][d]]
+ * so the partials are rotated; gqa_decode_merge_tq merges them and applies
+ * the inverse rotation.
+ *   q_rot, q_jl  [S][T][H][D] float32: the query rotated by the key rotation,
+ *                and its JL projection (both prepared by the caller)
+ *   k_polar      [S][Hk][Lmax][D/16] uint32: 2-bit centroid indices, dim
+ *                16w + i in bits 2i, 2i+1 of word w (per cell, head-major as
+ *                the page's slot = kv_head * cache_cap + t)
+ *   k_jl         [S][Hk][Lmax][D/32] uint32: sign bits, dim 32w + i in bit i
+ *   k_norms      [S][Hk][Lmax] uint32: f16 norm (low half), f16 residual
+ *                norm (high half)
+ *   v_polar      [S][Hk][Lmax][D/16] uint32, v_norms [S][Hk][Lmax] uint32
+ *                (f16 value norm in the low half)
+ *   c0 .. c3     the four centroids; qjl_scale (the page uses
+ *                sqrt(pi/2) / head_dim); scale the score scale
+ * D must be 64 or 128 (the page: at most 128); no ids.  Workspace, chunk,
+ * stream and errors as gqa_decode_attn_f16. */
+int gqa_decode_attn_tq(const float *q_rot, const float *q_jl, const uint32_t *k_polar,
+                       const uint32_t *k_jl, const uint32_t *k_norms, const uint32_t *v_polar,
+                       const uint32_t *v_norms, const int32_t *seq_lens,
+                       float *part, size_t part_bytes,
+                       int S, int T, int Lmax, int H, int Hk, int D,
+                       float c0, float c1, float c2, float c3, float qjl_scale, float scale,
+                       int chunk, void *stream);
+
+/* Merge of gqa_decode_attn_tq's rotated partials followed by the inverse
+ * randomized Hadamard rotation (flash_attention_tq.metal, epilogue):
+ *   out = signs * (H_D @ merged) / sqrt(D)
+ * where H_D is the Sylvester Walsh-Hadamard matrix (the page's butterfly
+ * passes) and signs [D] float32 is the key rotation's sign flips (+-1).
+ * Rows with an empty window get zeros.  Other arguments and errors as
+ * gqa_decode_merge (no ids; D 64 or 128). */
+int gqa_decode_merge_tq(const float *part, const int32_t *seq_lens, const float *signs,
+                        float *out, int S, int T, int Lmax, int H, int D, int chunk,
+                        void *stream);
 
 /* Budget selection: the ids a budgeted token attends (qsa2.metal, kernel
  * qsa_topk2).  Cells come in blocks of 4 with one score per block; with

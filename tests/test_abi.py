@@ -96,6 +96,26 @@ def test_merge_gated_rejects():
     assert m(FAKE, FAKE, None, FAKE, 96, FAKE, 1, 1, 16, 0, 8, 96, 32, 0) == _lib.GQA_ERR_HEAD_DIM
 
 
+def test_tq_rejects():
+    a = gq.gqa_decode_attn_tq
+    args = lambda **kw: dict(dict(q_rot=FAKE, q_jl=FAKE, k_polar=FAKE, k_jl=FAKE, k_norms=FAKE,
+                                  v_polar=FAKE, v_norms=FAKE, seq_lens=FAKE, part=FAKE,
+                                  part_bytes=1 << 40, S=1, T=1, Lmax=64, H=8, Hk=2, D=64, c0=-1.0,
+                                  c1=-0.3, c2=0.3, c3=1.0, qjl_scale=0.02, scale=0.125, chunk=32),
+                             **kw)
+    call = lambda **kw: a(**args(**kw), stream=0)
+    assert call(k_jl=None) == _lib.GQA_ERR_NULL
+    assert call(q_jl=None) == _lib.GQA_ERR_NULL
+    assert call(D=256) == _lib.GQA_ERR_HEAD_DIM            # the page's limit: head_dim <= 128
+    assert call(D=96) == _lib.GQA_ERR_HEAD_DIM
+    assert call(H=6, Hk=4) == _lib.GQA_ERR_GROUP
+    assert call(part_bytes=16) == _lib.GQA_ERR_WORKSPACE
+    m = gq.gqa_decode_merge_tq
+    assert m(FAKE, FAKE, None, FAKE, 1, 1, 64, 8, 64, 32, 0) == _lib.GQA_ERR_NULL
+    assert m(FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 8, 256, 32, 0) == _lib.GQA_ERR_HEAD_DIM
+    assert m(FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 8, 64, 0, 0) == _lib.GQA_ERR_CHUNK
+
+
 def test_part_bytes_formula():
     # splits = ceil(width / chunk); one (D + 2)-float partial per query row and split
     assert gq.gqa_decode_part_bytes(8, 1, 32768, 0, 24, 256, 512) == 8 * 24 * 64 * 258 * 4

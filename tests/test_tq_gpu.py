@@ -1,0 +1,98 @@
+"""GPU parity of decode attention over a TurboQuant-compressed cache
+(gqa_decode_attn_tq + gqa_decode_merge_tq) against the fp64 oracle
+(oracle/tq_ref.py), on identical seeded inputs.  Same bar as the other
+attention paths (tests/conftest.py)."""
+import numpy as np
+import pytest
+
+from conftest import assert_parity
+from oracle import tq_ref as R
+from workloads import make_tq_case, make_tq_inputs, TQ_WORKLOADS
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import decode_attention_kv_gqa_amd  # noqa: F401
+
+
+def dev(x):
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint32:
+        x = x.view(np.int32)                     # torch has no uint32 arithmetic; bits are kept
+    return torch.from_numpy(x).cuda()
+
+
+def run_tq(inp, chunk=0):
+    import decode_attention_kv_gqa_amd as gq
+    print(f"[gpu] tq shape={inp.shape} lens={list(inp.seq_lens)[:4]} chunk={chunk}", flush=True)
+    out = gq.tq_decode_attention(dev(inp.q_rot), dev(inp.q_jl), dev(inp.k_polar), dev(inp.k_jl),
+                                 dev(inp.k_norms), dev(inp.v_polar), dev(inp.v_norms),
+                                 dev(inp.seq_lens), dev(inp.signs), inp.centroids, inp.qjl_scale,
+                                 inp.scale, chunk=chunk)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def oracle(inp, rows=None):
+    return R.tq_decode_ref(inp.q_rot, inp.q_jl, inp.k_polar, inp.k_jl, inp.k_norms, inp.v_polar,
+                           inp.v_norms, inp.seq_lens, inp.signs, inp.centroids, inp.qjl_scale,
+                           inp.scale, rows=rows)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("G", [1, 4])
+@pytest.mark.parametrize("T", [1, 3])
+def test_tq_small(D, G, T):
+    inp = make_tq_case(3, T, 2 * G, 2, D, 700, [700, 333, 0], seed=D + 10 * G + T)
+    ref = oracle(inp)
+    for chunk in (32, 100, 0):
+        got = run_tq(inp, chunk)
+        assert_parity(got, ref, f"tq D={D} G={G} T={T} chunk={chunk}")
+        assert not got[2].any()                   # empty windows give zeros
+
+
+@pytest.mark.parametrize("L", [1, 31, 32, 33, 64, 129])
+def test_tq_lengths_around_tiles(L):
+    inp = make_tq_case(2, 1, 8, 2, 128, 200, [L, max(0, L - 1)], seed=L)
+    ref = oracle(inp)
+    for chunk in (32, 64, 0):
+        assert_parity(run_tq(inp, chunk), ref, f"tq L={L} chunk={chunk}")
+
+
+def test_tq_two_row_blocks_and_many_rows():
+    # 12 query heads per KV head x 2 tokens = 24 rows: two 16-row MFMA blocks;
+    # 40 query heads per KV head: two workgroup row blocks
+    for H, Hk, T in ((24, 2, 2), (40, 1, 1)):
+        inp = make_tq_case(2, T, H, Hk, 64, 300, [300, 150], seed=H + T)
+        assert_parity(run_tq(inp, 0), oracle(inp), f"tq rows H={H} Hk={Hk} T={T}")
+
+
+def test_tq_large_value_norms_and_sharp_scores():
+    # value norms above 255 (exact running max) and large scores (scale 4)
+    inp = make_tq_case(1, 1, 8, 2, 128, 500, [500], seed=77, scale=4.0)
+    v = inp.v_norms.astype(np.uint32)
+    big = np.float16(1000.0).view(np.uint16)
+    v[0, :, ::7] = big
+    inp.v_norms[...] = v
+    assert_parity(run_tq(inp, 64), oracle(inp), "tq big value norms, scale 4")
+
+
+def test_tq_full_size_sampled_rows():
+    name = "tq_128k"
+    w = TQ_WORKLOADS[name]
+    inp = make_tq_inputs(name)
+    got = run_tq(inp, 0)
+    assert np.isfinite(got).all()
+    S, T, H, _ = inp.q_rot.shape
+    rng = np.random.default_rng(w["index"])
+    rows = sorted({(int(rng.integers(S)), 0, int(rng.integers(H))) for _ in range(10)}
+                  | {(0, 0, 0), (S - 1, 0, H - 1)})
+    ref = oracle(inp, rows=rows)
+    g = np.stack([got[s, t, h] for (s, t, h) in rows])
+    assert_parity(g, ref, f"{name} sampled rows")
