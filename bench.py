@@ -49,6 +49,7 @@ KERNEL_SOURCES = {
     "attn": ["attn_mfma.h", "common.h", "gqa_decode.hip", "plan.h", "plan.cpp"],
     "append": ["append.hip"],
     "select": ["select.hip"],
+    "tq": ["attn_tq.h", "attn_mfma.h", "common.h", "tq.hip", "plan.h", "plan.cpp"],
 }
 
 
@@ -220,6 +221,85 @@ def bench_append(args):
                      "traffic": load_traffic(args.workload, "append")}}), flush=True)
 
 
+def bench_tq(args):
+    """Decode step over a TurboQuant-compressed cache (gqa_decode_attn_tq +
+    gqa_decode_merge_tq): compressed cache resident in HBM, copies rotated so
+    no step finds its cache in the last-level cache; K steps timed by wall
+    clock, the chunk kernel alone by HIP events over bursts.  One JSON line."""
+    import numpy as np
+    import torch
+    import decode_attention_kv_gqa_amd as gq
+    from workloads import TQ_WORKLOADS, make_tq_inputs, tq_bytes
+    inp = make_tq_inputs(args.workload)
+    sh = inp.shape
+    nbytes = tq_bytes(inp)
+    dev = torch.device("cuda:0")
+    d = lambda x: torch.from_numpy(np.ascontiguousarray(x.view(np.int32) if x.dtype == np.uint32
+                                                        else x)).to(dev)
+    foot = sum(x.nbytes for x in (inp.k_polar, inp.k_jl, inp.k_norms, inp.v_polar, inp.v_norms))
+    copies = args.copies or max(2, min(8, math.ceil(3 * LLC_BYTES / foot) + 1))
+    sets = [dict(q_rot=d(inp.q_rot), q_jl=d(inp.q_jl), k_polar=d(inp.k_polar), k_jl=d(inp.k_jl),
+                 k_norms=d(inp.k_norms), v_polar=d(inp.v_polar), v_norms=d(inp.v_norms))
+            for _ in range(copies)]
+    lens, signs = d(inp.seq_lens), d(inp.signs)
+    step = gq.TqDecodeAttention(sh["S"], sh["T"], sh["H"], sh["Hk"], sh["D"], sh["Lmax"],
+                                chunk=max(0, args.chunk), device=dev)
+
+    def attn(i):
+        x = sets[i % copies]
+        step.attn(x["q_rot"], x["q_jl"], x["k_polar"], x["k_jl"], x["k_norms"], x["v_polar"],
+                  x["v_norms"], lens, inp.centroids, inp.qjl_scale, inp.scale)
+
+    def one(i):
+        attn(i)
+        step.merge(lens, signs)
+
+    for i in range(args.warmup):
+        one(i)
+    torch.cuda.synchronize()
+    t_w, extra = time.perf_counter(), 0
+    while time.perf_counter() - t_w < SETTLE_S:
+        for i in range(10):
+            one(i)
+        extra += 10
+        torch.cuda.synchronize()
+    K = args.steps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        one(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stream = torch.cuda.current_stream()
+    bursts, per = 5, max(1, K // 5)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(bursts)]
+    for b in range(bursts):
+        evs[b][0].record(stream)
+        for i in range(per):
+            attn(b * per + i)
+        evs[b][1].record(stream)
+    torch.cuda.synchronize()
+    attn_ms = np.array([a.elapsed_time(b) / per for a, b in evs])
+    kern_s = float(attn_ms.mean()) / 1e3
+    achieved = nbytes / kern_s / 1e9
+    print(json.dumps({
+        "metric": "TurboQuant-cache decode effective cache GB/s and us/step, 1 MI355X",
+        "value": round(nbytes / (wall / K) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "extra_warmup_steps": extra, "us_per_step": round(wall / K * 1e6, 2),
+        "higher_is_better": True, "dtype": "2-bit polar + 1-bit QJL codes, f16 norms",
+        "data": "synthetic (seeded numpy: uniform codes, f16 norms, N(0,1) rotated queries)",
+        "config": {"workload": args.workload, **sh, "chunk": step.chunk,
+                   "cache_bytes_per_step": nbytes, "input_copies_rotated": copies},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": load_traffic(args.workload, "tq"), "kernel": "attn_tq",
+                     "kernel_us_mean": round(kern_s * 1e6, 3),
+                     "kernel_us_burst_min_max": [round(float(attn_ms.min()) * 1e3, 3),
+                                                 round(float(attn_ms.max()) * 1e3, 3)]}}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -247,7 +327,8 @@ def main():
     import numpy as np
     import torch
     import decode_attention_kv_gqa_amd as gq
-    from workloads import WORKLOADS, SELECT_WORKLOADS, APPEND_WORKLOADS, make_inputs, kv_bytes
+    from workloads import (WORKLOADS, SELECT_WORKLOADS, APPEND_WORKLOADS, TQ_WORKLOADS,
+                           make_inputs, kv_bytes)
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -257,6 +338,9 @@ def main():
         return
     if args.workload in APPEND_WORKLOADS:
         bench_append(args)
+        return
+    if args.workload in TQ_WORKLOADS:
+        bench_tq(args)
         return
     w = WORKLOADS[args.workload]
     chunk = w.chunk if args.chunk < 0 else args.chunk

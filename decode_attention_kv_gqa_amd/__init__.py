@@ -225,7 +225,7 @@ class TqDecodeAttention:
         import torch
         self.S, self.T, self.H, self.Hk, self.D, self.Lmax = S, T, H, Hk, D, Lmax
         if chunk <= 0:
-            chunk = gqa_decode_auto_chunk(S, T, Lmax, 0, H, Hk, D, True)
+            chunk = gqa_decode_auto_chunk(S, T, Lmax, 0, H, Hk, D, 2)
             if chunk <= 0:
                 raise GqaDecodeError("gqa_decode_auto_chunk", chunk)
         self.chunk = int(chunk)

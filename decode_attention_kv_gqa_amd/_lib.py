@@ -124,8 +124,9 @@ def gqa_decode_part_bytes(S, T, Lmax, B, H, D, chunk) -> int:
     return load().gqa_decode_part_bytes(S, T, Lmax, B, H, D, chunk)
 
 
-def gqa_decode_auto_chunk(S, T, Lmax, B, H, Hk, D, kv_is_i8) -> int:
-    return load().gqa_decode_auto_chunk(S, T, Lmax, B, H, Hk, D, int(bool(kv_is_i8)))
+def gqa_decode_auto_chunk(S, T, Lmax, B, H, Hk, D, kv_kind) -> int:
+    """kv_kind: 0 (or False) f16, 1 (or True) int8, 2 TurboQuant."""
+    return load().gqa_decode_auto_chunk(S, T, Lmax, B, H, Hk, D, int(kv_kind))
 
 
 def gqa_decode_select_ids(block_scores, seq_lens, ids, S, T, Lmax, B, stream=0) -> int:

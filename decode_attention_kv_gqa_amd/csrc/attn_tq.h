@@ -22,11 +22,12 @@
 // rows.  Lane group lb (lanes 16 lb .. 16 lb + 15) owns dims [lb D/4, (lb+1)
 // D/4) of every cell -- D/64 polar words and D/4 sign bits -- and covers
 // 8 of them per k-step; the query operands use the same dim assignment.
-//   polar:  each 2-bit index selects the f16 high and low parts of its
-//           centroid with one byte permute each (the centroid table is two
-//           dwords), so q_rot . c[idx] keeps ~22 bits: hi*hi + hi*lo + lo*hi.
-//   QJL:    sign bits become f16 0 / 1; the MFMA gives sum over set bits,
-//           and the signed sum is 2 * that - sum_d q_jl[d] (page's form).
+//   polar:  each pair of 2-bit indices looks up the f16 high and low parts
+//           of its two centroids in a 16-entry LDS table, so q_rot . c[idx]
+//           keeps ~22 bits: hi*hi + hi*lo + lo*hi.
+//   QJL:    each nibble of sign bits looks up four f16 0 / 1 values; the
+//           MFMA gives the sum over set bits, and the signed sum is
+//           2 * that - sum_d q_jl[d] (the page's form).
 // PV on the same MFMA: A = p * vnorm (f16 hi + lo) straight from the score
 // accumulators, B = decoded value fragments: a lane needs one dim of eight
 // cells, so the tile's V index words are staged in LDS transposed
@@ -73,33 +74,44 @@ struct TqLds {
   static constexpr int BYTES = (MAIN > BUF ? MAIN : BUF) + QS + ML;
 };
 
+// Decoding goes through 16-entry tables in the kernel's static LDS (at fixed
+// addresses, so a lookup's address is the extracted field scaled to the entry
+// size), built once per workgroup; a lookup replaces the bit arithmetic:
+//   chi[u], u = (b << 2) | a for two 2-bit indices a, b: the f16 high parts
+//           of centroids a and b (one dword of the MFMA operand);
+//   clo[u]  their f16 low parts -- 1 KB after chi, so the compiler keeps the
+//           two reads apart and each lands in its own operand register;
+//   jtab[u], u = four sign bits: four f16 values 0 / 1.
+// Each table's entries sit in distinct banks, so a wave's lookups never
+// conflict (equal entries broadcast).
+constexpr int kTqCtabHi = 0, kTqJtab = 64, kTqCtabLo = 1024, kTqTabBytes = 1088;
+
+__device__ __forceinline__ uint32_t lds_u32(const uint8_t* base, uint32_t byte) {
+  return *reinterpret_cast<const uint32_t*>(base + byte);
+}
+
 // Eight 2-bit indices (bits off .. off+15 of w) -> f16 high and low parts of
-// their centroids.  Pair j (fields 2j, 2j+1 -> a, b): the byte selector
-// [2a, 2a+1, 2b, 2b+1] picks both halves of centroid a and of centroid b out of
-// the 8-byte table.
-__device__ __forceinline__ void tq_polar8(uint32_t w, int off, uint32_t thi_lo, uint32_t thi_hi,
-                                          uint32_t tlo_lo, uint32_t tlo_hi, half8& hi, half8& lo) {
+// their centroids.
+__device__ __forceinline__ void tq_polar8(uint32_t w, int off, const uint8_t* tab, half8& hi,
+                                          half8& lo) {
   u32x4 h, l;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const uint32_t u = __builtin_amdgcn_ubfe(w, off + 4 * j, 4);
-    const uint32_t x = (u * 0x4001u) & 0x00030003u;          // a at bit 0, b at bit 16
-    const uint32_t sel = x * 0x0202u + 0x01000100u;
-    h[j] = __builtin_amdgcn_perm(thi_hi, thi_lo, sel);
-    l[j] = __builtin_amdgcn_perm(tlo_hi, tlo_lo, sel);
+    const uint32_t a4 = __builtin_amdgcn_ubfe(w, off + 4 * j, 4) << 2;
+    h[j] = lds_u32(tab + kTqCtabHi, a4);
+    l[j] = lds_u32(tab + kTqCtabLo, a4);
   }
   hi = __builtin_bit_cast(half8, h);
   lo = __builtin_bit_cast(half8, l);
 }
 
 // Eight sign bits (bits off .. off+7 of w) -> f16 1.0 where set, 0 elsewhere.
-__device__ __forceinline__ half8 tq_bits8(uint32_t w, int off) {
-  u32x4 r;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t t = __builtin_amdgcn_ubfe(w, off + 2 * j, 2);
-    r[j] = ((t * 0x8001u) & 0x00010001u) * 0x3C00u;         // bit 0 -> low f16, bit 1 -> high
-  }
+__device__ __forceinline__ half8 tq_bits8(uint32_t w, int off, const uint8_t* tab) {
+  const uint32_t a0 = __builtin_amdgcn_ubfe(w, off, 4) << 3;
+  const uint32_t a1 = __builtin_amdgcn_ubfe(w, off + 4, 4) << 3;
+  const u32x2 e0 = *reinterpret_cast<const u32x2*>(tab + kTqJtab + a0);
+  const u32x2 e1 = *reinterpret_cast<const u32x2*>(tab + kTqJtab + a1);
+  const u32x4 r = {e0[0], e0[1], e1[0], e1[1]};
   return __builtin_bit_cast(half8, r);
 }
 
@@ -114,6 +126,7 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
   constexpr int KW = D / 64;                     // polar words per lane group and cell
   static_assert(D == 64 || D == 128, "head_dim");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ __attribute__((aligned(16))) uint8_t tab[kTqTabBytes];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -154,12 +167,25 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
   const int cend = (int)((c0l + a.chunk < wmax) ? c0l + a.chunk : wmax);
   const int lim_lo = width_of(r0) < cend ? width_of(r0) : cend;
 
-  uint32_t* vtw = reinterpret_cast<uint32_t*>(smem) + wave * VW * TC;          // [VW][TC]
-  uint32_t* nrm = reinterpret_cast<uint32_t*>(smem + L::VT) + wave * 2 * TC;   // K norms, V norms
-  u32x4* qlds = reinterpret_cast<u32x4*>(smem + L::VT + L::NM);
+  uint8_t* work = smem;
+  uint32_t* vtw = reinterpret_cast<uint32_t*>(work) + wave * VW * TC;          // [VW][TC]
+  uint32_t* nrm = reinterpret_cast<uint32_t*>(work + L::VT) + wave * 2 * TC;   // K norms, V norms
+  u32x4* qlds = reinterpret_cast<u32x4*>(work + L::VT + L::NM);
   const int tail = L::MAIN > L::BUF ? L::MAIN : L::BUF;
-  float* qsum = reinterpret_cast<float*>(smem + tail);
-  float* mls = reinterpret_cast<float*>(smem + tail + L::QS);
+  float* qsum = reinterpret_cast<float*>(work + tail);
+  float* mls = reinterpret_cast<float*>(work + tail + L::QS);
+  if (tid < 16) {
+    // entry u = (b << 2) | a: the byte selector [2a, 2a+1, 2b, 2b+1] picks
+    // the two f16 halves of centroids a and b out of each 8-byte table
+    const uint32_t sel = ((uint32_t)(tid & 3) | ((uint32_t)(tid >> 2) << 16)) * 0x0202u + 0x01000100u;
+    reinterpret_cast<uint32_t*>(tab + kTqCtabHi)[tid] = __builtin_amdgcn_perm(a.chi_hi, a.chi_lo, sel);
+    reinterpret_cast<uint32_t*>(tab + kTqCtabLo)[tid] = __builtin_amdgcn_perm(a.clo_hi, a.clo_lo, sel);
+  } else if (tid < 32) {
+    const uint32_t u = (uint32_t)(tid - 16);
+    auto f = [](uint32_t bit) -> uint32_t { return bit ? 0x3C00u : 0u; };
+    reinterpret_cast<u32x2*>(tab + kTqJtab)[u] =
+        u32x2{f(u & 1) | (f((u >> 1) & 1) << 16), f((u >> 2) & 1) | (f((u >> 3) & 1) << 16)};
+  }
 
   // ---- query operands: q_rot and q_jl rows as f16 hi + lo, and each row's
   // sum of q_jl (fp32) ----
@@ -300,9 +326,8 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
       const int dl = 8 * ks;                     // dim offset inside the lane group's span
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
-        tq_polar8(R.pol[cb][dl / 16], 2 * (dl % 16), a.chi_lo, a.chi_hi, a.clo_lo, a.clo_hi,
-                  ch[cb], cl[cb]);
-        jb[cb] = tq_bits8(R.jl[cb], (lb * (D / 4) + dl) % 32);
+        tq_polar8(R.pol[cb][dl / 16], 2 * (dl % 16), tab, ch[cb], cl[cb]);
+        jb[cb] = tq_bits8(R.jl[cb], (lb * (D / 4) + dl) % 32, tab);
       }
 #pragma unroll
       for (int k = 0; k < NRB; ++k) {
@@ -414,9 +439,9 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
       for (int j = 0; j < 4; ++j) {
         const uint32_t ia = __builtin_amdgcn_ubfe(w[2 * j], 2 * lr, 2);
         const uint32_t ib = __builtin_amdgcn_ubfe(w[2 * j + 1], 2 * lr, 2);
-        const uint32_t sel = (ia | (ib << 16)) * 0x0202u + 0x01000100u;
-        h[j] = __builtin_amdgcn_perm(a.chi_hi, a.chi_lo, sel);
-        l[j] = __builtin_amdgcn_perm(a.clo_hi, a.clo_lo, sel);
+        const uint32_t a4 = (ia << 2) | (ib << 4);
+        h[j] = lds_u32(tab + kTqCtabHi, a4);
+        l[j] = lds_u32(tab + kTqCtabLo, a4);
       }
       const half8 vh = __builtin_bit_cast(half8, h);
       const half8 vl = __builtin_bit_cast(half8, l);
@@ -464,7 +489,7 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
     }
   }
   __syncthreads();
-  float* buf = reinterpret_cast<float*>(smem);
+  float* buf = reinterpret_cast<float*>(work);
   constexpr int HALF = NW / 2;
 #pragma unroll
   for (int k = 0; k < NRB; ++k) {

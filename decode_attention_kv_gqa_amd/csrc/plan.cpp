@@ -26,7 +26,11 @@ int check_shape(const Shape& s) {
 int auto_chunk(const Shape& s) {
   int rc = check_shape(s);
   if (rc != GQA_OK) return rc;
-  const int64_t kTargetWorkgroups = 256;
+  // The TurboQuant kernel is bound by decode latency, not by the stream:
+  // eight of its workgroups per compute unit (four waves per SIMD) hide it
+  // (int8-shaped 128K cache, 8 KV heads: 292 us at one workgroup per unit,
+  // 195 us at eight).
+  const int64_t kTargetWorkgroups = s.tq ? 2048 : 256;
   const int64_t kMinSplitsPerUnit = 8;
   const int64_t kMinChunk = 64;
   int64_t W = width_cap(s);
@@ -58,8 +62,9 @@ size_t gqa_decode_part_bytes(int S, int T, int Lmax, int B, int H, int D, int ch
   return gqa::part_bytes(s, chunk);
 }
 
-int gqa_decode_auto_chunk(int S, int T, int Lmax, int B, int H, int Hk, int D, int kv_is_i8) {
-  gqa::Shape s{S, T, Lmax, B, H, Hk, D, B > 0, kv_is_i8 != 0};
+int gqa_decode_auto_chunk(int S, int T, int Lmax, int B, int H, int Hk, int D, int kv_kind) {
+  if (kv_kind < 0 || kv_kind > 2) return GQA_ERR_SHAPE;
+  gqa::Shape s{S, T, Lmax, B, H, Hk, D, B > 0, kv_kind != 0, kv_kind == 2};
   return gqa::auto_chunk(s);
 }
 

@@ -19,6 +19,7 @@ struct Shape {
   int S, T, Lmax, B, H, Hk, D;
   bool ids;   // gather through a budget of cell ids
   bool i8;    // int8 rows with f16 group scales
+  bool tq = false;   // TurboQuant-compressed cache (gqa_decode_attn_tq)
 };
 
 // Positions a split can cover: min(B, Lmax) with ids, else Lmax.

@@ -168,7 +168,7 @@ int gqa_decode_attn_tq(const float* q_rot, const float* q_jl, const uint32_t* k_
                        int chunk, void* stream) {
   if (!q_rot || !q_jl || !seq_lens || !part) return GQA_ERR_NULL;
   if (Lmax > 0 && (!k_polar || !k_jl || !k_norms || !v_polar || !v_norms)) return GQA_ERR_NULL;
-  gqa::Shape sh{S, T, Lmax, 0, H, Hk, D, false, true};
+  gqa::Shape sh{S, T, Lmax, 0, H, Hk, D, false, true, true};
   int rc = gqa::check_shape(sh);
   if (rc != GQA_OK) return rc;
   if (D != 64 && D != 128) return GQA_ERR_HEAD_DIM;

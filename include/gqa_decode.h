@@ -85,9 +85,12 @@ size_t gqa_decode_part_bytes(int S, int T, int Lmax, int B, int H, int D, int ch
  * deterministic host function of the shapes: it picks the cells per split so
  * that the grid gives every one of the 256 compute units several
  * workgroups, while the partials stay a small fraction of the KV bytes.
- * `kv_is_i8` selects the int8 row size.  Returns a positive chunk, or a
+ * `kv_kind` names the cache: 0 f16, 1 int8 (both stream best with one
+ * long-running four-wave workgroup per compute unit), 2 TurboQuant
+ * (gqa_decode_attn_tq: decoding is latency-bound, so its splits are sized
+ * for several workgroups per compute unit).  Returns a positive chunk, or a
  * negative GQA_ERR_* code. */
-int gqa_decode_auto_chunk(int S, int T, int Lmax, int B, int H, int Hk, int D, int kv_is_i8);
+int gqa_decode_auto_chunk(int S, int T, int Lmax, int B, int H, int Hk, int D, int kv_kind);
 
 /* Chunk partials over an f16 cache.
  *   q         [S][T][H][D]       float32

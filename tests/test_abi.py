@@ -141,6 +141,9 @@ def test_auto_chunk_plan():
     assert ac(8, 1, 32768, 0, 24, 2, 256, 1) == 2048
     assert ac(32, 1, 4096, 0, 32, 8, 128, 0) == 512
     assert ac(8, 1, 32768, 0, 25, 2, 256, 1) == _lib.GQA_ERR_GROUP
+    # the TurboQuant cache is planned for eight workgroups per compute unit
+    assert ac(4, 1, 131072, 0, 32, 8, 128, 2) == 2048
+    assert ac(4, 1, 131072, 0, 32, 8, 128, 3) == _lib.GQA_ERR_SHAPE
 
 
 def test_python_wrapper_refuses_cpu_tensors():
