@@ -38,6 +38,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# G wave64 VALU instructions per second: 256 CUs x 4 SIMDs x 2.4 GHz, one
+# instruction per SIMD every 4 cycles (16 lanes per cycle)
+VALU_ISSUE_PEAK_G = 256 * 4 * 2.4 / 4
 LLC_BYTES = 256 << 20
 SETTLE_S = 0.05
 PROFILES = os.path.join(ROOT, "profiles")
@@ -62,9 +65,10 @@ def kernel_source_hash(kernel: str = "attn") -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str, kernel: str = "attn"):
-    """HBM bytes per launch of the workload's measured kernel from rocprofv3
-    counters, if they were taken on the current kernel source."""
+def load_traffic_record(workload: str, kernel: str = "attn"):
+    """The rocprofv3 counter record of the workload's measured kernel
+    (profiles/traffic_<workload>.json), if it was taken on the current kernel
+    source; else None."""
     path = os.path.join(PROFILES, f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -72,7 +76,14 @@ def load_traffic(workload: str, kernel: str = "attn"):
         rec = json.load(f)
     if rec.get("kernel_source_hash") != kernel_source_hash(kernel):
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec
+
+
+def load_traffic(workload: str, kernel: str = "attn"):
+    """HBM bytes per launch of the workload's measured kernel from rocprofv3
+    counters, if they were taken on the current kernel source."""
+    rec = load_traffic_record(workload, kernel)
+    return None if rec is None else rec.get("hbm_bytes_per_launch")
 
 
 def cpu_baseline(inp, budget_s: float = 12.0):
@@ -283,6 +294,25 @@ def bench_tq(args):
     attn_ms = np.array([a.elapsed_time(b) / per for a, b in evs])
     kern_s = float(attn_ms.mean()) / 1e3
     achieved = nbytes / kern_s / 1e9
+    # The kernel is bound by vector-ALU issue (unpacking the codes), so its
+    # roofline is the issue rate of wave64 VALU instructions: 256 CUs x 4 SIMDs
+    # x 2.4 GHz / 4 cycles per instruction = 614.4 G/s.  The instruction count
+    # per launch comes from the rocprofv3 SQ_INSTS_VALU run kept in profiles/
+    # (null once the kernel source changes); the HBM view is reported beside it.
+    rec = load_traffic_record(args.workload, "tq")
+    valu = rec.get("valu_wave_instructions_per_launch") if rec else None
+    hbm = {"achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": round(achieved / HBM_PEAK_GBS, 4),
+           "traffic": rec.get("hbm_bytes_per_launch") if rec else None}
+    roof = {"bound": "alu", "achieved": None, "peak": VALU_ISSUE_PEAK_G, "unit": "G VALU instr/s",
+            "frac": None, "traffic": hbm["traffic"], "kernel": "attn_tq",
+            "kernel_us_mean": round(kern_s * 1e6, 3),
+            "kernel_us_burst_min_max": [round(float(attn_ms.min()) * 1e3, 3),
+                                        round(float(attn_ms.max()) * 1e3, 3)],
+            "hbm_view": hbm}
+    if valu:
+        roof["achieved"] = round(valu / kern_s / 1e9, 2)
+        roof["frac"] = round(valu / kern_s / 1e9 / VALU_ISSUE_PEAK_G, 4)
     print(json.dumps({
         "metric": "TurboQuant-cache decode effective cache GB/s and us/step, 1 MI355X",
         "value": round(nbytes / (wall / K) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
@@ -291,13 +321,7 @@ def bench_tq(args):
         "data": "synthetic (seeded numpy: uniform codes, f16 norms, N(0,1) rotated queries)",
         "config": {"workload": args.workload, **sh, "chunk": step.chunk,
                    "cache_bytes_per_step": nbytes, "input_copies_rotated": copies},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": load_traffic(args.workload, "tq"), "kernel": "attn_tq",
-                     "kernel_us_mean": round(kern_s * 1e6, 3),
-                     "kernel_us_burst_min_max": [round(float(attn_ms.min()) * 1e3, 3),
-                                                 round(float(attn_ms.max()) * 1e3, 3)]}}),
-          flush=True)
+        "roofline": roof}), flush=True)
 
 
 def main():
