@@ -17,13 +17,14 @@
 //      the bins from the top with a wave-wide prefix sum and finds the digit
 //      itself, so a pass needs two barriers.  Up to 16 keys per thread stay
 //      in registers across the passes.
-//   2. Emission: every thread owns a contiguous block range; block-wide
-//      prefix sums give each thread its share of the Tk blocks (in block
-//      order) and its output offset, so the ids come out ascending.  The
+//   2. Emission: every thread owns a contiguous block range; one block-wide
+//      prefix sum of its counts of blocks above and at Tk gives each thread
+//      its share of the Tk blocks (in block order) and its output offset,
+//      so the ids come out ascending.  The
 //      keys come from LDS, and the ids are gathered in LDS and written to
 //      memory in one coalesced pass.
 // The page's kernel makes the same two phases on Apple simdgroups; here the
-// scans are wave64 shuffles and the histogram lives in LDS.
+// scans are wave64 DPP moves and the histogram lives in LDS.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -38,6 +39,9 @@ constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kKeysInRegs = 16;         // blocks per thread kept in registers (radix passes)
 constexpr int kKeysInLds = 28672;       // block keys staged in LDS (112 KB) for the emission
 constexpr int kSelOutLds = 4096;        // budgets up to this are written through LDS
+constexpr int kMaxPer = (kKeysInLds + kSelThreads - 1) / kSelThreads;  // blocks per thread, emission
+constexpr int kKeyPad = 32;             // LDS keys past the last block (read, never used)
+static_assert(kMaxPer <= 32 && kMaxPer <= kKeyPad, "emission block mask / key padding");
 
 // Order-preserving map of a float's bits to an unsigned key (floats compare
 // like their keys; -0 sorts below +0).
@@ -46,13 +50,18 @@ __device__ __forceinline__ uint32_t okey(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+// Inclusive prefix sum over the 64 lanes of a wave, with DPP moves (no LDS
+// round trips): shifts by 1, 2, 4 and 8 lanes inside each row of 16, then
+// row 0's total into row 1 and row 2's into row 3 (row_bcast:15), then the
+// total of rows 0-1 into rows 2-3 (row_bcast:31).  Lanes whose source is
+// outside the row, and rows the row mask leaves out, add 0.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31
   return x;
 }
 
@@ -63,17 +72,24 @@ struct SelArgs {
   int S, T, Lmax, B, nbs;
 };
 
-// Exclusive prefix sum of one value per thread over the workgroup, in
-// thread order; wsum is a kSelWaves-entry LDS scratch array.
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* wsum, int tid) {
+// Exclusive prefix sums of two values per thread over the workgroup, in
+// thread order; wsum is a 2 * kSelWaves-entry LDS scratch array.  Every
+// wave reads all the wave totals at once and scans them itself.
+__device__ __forceinline__ void block_excl_scan2(uint32_t x, uint32_t y, uint32_t* wsum, int tid,
+                                                 uint32_t& xe, uint32_t& ye) {
   const int lane = tid & 63, wave = tid >> 6;
-  const uint32_t inc = wave_incl_scan(x, lane);
-  if (lane == 63) wsum[wave] = inc;
+  const uint32_t xi = wave_incl_scan(x), yi = wave_incl_scan(y);
+  if (lane == 63) {
+    wsum[wave] = xi;
+    wsum[kSelWaves + wave] = yi;
+  }
   __syncthreads();
-  uint32_t before = 0;
-  for (int w = 0; w < wave; ++w) before += wsum[w];
-  __syncthreads();                      // wsum is reused by the next scan
-  return before + inc - x;
+  const uint32_t xt = wave_incl_scan(lane < kSelWaves ? wsum[lane] : 0u);
+  const uint32_t yt = wave_incl_scan(lane < kSelWaves ? wsum[kSelWaves + lane] : 0u);
+  const uint32_t xb = wave > 0 ? (uint32_t)__shfl((int)xt, wave - 1, 64) : 0u;
+  const uint32_t yb = wave > 0 ? (uint32_t)__shfl((int)yt, wave - 1, 64) : 0u;
+  xe = xb + xi - x;
+  ye = yb + yi - y;
 }
 
 __global__ __launch_bounds__(kSelThreads) void select_ids(SelArgs a) {
@@ -82,7 +98,7 @@ __global__ __launch_bounds__(kSelThreads) void select_ids(SelArgs a) {
   // every wave's adds on the same bins
   __shared__ uint32_t hist[kSelWaves][256];
   __shared__ uint32_t tot[256];
-  __shared__ uint32_t wsum[kSelWaves];
+  __shared__ uint32_t wsum[2 * kSelWaves];
   __shared__ int32_t obuf[kSelOutLds];   // the token's ids before the coalesced write
   extern __shared__ uint32_t keyl[];     // block keys (first kKeysInLds blocks)
   const int tid = threadIdx.x;
@@ -90,7 +106,25 @@ __global__ __launch_bounds__(kSelThreads) void select_ids(SelArgs a) {
   const int wave = tid >> 6;
   const int tok = blockIdx.x;            // s * T + t
   const int s = tok / a.T, t = tok % a.T;
-  int n = a.seq_lens[s] - (a.T - 1 - t);
+  const int len = a.seq_lens[s];
+  const float* sc = a.scores + (size_t)tok * a.nbs;
+
+  // Keys: 16 blocks per thread (b = tid + 1024 i) in registers for the radix
+  // passes, and the first kKeysInLds blocks also in LDS for the emission;
+  // blocks past both are re-read from memory.  The loads cover the whole
+  // score row and do not wait for the sequence length, so the two memory
+  // round trips overlap; keys past the window are never counted.
+  uint32_t kr[kKeysInRegs];
+#pragma unroll
+  for (int i = 0; i < kKeysInRegs; ++i) {
+    const int b = tid + kSelThreads * i;
+    kr[i] = b < a.nbs ? okey(sc[b]) : 0u;
+    if (b < a.nbs && b < kKeysInLds) keyl[b] = kr[i];
+  }
+  for (int b = tid + kSelThreads * kKeysInRegs; b < a.nbs && b < kKeysInLds; b += kSelThreads)
+    keyl[b] = okey(sc[b]);
+
+  int n = len - (a.T - 1 - t);
   n = n < 0 ? 0 : (n > a.Lmax ? a.Lmax : n);
   int32_t* out = a.ids + (size_t)tok * a.B;
   if (n <= a.B) {                        // the whole window fits the budget
@@ -98,21 +132,7 @@ __global__ __launch_bounds__(kSelThreads) void select_ids(SelArgs a) {
     return;
   }
   const int n_bid = n >> 2, rem = n & 3, nb = n_bid + 1;
-  const float* sc = a.scores + (size_t)tok * a.nbs;
   auto cells_of = [&](int b) -> uint32_t { return b < n_bid ? 4u : (uint32_t)rem; };
-
-  // Keys: 16 blocks per thread (b = tid + 1024 i) in registers for the radix
-  // passes, and the first kKeysInLds blocks also in LDS for the emission;
-  // blocks past both are re-read from memory.
-  uint32_t kr[kKeysInRegs];
-#pragma unroll
-  for (int i = 0; i < kKeysInRegs; ++i) {
-    const int b = tid + kSelThreads * i;
-    kr[i] = b < nb ? okey(sc[b]) : 0u;
-    if (b < nb && b < kKeysInLds) keyl[b] = kr[i];
-  }
-  for (int b = tid + kSelThreads * kKeysInRegs; b < nb && b < kKeysInLds; b += kSelThreads)
-    keyl[b] = okey(sc[b]);
   auto key = [&](int b) -> uint32_t { return b < kKeysInLds ? keyl[b] : okey(sc[b]); };
 #pragma unroll
   for (int j = 0; j < 4; ++j) hist[wave][lane + 64 * j] = 0;
@@ -148,7 +168,7 @@ __global__ __launch_bounds__(kSelThreads) void select_ids(SelArgs a) {
     uint32_t c[4], lsum = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) { c[j] = tot[255 - 4 * lane - j]; lsum += c[j]; }
-    uint32_t above = wave_incl_scan(lsum, lane) - lsum;   // cells in higher digits
+    uint32_t above = wave_incl_scan(lsum) - lsum;   // cells in higher digits
     uint32_t dsel = 0, nsel = 0;
     bool found = false;
 #pragma unroll
@@ -174,34 +194,79 @@ __global__ __launch_bounds__(kSelThreads) void select_ids(SelArgs a) {
   const int per = (nb + kSelThreads - 1) / kSelThreads;
   const int b0 = tid * per < nb ? tid * per : nb;
   const int b1 = b0 + per < nb ? b0 + per : nb;
-  uint32_t gt = 0, eq = 0;
-  for (int b = b0; b < b1; ++b) {
-    const uint32_t k = key(b);
-    if (k > Tk) gt += cells_of(b);
-    else if (k == Tk) eq += cells_of(b);
-  }
-  const uint32_t eq_before = block_excl_scan(eq, wsum, tid);
-  const uint32_t eq_take = eq_before >= need ? 0u : (eq < need - eq_before ? eq : need - eq_before);
-  uint32_t off = block_excl_scan(gt + eq_take, wsum, tid);
   const bool staged = a.B <= kSelOutLds;
-  uint32_t left = eq_take;
-  for (int b = b0; b < b1; ++b) {
-    const uint32_t k = key(b);
-    const uint32_t cells = cells_of(b);
-    uint32_t take = 0;
-    if (k > Tk) {
-      take = cells;
-    } else if (k == Tk) {
-      take = cells < left ? cells : left;
-      left -= take;
+  auto put = [&](uint32_t pos, int id) {
+    if (pos < (uint32_t)a.B) {           // never past the row
+      if (staged) obuf[pos] = id;
+      else out[pos] = id;
     }
-    for (uint32_t c = 0; c < take; ++c) {
-      if (off + c < (uint32_t)a.B) {     // never past the row
-        if (staged) obuf[off + c] = 4 * b + (int)c;
-        else out[off + c] = 4 * b + (int)c;
+  };
+  if (staged && nb <= kKeysInLds) {
+    // every key is in LDS, a thread's range has at most kMaxPer blocks, and
+    // the ids go to LDS.  The counting loop has a fixed length and no
+    // branches (a range's reads may run up to kMaxPer - 1 keys past the last
+    // block, into the kKeyPad padding; those keys count no cells); it also
+    // marks the blocks with a key >= Tk, and the writing loop visits only
+    // those -- a few per thread when B is a small part of the window.
+    uint32_t gt = 0, eq = 0, cand = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxPer; ++i) {
+      const int b = b0 + i;
+      const uint32_t k = keyl[b];
+      const uint32_t cells = b < b1 ? cells_of(b) : 0u;
+      gt += k > Tk ? cells : 0u;
+      eq += k == Tk ? cells : 0u;
+      cand |= (k >= Tk && cells) ? 1u << i : 0u;
+    }
+    uint32_t gt_before, eq_before;
+    block_excl_scan2(gt, eq, wsum, tid, gt_before, eq_before);
+    // the Tk blocks are taken in block order until `need` cells are taken,
+    // so the threads before this one took min(eq_before, need) of them
+    uint32_t left = eq_before >= need ? 0u : (eq < need - eq_before ? eq : need - eq_before);
+    uint32_t off = gt_before + (eq_before < need ? eq_before : need);
+    while (cand) {
+      const int i = __builtin_ctz(cand);
+      cand &= cand - 1;
+      const int b = b0 + i;
+      const uint32_t k = keyl[b];
+      const uint32_t cells = cells_of(b);
+      uint32_t take = cells;
+      if (k == Tk) {
+        take = cells < left ? cells : left;
+        left -= take;
       }
+      // off + take never passes B; the clamp only keeps a stray write in LDS
+#pragma unroll
+      for (uint32_t c = 0; c < 4; ++c) {
+        const uint32_t pos = off + c < (uint32_t)(kSelOutLds - 1) ? off + c : (uint32_t)(kSelOutLds - 1);
+        if (c < take) obuf[pos] = 4 * b + (int)c;
+      }
+      off += take;
     }
-    off += take;
+  } else {
+    uint32_t gt = 0, eq = 0;
+    for (int b = b0; b < b1; ++b) {
+      const uint32_t k = key(b);
+      if (k > Tk) gt += cells_of(b);
+      else if (k == Tk) eq += cells_of(b);
+    }
+    uint32_t gt_before, eq_before;
+    block_excl_scan2(gt, eq, wsum, tid, gt_before, eq_before);
+    uint32_t left = eq_before >= need ? 0u : (eq < need - eq_before ? eq : need - eq_before);
+    uint32_t off = gt_before + (eq_before < need ? eq_before : need);
+    for (int b = b0; b < b1; ++b) {
+      const uint32_t k = key(b);
+      const uint32_t cells = cells_of(b);
+      uint32_t take = 0;
+      if (k > Tk) {
+        take = cells;
+      } else if (k == Tk) {
+        take = cells < left ? cells : left;
+        left -= take;
+      }
+      for (uint32_t c = 0; c < take; ++c) put(off + c, 4 * b + (int)c);
+      off += take;
+    }
   }
   if (staged) {
     __syncthreads();
@@ -219,7 +284,7 @@ extern "C" int gqa_decode_select_ids(const float* block_scores, const int32_t* s
   if ((int64_t)S * T > 0x7fffffff) return GQA_ERR_SHAPE;
   SelArgs a{block_scores, seq_lens, ids, S, T, Lmax, B, Lmax / 4 + 1};
   const int nl = a.nbs < kKeysInLds ? a.nbs : kKeysInLds;
-  const int bytes = nl * 4;
+  const int bytes = (nl + kKeyPad) * 4;
   if (bytes > 65536) {
     // more than 64 KB of dynamic LDS must be allowed once per device
     static std::atomic<uint64_t> attr_set{0};
@@ -229,7 +294,7 @@ extern "C" int gqa_decode_select_ids(const float* block_scores, const int32_t* s
     const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
     if (!(attr_set.load(std::memory_order_acquire) & bit)) {
       e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_ids),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kKeysInLds * 4);
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (kKeysInLds + kKeyPad) * 4);
       if (e != hipSuccess) return (int)e;
       attr_set.fetch_or(bit, std::memory_order_acq_rel);
     }
