@@ -110,6 +110,40 @@ def test_multi_query_causal(kv, T):
             assert got[1, t].any() == (3 - (T - 1 - t) > 0)
 
 
+@pytest.mark.parametrize("Hk,G,T", [(2, 12, 1), (4, 3, 4), (4, 16, 1), (6, 2, 8), (2, 17, 1)])
+def test_int8_hd256_kv_head_counts(Hk, G, T):
+    # int8 head_dim 256 with 2-6 KV heads, up to 16 query rows per KV head
+    # (one row block) and 17 (two), one- and four-wave splits
+    inp = make_case(3, T, G * Hk, Hk, 256, 300, [300, 170, 2], kv="i8", seed=Hk * 100 + G * 10 + T)
+    ref = oracle(inp)
+    for chunk in (1, 32, 100, 0):
+        got = run_gpu(inp, chunk=chunk)
+        assert_parity(got, ref, f"Hk={Hk} G={G} T={T} chunk={chunk}")
+
+
+@pytest.mark.parametrize("Hk", [1, 2])
+def test_int8_large_v_scales_after_a_lagging_max(Hk):
+    # Every wave's first tile scores 0 and its later tiles 7.85 (base 2): the
+    # lazily moved reference max lags by less than 8, so p reaches ~230.  The
+    # last KV head's V scales there are 300: p * scale would overflow f16
+    # unless the kernel tracks the exact max in tiles holding scales > 255.
+    # With Hk = 2 that head's rows sit at odd 256-byte offsets of the cells.
+    D, L = 256, 300
+    inp = make_case(1, 1, 4 * Hk, Hk, D, L, [L], kv="i8", scale=1.0 / 16.0, seed=41 + Hk)
+    inp.q[...] = 1.0
+    inp.k[0, :128] = 0
+    inp.k[0, 128:] = 34
+    inp.k_scales[...] = np.float16(0.01)
+    rng = np.random.default_rng(5)
+    inp.v[0, 128:, Hk - 1] = rng.integers(-1, 2, size=(L - 128, D)).astype(np.int8)
+    inp.v_scales[0, 128:, Hk - 1] = np.float16(300.0)
+    ref = oracle(inp)
+    for chunk in (256, 0):
+        got = run_gpu(inp, chunk=chunk)
+        assert np.isfinite(got).all()
+        assert_parity(got, ref, f"large V scales Hk={Hk} chunk={chunk}")
+
+
 def test_rows_beyond_one_block():
     # G * T = 64 query rows per KV head: two row blocks, each streams K/V
     inp = make_case(2, 8, 16, 2, 128, 300, [300, 190], kv="f16", seed=5)
