@@ -79,12 +79,15 @@ struct TqLds {
 // size), built once per workgroup; a lookup replaces the bit arithmetic:
 //   chi[u], u = (b << 2) | a for two 2-bit indices a, b: the f16 high parts
 //           of centroids a and b (one dword of the MFMA operand);
-//   clo[u]  their f16 low parts -- 1 KB after chi, so the compiler keeps the
-//           two reads apart and each lands in its own operand register;
+//   clo[u]  their f16 low parts -- 1028 bytes after chi: farther than a
+//           paired dword read reaches and not a multiple of 256 bytes, so the
+//           compiler cannot fuse a chi and a clo read into one two-dword read
+//           (whose two results land in adjacent registers and then need a move
+//           each into the hi and lo operand registers);
 //   jtab[u], u = four sign bits: four f16 values 0 / 1.
 // Each table's entries sit in distinct banks, so a wave's lookups never
 // conflict (equal entries broadcast).
-constexpr int kTqCtabHi = 0, kTqJtab = 64, kTqCtabLo = 1024, kTqTabBytes = 1088;
+constexpr int kTqCtabHi = 0, kTqJtab = 64, kTqCtabLo = 1028, kTqTabBytes = 1104;
 
 __device__ __forceinline__ uint32_t lds_u32(const uint8_t* base, uint32_t byte) {
   return *reinterpret_cast<const uint32_t*>(base + byte);
