@@ -14,6 +14,8 @@ Reported (one JSON line on stdout):
                step / wall-clock seconds per step (K steps back to back,
                bracketed by device synchronisation)
   ms_per_step  wall-clock milliseconds per step
+  step_us_p10_p50_p90  percentiles of single steps (attention + merge), each
+               between its own pair of HIP events
   roofline     the chunk kernel alone: algorithmic bytes per launch / its
                mean duration from HIP events on its stream (bursts of
                back-to-back launches), against the 8 TB/s HBM peak; `traffic` is HBM bytes per launch measured
@@ -448,6 +450,19 @@ def main():
     attn_ms = np.array([a.elapsed_time(b) / per for a, b in evs])
     attn_mean_s = float(attn_ms.mean()) / 1e3
 
+    # spread of single steps: each step (attention + merge) between its own
+    # pair of events, input copies still rotating
+    nst = min(K, 100)
+    sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(nst)]
+    torch.cuda.synchronize()
+    for i in range(nst):
+        sev[i][0].record(stream)
+        one(i)
+        sev[i][1].record(stream)
+    torch.cuda.synchronize()
+    step_us = np.array([a.elapsed_time(b) * 1e3 for a, b in sev])
+
     achieved = step_bytes / attn_mean_s / 1e9
     traffic = load_traffic(args.workload)
     res = {
@@ -460,6 +475,7 @@ def main():
         "extra_warmup_steps": extra,
         "ms_per_step": round(ms_per_step, 5),
         "us_per_step": round(ms_per_step * 1e3, 2),
+        "step_us_p10_p50_p90": [round(float(np.percentile(step_us, q)), 2) for q in (10, 50, 90)],
         "pct_of_hbm_peak": round(100 * step_bytes / (wall / K) / 1e9 / HBM_PEAK_GBS, 2),
         "higher_is_better": True,
         "scaling": "weak",
