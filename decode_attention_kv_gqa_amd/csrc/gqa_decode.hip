@@ -51,11 +51,13 @@ constexpr float kLog2e = 1.4426950408889634f;
 // splits online (a running max with rescaling, the same update as the
 // attention's softmax but over partials), so every load of the row is issued
 // up front and no wave waits for another before reading o; the four waves'
-// (max, sum, o) are then combined through LDS.
-template <int D>
+// (max, sum, o) are then combined through LDS.  U splits per wave have their
+// loads in flight together: U = 4 covers 16 splits in one round trip, and
+// longer rows (budgeted windows cut into 32-cell splits: 64 of them) get
+// U = 8 or 16 so that they also take one.
+template <int D, int U>
 __global__ __launch_bounds__(kThreads) void merge_rows(MergeArgs a) {
   constexpr int V = D / 64;
-  constexpr int U = 4;                    // splits per wave whose loads are in flight together
   __shared__ float red_o[4][D];
   __shared__ float red_ml[4][2];
   const int tid = threadIdx.x;
@@ -156,6 +158,15 @@ __global__ __launch_bounds__(kThreads) void merge_rows(MergeArgs a) {
       if (gated) x *= 1.0f / (1.0f + __expf(-gt[e]));
       out[e] = x;
     }
+  }
+}
+
+template <int U>
+void launch_merge(const MergeArgs& a, int D, dim3 grid, hipStream_t st) {
+  switch (D) {
+    case 64: hipLaunchKernelGGL((merge_rows<64, U>), grid, dim3(kThreads), 0, st, a); break;
+    case 128: hipLaunchKernelGGL((merge_rows<128, U>), grid, dim3(kThreads), 0, st, a); break;
+    default: hipLaunchKernelGGL((merge_rows<256, U>), grid, dim3(kThreads), 0, st, a); break;
   }
 }
 
@@ -298,11 +309,12 @@ static int merge_common(const float* part, const int32_t* seq_lens, const int32_
   if (rows > 0x7fffffffu) return GQA_ERR_SHAPE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   dim3 grid((unsigned)rows);
-  switch (D) {
-    case 64: hipLaunchKernelGGL(merge_rows<64>, grid, dim3(kThreads), 0, st, a); break;
-    case 128: hipLaunchKernelGGL(merge_rows<128>, grid, dim3(kThreads), 0, st, a); break;
-    default: hipLaunchKernelGGL(merge_rows<256>, grid, dim3(kThreads), 0, st, a); break;
-  }
+  if (P <= 16)
+    launch_merge<4>(a, D, grid, st);
+  else if (P <= 32)
+    launch_merge<8>(a, D, grid, st);
+  else
+    launch_merge<16>(a, D, grid, st);
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? GQA_OK : (int)e;
 }
