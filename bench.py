@@ -52,6 +52,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 # version of a kernel do not describe another
 KERNEL_SOURCES = {
     "attn": ["attn_mfma.h", "common.h", "gqa_decode.hip", "plan.h", "plan.cpp"],
+    "merge": ["merge.hip", "common.h", "plan.h"],
     "append": ["append.hip"],
     "select": ["select.hip"],
     "tq": ["attn_tq.h", "attn_mfma.h", "common.h", "tq.hip", "plan.h", "plan.cpp"],

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libgqa_decode.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["gqa_decode.hip", "select.hip", "append.hip", "tq.hip", "plan.cpp"]
+SOURCES = ["gqa_decode.hip", "merge.hip", "select.hip", "append.hip", "tq.hip", "plan.cpp"]
 
 # Every HIP translation unit is built for gfx950 only, with packed-fp32 VALU
 # instructions disabled (the compiler otherwise forms v_pk_*_f32 from plain

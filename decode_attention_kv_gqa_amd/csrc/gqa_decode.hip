@@ -6,8 +6,7 @@
 //               for every query row of the GQA group (all G heads, and all T
 //               tokens of a dense causal window), runs an online softmax per
 //               row and writes one partial (o unnormalised, m, l) per row.
-//   merge_rows  one workgroup per output row: log-sum-exp merge of the
-//               partials of that row's splits.
+// The log-sum-exp merge of the partials is in merge.hip.
 // The attention grid is one-dimensional and ordered so that consecutive
 // workgroups, which the hardware hands to different XCDs, carry equal work.
 //
@@ -24,7 +23,7 @@
 // scale * log2(e) so the exponentials are exp2, which is the hardware's
 // native v_exp_f32.  exp2(x * log2 e) = exp(x), so this is the same
 // natural-base softmax.  The running max stored in a partial is therefore
-// in base-2 units; only the merge below reads it.
+// in base-2 units; only the merge reads it.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -39,136 +38,8 @@
 namespace {
 
 using gqa_kern::AttnArgs;
-using gqa_kern::MergeArgs;
 
-constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
-
-// One workgroup per output row (s, t, h); its four waves split the row's
-// partials (wave w takes splits w, w+4, ...) and lane l holds dims
-// l*V .. l*V+V-1 (V = D/64), so one split's o is one 16/8/4-byte load per
-// lane, 1 KB / 512 B / 256 B per wave, coalesced.  Each wave merges its
-// splits online (a running max with rescaling, the same update as the
-// attention's softmax but over partials), so every load of the row is issued
-// up front and no wave waits for another before reading o; the four waves'
-// (max, sum, o) are then combined through LDS.  U splits per wave have their
-// loads in flight together: U = 4 covers 16 splits in one round trip, and
-// longer rows (budgeted windows cut into 32-cell splits: 64 of them) get
-// U = 8 or 16 so that they also take one.
-template <int D, int U>
-__global__ __launch_bounds__(kThreads) void merge_rows(MergeArgs a) {
-  constexpr int V = D / 64;
-  __shared__ float red_o[4][D];
-  __shared__ float red_ml[4][2];
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int row = blockIdx.x;             // ((s * T) + t) * H + h
-  // The attention call writes every (row, split) slot; a split without a
-  // visible cell of the row carries m = -inf and is skipped, so the row's
-  // window need not be recomputed here and every load is issued at once.
-  const int nv = a.P;
-  const float* ml = a.part_ml + (size_t)row * a.P * 2;
-  const float* po = a.part_o + (size_t)row * a.P * D + lane * V;
-  // output gate (qsa2.metal, qsa_merge2; FORWARD_MSL, attn_combine): the
-  // merged row is multiplied by sigmoid(gate) elementwise.  Wave 0 writes
-  // the row, so it requests its gate elements first.
-  float gt[V];
-  const bool gated = a.gate != nullptr;
-  if (gated && wave == 0) {
-    const float* gsrc = a.gate + (size_t)row * a.gate_stride + lane * V;
-#pragma unroll
-    for (int e = 0; e < V; ++e) gt[e] = gsrc[e];
-  }
-
-  float M = -INFINITY, lsum = 0.f;
-  float acc[V];
-#pragma unroll
-  for (int e = 0; e < V; ++e) acc[e] = 0.f;
-  for (int j0 = wave; j0 < nv; j0 += 4 * U) {
-    float mj[U], lj[U], oj[U][V];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = j0 + 4 * u;
-      mj[u] = -INFINITY;
-      lj[u] = 0.f;
-#pragma unroll
-      for (int e = 0; e < V; ++e) oj[u][e] = 0.f;
-      if (j < nv) {
-        mj[u] = ml[2 * j];
-        lj[u] = ml[2 * j + 1];
-        const float* src = po + (size_t)j * D;
-        if constexpr (V == 4) {
-          const float4 x = *reinterpret_cast<const float4*>(src);
-          oj[u][0] = x.x; oj[u][1] = x.y; oj[u][2] = x.z; oj[u][3] = x.w;
-        } else if constexpr (V == 2) {
-          const float2 x = *reinterpret_cast<const float2*>(src);
-          oj[u][0] = x.x; oj[u][1] = x.y;
-        } else {
-          oj[u][0] = *src;
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (mj[u] == -INFINITY) continue;   // no visible cell in that split: weight 0
-      if (mj[u] > M) {
-        const float c = (M == -INFINITY) ? 0.f : exp2f(M - mj[u]);
-        lsum *= c;
-#pragma unroll
-        for (int e = 0; e < V; ++e) acc[e] *= c;
-        M = mj[u];
-      }
-      const float w = exp2f(mj[u] - M);
-      lsum = fmaf(w, lj[u], lsum);
-#pragma unroll
-      for (int e = 0; e < V; ++e) acc[e] = fmaf(w, oj[u][e], acc[e]);
-    }
-  }
-#pragma unroll
-  for (int e = 0; e < V; ++e) red_o[wave][lane * V + e] = acc[e];
-  if (lane == 0) {
-    red_ml[wave][0] = M;
-    red_ml[wave][1] = lsum;
-  }
-  __syncthreads();
-  if (wave == 0) {
-    float* out = a.out + (size_t)row * D + lane * V;
-    float Mt = red_ml[0][0];
-#pragma unroll
-    for (int w = 1; w < 4; ++w) Mt = fmaxf(Mt, red_ml[w][0]);
-    if (Mt == -INFINITY) {                  // no visible cell: zeros
-#pragma unroll
-      for (int e = 0; e < V; ++e) out[e] = 0.f;
-      return;
-    }
-    float f[4], Ls = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float mw = red_ml[w][0];
-      f[w] = (mw == -INFINITY) ? 0.f : exp2f(mw - Mt);
-      Ls = fmaf(f[w], red_ml[w][1], Ls);
-    }
-#pragma unroll
-    for (int e = 0; e < V; ++e) {
-      float x = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) x = fmaf(f[w], red_o[w][lane * V + e], x);
-      x = x / Ls;
-      if (gated) x *= 1.0f / (1.0f + __expf(-gt[e]));
-      out[e] = x;
-    }
-  }
-}
-
-template <int U>
-void launch_merge(const MergeArgs& a, int D, dim3 grid, hipStream_t st) {
-  switch (D) {
-    case 64: hipLaunchKernelGGL((merge_rows<64, U>), grid, dim3(kThreads), 0, st, a); break;
-    case 128: hipLaunchKernelGGL((merge_rows<128, U>), grid, dim3(kThreads), 0, st, a); break;
-    default: hipLaunchKernelGGL((merge_rows<256, U>), grid, dim3(kThreads), 0, st, a); break;
-  }
-}
 
 template <int D, bool I8, bool IDS, int NRB, int NW>
 hipError_t launch_one(const AttnArgs& a, dim3 grid, hipStream_t st) {
@@ -285,53 +156,6 @@ int gqa_decode_attn_i8(const float* q, const int8_t* k, const int8_t* v, const u
                        int Hk, int D, float scale, int chunk, void* stream) {
   return attn_common(true, q, k, v, k_scales, v_scales, ids, seq_lens, part, part_bytes, S, T,
                      Lmax, B, H, Hk, D, scale, chunk, stream);
-}
-
-static int merge_common(const float* part, const int32_t* seq_lens, const int32_t* ids_or_null,
-                        const float* gate, int64_t gate_stride, float* out, int S, int T,
-                        int Lmax, int B, int H, int D, int chunk, void* stream) {
-  if (!part || !seq_lens || !out) return GQA_ERR_NULL;
-  const bool ids = ids_or_null != nullptr;
-  gqa::Shape sh{S, T, Lmax, ids ? B : 0, H, H, D, ids, false};
-  int rc = gqa::check_shape(sh);
-  if (rc != GQA_OK) return rc;
-  if (chunk < 1) return GQA_ERR_CHUNK;
-  if (gate && gate_stride < D) return GQA_ERR_SHAPE;
-  const int64_t P = gqa::num_splits(sh, chunk);
-  MergeArgs a;
-  a.part_o = part;
-  a.part_ml = part + gqa::part_o_floats(sh, P);
-  a.out = out;
-  a.gate = gate;
-  a.gate_stride = gate_stride;
-  a.P = (int)P;
-  const size_t rows = (size_t)S * T * H;
-  if (rows > 0x7fffffffu) return GQA_ERR_SHAPE;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  dim3 grid((unsigned)rows);
-  if (P <= 16)
-    launch_merge<4>(a, D, grid, st);
-  else if (P <= 32)
-    launch_merge<8>(a, D, grid, st);
-  else
-    launch_merge<16>(a, D, grid, st);
-  hipError_t e = hipGetLastError();
-  return e == hipSuccess ? GQA_OK : (int)e;
-}
-
-int gqa_decode_merge(const float* part, const int32_t* seq_lens, const int32_t* ids_or_null,
-                     float* out, int S, int T, int Lmax, int B, int H, int D, int chunk,
-                     void* stream) {
-  return merge_common(part, seq_lens, ids_or_null, nullptr, 0, out, S, T, Lmax, B, H, D, chunk,
-                      stream);
-}
-
-int gqa_decode_merge_gated(const float* part, const int32_t* seq_lens, const int32_t* ids_or_null,
-                           const float* gate, int64_t gate_stride, float* out, int S, int T,
-                           int Lmax, int B, int H, int D, int chunk, void* stream) {
-  if (!gate) return GQA_ERR_NULL;
-  return merge_common(part, seq_lens, ids_or_null, gate, gate_stride, out, S, T, Lmax, B, H, D,
-                      chunk, stream);
 }
 
 }  // extern "C"
