@@ -169,7 +169,7 @@ struct AttnLds {
   using G = TileGeom<D, I8>;
   static constexpr int RB = 16 * NRB;
   static constexpr int VT = NW * G::TC * G::RBY;         // per-wave V tiles (and K tiles)
-  static constexpr int BUF = NW / 2 * RB * D * 4;        // cross-wave merge buffers (alias tiles)
+  static constexpr int BUF2 = NW / 2 * RB * D * 4;       // two-stage cross-wave combine buffers
   static constexpr int QB = NRB * G::KS * 2 * 64 * 16;   // query B operands, hi and lo
   static constexpr int SC = I8 ? NW * 2 * G::TC * G::NG * 2 : 0;  // per-wave K/V scales
   static constexpr int ML = NW * RB * 2 * 4;             // per-wave (m, l)
@@ -182,9 +182,19 @@ struct AttnLds {
   // 64 us).  int8 K, whose path is already bound by the vector ALU, and
   // tiles that do not fit load each lane's K operand fragment straight into
   // registers (int8 32K: 50 us that way, 55 us through LDS).
-  static constexpr int MAIN_KL = 2 * VT > BUF ? 2 * VT : BUF;
+  static constexpr int MAIN_KL = 2 * VT > BUF2 ? 2 * VT : BUF2;
   static constexpr bool KL = !I8 && MAIN_KL + QB + SC + ML + IDSB <= CAP;
-  static constexpr int MAIN = KL ? MAIN_KL : (VT > BUF ? VT : BUF);
+  static constexpr int TILES = KL ? 2 * VT : VT;
+  // The waves combine in one pass (each parks its unscaled accumulators in a
+  // buffer of its own, one barrier, every output element sums the NW
+  // buffers) when NW buffers fit beside everything else; otherwise in two
+  // (half the waves park, the other half add, then the sums are added).
+  // The buffers alias the tiles either way.
+  static constexpr int BUF1 = NW * RB * D * 4;
+  static constexpr bool ONE_PASS =
+      NW > 1 && (TILES > BUF1 ? TILES : BUF1) + QB + SC + ML + IDSB <= CAP;
+  static constexpr int BUF = ONE_PASS ? BUF1 : BUF2;     // cross-wave combine buffers (alias tiles)
+  static constexpr int MAIN = TILES > BUF ? TILES : BUF;
   static constexpr int BYTES = MAIN + QB + SC + ML;
 };
 
@@ -717,71 +727,119 @@ __global__ __launch_bounds__(64 * NW, (attn_occupancy<D, I8, NRB>())) void attn_
     return;
   }
 
-  // ---- combine the NW waves: one partial per query row.  Each wave
-  // rescales its accumulators to the rows' common max, the upper half of the
-  // waves parks them in LDS, the lower half adds theirs, and the NW/2 sums
-  // are added while the partial is written. ----
-  constexpr int HALF = NW / 2 > 0 ? NW / 2 : 1;
-  __syncthreads();
-  if (lb == 0) {
+  // ---- combine the NW waves: one partial per query row. ----
+  if constexpr (L::ONE_PASS) {
+    // Every wave parks its (m, l) and its unscaled accumulators in its own
+    // buffer; after one barrier each output element is the sum over the
+    // waves of exp2(m_w - M) * o_w, with M the rows' common max.
+    __syncthreads();                               // the tiles the buffers alias are done with
+    if (lb == 0) {
+#pragma unroll
+      for (int k = 0; k < NRB; ++k) {
+        mls[(wave * RB + 16 * k + lr) * 2] = m_run[k];
+        mls[(wave * RB + 16 * k + lr) * 2 + 1] = l_run[k];
+      }
+    }
+    float* bw = reinterpret_cast<float*>(smem) + wave * RB * D;
+#pragma unroll
+    for (int k = 0; k < NRB; ++k)
+#pragma unroll
+      for (int nb = 0; nb < G::NB; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bw[(16 * k + 4 * lb + i) * D + 16 * nb + lr] = O[k][nb][i];
+    __syncthreads();
+    const float* b0 = reinterpret_cast<const float*>(smem);
+    for (int idx = tid; idx < RB * D / 4; idx += NT) {
+      const int row = idx / (D / 4);
+      const int d4 = idx % (D / 4);
+      const int r = r0 + row;
+      if (r < a.R) {
+        float mw[NW], M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          mw[w] = mls[(w * RB + row) * 2];
+          M = fmaxf(M, mw[w]);
+        }
+        float4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          const float f = (mw[w] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw[w] - M);
+          const float4 y = *reinterpret_cast<const float4*>(b0 + w * RB * D + row * D + 4 * d4);
+          x.x = __builtin_fmaf(f, y.x, x.x);
+          x.y = __builtin_fmaf(f, y.y, x.y);
+          x.z = __builtin_fmaf(f, y.z, x.z);
+          x.w = __builtin_fmaf(f, y.w, x.w);
+        }
+        const size_t prow = ((size_t)(s * a.T + row_t(r)) * a.H + row_h(r)) * a.P + p;
+        *reinterpret_cast<float4*>(a.part_o + prow * D + 4 * d4) = x;
+      }
+    }
+  } else {
+    // Two passes: each wave rescales its accumulators to the rows' common max,
+    // the upper half of the waves parks them in LDS, the lower half adds
+    // theirs, and the NW/2 sums are added while the partial is written.
+    constexpr int HALF = NW / 2 > 0 ? NW / 2 : 1;
+    __syncthreads();
+    if (lb == 0) {
+#pragma unroll
+      for (int k = 0; k < NRB; ++k) {
+        mls[(wave * RB + 16 * k + lr) * 2] = m_run[k];
+        mls[(wave * RB + 16 * k + lr) * 2 + 1] = l_run[k];
+      }
+    }
+    __syncthreads();
+    float* buf = reinterpret_cast<float*>(smem);
 #pragma unroll
     for (int k = 0; k < NRB; ++k) {
-      mls[(wave * RB + 16 * k + lr) * 2] = m_run[k];
-      mls[(wave * RB + 16 * k + lr) * 2 + 1] = l_run[k];
-    }
-  }
-  __syncthreads();
-  float* buf = reinterpret_cast<float*>(smem);
 #pragma unroll
-  for (int k = 0; k < NRB; ++k) {
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * k + 4 * lb + i;
+        float M = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 16 * k + 4 * lb + i;
-      float M = -INFINITY;
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, mls[(w * RB + row) * 2]);
+        const float ms = mls[(wave * RB + row) * 2];
+        const float f = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
 #pragma unroll
-      for (int w = 0; w < NW; ++w) M = fmaxf(M, mls[(w * RB + row) * 2]);
-      const float ms = mls[(wave * RB + row) * 2];
-      const float f = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-#pragma unroll
-      for (int nb = 0; nb < G::NB; ++nb) O[k][nb][i] *= f;
-    }
-  }
-  if (wave >= HALF) {
-    float* b = buf + (wave - HALF) * RB * D;
-#pragma unroll
-    for (int k = 0; k < NRB; ++k)
-#pragma unroll
-      for (int nb = 0; nb < G::NB; ++nb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) b[(16 * k + 4 * lb + i) * D + 16 * nb + lr] = O[k][nb][i];
-  }
-  __syncthreads();
-  if (wave < HALF) {
-    float* b = buf + wave * RB * D;
-#pragma unroll
-    for (int k = 0; k < NRB; ++k)
-#pragma unroll
-      for (int nb = 0; nb < G::NB; ++nb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float* x = b + (16 * k + 4 * lb + i) * D + 16 * nb + lr;
-          *x = *x + O[k][nb][i];
-        }
-  }
-  __syncthreads();
-  for (int idx = tid; idx < RB * D / 4; idx += NT) {
-    const int row = idx / (D / 4);
-    const int d4 = idx % (D / 4);
-    const int r = r0 + row;
-    if (r < a.R) {
-      float4 x = *reinterpret_cast<const float4*>(buf + row * D + 4 * d4);
-#pragma unroll
-      for (int w = 1; w < HALF; ++w) {
-        const float4 y = *reinterpret_cast<const float4*>(buf + w * RB * D + row * D + 4 * d4);
-        x.x += y.x; x.y += y.y; x.z += y.z; x.w += y.w;
+        for (int nb = 0; nb < G::NB; ++nb) O[k][nb][i] *= f;
       }
-      const size_t prow = ((size_t)(s * a.T + row_t(r)) * a.H + row_h(r)) * a.P + p;
-      *reinterpret_cast<float4*>(a.part_o + prow * D + 4 * d4) = x;
+    }
+    if (wave >= HALF) {
+      float* b = buf + (wave - HALF) * RB * D;
+#pragma unroll
+      for (int k = 0; k < NRB; ++k)
+#pragma unroll
+        for (int nb = 0; nb < G::NB; ++nb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) b[(16 * k + 4 * lb + i) * D + 16 * nb + lr] = O[k][nb][i];
+    }
+    __syncthreads();
+    if (wave < HALF) {
+      float* b = buf + wave * RB * D;
+#pragma unroll
+      for (int k = 0; k < NRB; ++k)
+#pragma unroll
+        for (int nb = 0; nb < G::NB; ++nb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float* x = b + (16 * k + 4 * lb + i) * D + 16 * nb + lr;
+            *x = *x + O[k][nb][i];
+          }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < RB * D / 4; idx += NT) {
+      const int row = idx / (D / 4);
+      const int d4 = idx % (D / 4);
+      const int r = r0 + row;
+      if (r < a.R) {
+        float4 x = *reinterpret_cast<const float4*>(buf + row * D + 4 * d4);
+#pragma unroll
+        for (int w = 1; w < HALF; ++w) {
+          const float4 y = *reinterpret_cast<const float4*>(buf + w * RB * D + row * D + 4 * d4);
+          x.x += y.x; x.y += y.y; x.z += y.z; x.w += y.w;
+        }
+        const size_t prow = ((size_t)(s * a.T + row_t(r)) * a.H + row_h(r)) * a.P + p;
+        *reinterpret_cast<float4*>(a.part_o + prow * D + 4 * d4) = x;
+      }
     }
   }
   if (tid < RB && r0 + tid < a.R) {
