@@ -51,11 +51,11 @@ PROFILES = os.path.join(ROOT, "profiles")
 # the sources each measured kernel is built from: counters taken on one
 # version of a kernel do not describe another
 KERNEL_SOURCES = {
-    "attn": ["attn_mfma.h", "common.h", "gqa_decode.hip", "plan.h", "plan.cpp"],
+    "attn": ["attn_mfma.h", "mfma_util.h", "common.h", "gqa_decode.hip", "plan.h", "plan.cpp"],
     "merge": ["merge.hip", "common.h", "plan.h"],
     "append": ["append.hip"],
     "select": ["select.hip"],
-    "tq": ["attn_tq.h", "attn_mfma.h", "common.h", "tq.hip", "plan.h", "plan.cpp"],
+    "tq": ["attn_tq.h", "mfma_util.h", "common.h", "tq.hip", "plan.h", "plan.cpp"],
 }
 
 

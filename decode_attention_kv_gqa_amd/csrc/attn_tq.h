@@ -34,7 +34,8 @@
 // ([word][cell]) and each lane extracts its 2-bit field from eight words.
 #pragma once
 
-#include "attn_mfma.h"
+#include "common.h"
+#include "mfma_util.h"
 
 namespace gqa_kern {
 
