@@ -190,6 +190,50 @@ def test_deterministic_and_on_side_stream():
     assert np.array_equal(a, b.cpu().numpy())
 
 
+@pytest.mark.parametrize("kv,budget", [("i8", 0), ("f16", 0), ("i8", 48)])
+def test_step_replays_under_graph_capture(kv, budget):
+    # The calls allocate nothing and record no memset, so a caller can
+    # capture the step (attention + merge) into a HIP graph.  Each replay,
+    # with eager work and synchronisations between replays, must give the
+    # eager result bit for bit, and match the oracle.
+    import decode_attention_kv_gqa_amd as gq
+    D = 256 if kv == "i8" else 128
+    inp = make_case(2, 2, 12, 2, D, 700, [700, 300], kv=kv, budget=budget, seed=11 + budget)
+    dev = to_dev(inp)
+    sh = inp.shape
+    step = gq.DecodeAttention(sh["S"], sh["T"], sh["H"], sh["Hk"], sh["D"], sh["Lmax"], kv,
+                              B=budget, chunk=0, device="cuda")
+
+    def one():
+        step.attn(dev["q"], dev["k"], dev["v"], dev["seq_lens"], inp.scale, dev["k_scales"],
+                  dev["v_scales"], dev["ids"])
+        step.merge(dev["seq_lens"], dev["ids"])
+
+    print(f"[gpu] graph capture kv={kv} budget={budget}", flush=True)
+    one()
+    torch.cuda.synchronize()
+    eager = step.out.clone()
+    assert_parity(eager.cpu().numpy(), oracle(inp), f"eager kv={kv} budget={budget}")
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            one()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for r in range(4):
+        step.out.zero_()
+        step.part.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(step.out, eager), f"replay {r}"
+        one()                                    # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(step.out, eager)
+
+
 def test_errors_do_not_launch():
     import decode_attention_kv_gqa_amd as gq
     from decode_attention_kv_gqa_amd import _lib

@@ -96,3 +96,43 @@ def test_tq_full_size_sampled_rows():
     ref = oracle(inp, rows=rows)
     g = np.stack([got[s, t, h] for (s, t, h) in rows])
     assert_parity(g, ref, f"{name} sampled rows")
+
+
+def test_tq_step_replays_under_graph_capture():
+    # attention + merge (with the inverse rotation) captured into a HIP graph:
+    # every replay, with eager work between replays, gives the eager result
+    import decode_attention_kv_gqa_amd as gq
+    inp = make_tq_case(2, 1, 8, 2, 128, 400, [400, 150], seed=21)
+    print("[gpu] tq graph capture", flush=True)
+    x = {k: dev(getattr(inp, k)) for k in ("q_rot", "q_jl", "k_polar", "k_jl", "k_norms",
+                                           "v_polar", "v_norms", "seq_lens", "signs")}
+    S, T, H, D = inp.q_rot.shape
+    Hk, Lmax = inp.k_polar.shape[1], inp.k_polar.shape[2]
+    step = gq.TqDecodeAttention(S, T, H, Hk, D, Lmax, chunk=0, device="cuda")
+
+    def one():
+        step.attn(x["q_rot"], x["q_jl"], x["k_polar"], x["k_jl"], x["k_norms"], x["v_polar"],
+                  x["v_norms"], x["seq_lens"], inp.centroids, inp.qjl_scale, inp.scale)
+        step.merge(x["seq_lens"], x["signs"])
+
+    one()
+    torch.cuda.synchronize()
+    eager = step.out.clone()
+    assert_parity(eager.cpu().numpy(), oracle(inp), "tq eager")
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            one()
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    for r in range(4):
+        step.out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(step.out, eager), f"replay {r}"
+        one()
+        torch.cuda.synchronize()
+        assert torch.equal(step.out, eager)
