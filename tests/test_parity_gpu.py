@@ -144,6 +144,28 @@ def test_int8_large_v_scales_after_a_lagging_max(Hk):
         assert_parity(got, ref, f"large V scales Hk={Hk} chunk={chunk}")
 
 
+@pytest.mark.parametrize("kv", ["f16", "i8"])
+@pytest.mark.parametrize("T", [1, 3])
+def test_uneven_batch(kv, T):
+    # windows of every kind in one batch (empty, one cell, short, one split,
+    # full), several KV heads, splits from 64 cells to the whole window
+    D = 128 if kv == "f16" else 256
+    lens = [700, 0, 1, 37, 513, 699, 64, 2]
+    inp = make_case(8, T, 8, 2, D, 700, lens, kv=kv, seed=31 + T)
+    ref = oracle(inp)
+    for chunk in (64, 100, 350, 700, 0):
+        got = run_gpu(inp, chunk=chunk)
+        assert_parity(got, ref, f"uneven kv={kv} T={T} chunk={chunk}")
+        assert not got[1].any()
+
+
+def test_many_short_sequences():
+    # 520 sequences of 0..40 cells: 1040 (sequence, KV head) units
+    lens = [(7 * i) % 41 for i in range(520)]
+    inp = make_case(520, 1, 4, 2, 64, 40, lens, kv="f16", seed=9)
+    assert_parity(run_gpu(inp, chunk=8), oracle(inp), "520 sequences")
+
+
 def test_rows_beyond_one_block():
     # G * T = 64 query rows per KV head: two row blocks, each streams K/V
     inp = make_case(2, 8, 16, 2, 128, 300, [300, 190], kv="f16", seed=5)
