@@ -8,15 +8,16 @@
 // written in ascending order; with n <= B the ids are 0 .. n-1.
 //
 // How (one workgroup of 1024 threads per token):
-//   1. Four 8-bit radix passes over the blocks' order-preserving 32-bit keys
-//      find the key Tk of the block where the running cell count, from the
-//      highest key down, reaches B, and how many cells `need` must still come
-//      from blocks whose key equals Tk.  Each pass builds a 256-bin histogram
-//      of cell counts in LDS (ds_add, one histogram per wave, then summed)
-//      over the blocks that match the digits found so far; every wave scans
-//      the bins from the top with a wave-wide prefix sum and finds the digit
-//      itself, so a pass needs two barriers.  Up to 16 keys per thread stay
-//      in registers across the passes.
+//   1. Three radix passes (12, 10 and 10 bits) over the blocks' order-
+//      preserving 32-bit keys find the key Tk of the block where the running
+//      cell count, from the highest key down, reaches B, and how many cells
+//      `need` must still come from blocks whose key equals Tk.  Each pass
+//      counts cells per digit with LDS atomics into a histogram region of
+//      its own (zeroed once, so no pass clears for the next), over the
+//      blocks that match the digits found so far; after one barrier every
+//      wave finds the digit itself (lane sums of 64 or 16 counters, a wave
+//      prefix sum to find the lane, a second one over that lane's counters).
+//      Up to 16 keys per thread stay in registers across the passes.
 //   2. Emission: every thread owns a contiguous block range; one block-wide
 //      prefix sum of its counts of blocks above and at Tk gives each thread
 //      its share of the Tk blocks (in block order) and its output offset,
@@ -92,12 +93,48 @@ __device__ __forceinline__ void block_excl_scan2(uint32_t x, uint32_t y, uint32_
   ye = yb + yi - y;
 }
 
+// Radix digits, most significant first: 12, 10 and 10 bits of the key.
+// Each pass counts into its own region of one LDS histogram (zeroed once),
+// so no pass waits for another's counts to be cleared.
+constexpr int kPasses = 3;
+constexpr int kDigitShift[kPasses] = {20, 10, 0};
+constexpr int kDigitBins[kPasses] = {4096, 1024, 1024};
+constexpr int kHistBase[kPasses] = {0, 4096, 5120};
+constexpr int kHistBins = 6144;
+
+// The digit of the threshold within one pass's histogram h of `bins`
+// counters, ranked from the top: the digit whose counter takes the running
+// count, from the highest digit down, to `need` cells, and how many cells
+// `need` still asks of blocks with that digit.  Every wave computes it
+// itself: lane l sums the bins/64 counters of digits from the top (l * w ..
+// l * w + w - 1 places down), a wave prefix sum finds the lane where the
+// count reaches `need`, and the wave's lanes then read that lane's w
+// counters one each and prefix-sum them to find the digit.
+template <int BINS>
+__device__ __forceinline__ void find_digit(const uint32_t* h, uint32_t need, int lane,
+                                           uint32_t& digit, uint32_t& left) {
+  constexpr int W = BINS / 64;
+  // lane l's counters are h[BINS - (l+1) W .. BINS - l W); lane l starts its
+  // walk l places in, so the lanes of one read hit different banks
+  const uint32_t* mine = h + BINS - (lane + 1) * W;
+  uint32_t lsum = 0;
+#pragma unroll
+  for (int j = 0; j < W; ++j) lsum += mine[(j + lane) & (W - 1)];
+  const uint32_t above = wave_incl_scan(lsum) - lsum;   // cells in higher digits
+  const uint64_t hit = __ballot(above < need && above + lsum >= need);
+  const int L = hit ? __builtin_ctzll(hit) : 0;
+  const uint32_t aboveL = (uint32_t)__shfl((int)above, L, 64);
+  // lane j < W takes the counter j places below the top of lane L's range
+  const uint32_t c = lane < W ? h[BINS - 1 - L * W - lane] : 0u;
+  const uint32_t ci = wave_incl_scan(c), ce = ci - c;
+  const uint64_t hit2 = __ballot(lane < W && aboveL + ce < need && aboveL + ci >= need);
+  const int J = hit2 ? __builtin_ctzll(hit2) : 0;
+  digit = hit ? (uint32_t)(BINS - 1 - L * W - J) : 0u;
+  left = hit ? need - aboveL - (uint32_t)__shfl((int)ce, J, 64) : need;
+}
+
 __global__ __launch_bounds__(kSelThreads) void select_ids(SelArgs a) {
-  // one 256-bin histogram per wave (summed per pass): the top key bytes of
-  // real scores take few values, and one shared histogram would serialise
-  // every wave's adds on the same bins
-  __shared__ uint32_t hist[kSelWaves][256];
-  __shared__ uint32_t tot[256];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kHistBins];
   __shared__ uint32_t wsum[2 * kSelWaves];
   __shared__ int32_t obuf[kSelOutLds];   // the token's ids before the coalesced write
   extern __shared__ uint32_t keyl[];     // block keys (first kKeysInLds blocks)
@@ -134,58 +171,35 @@ __global__ __launch_bounds__(kSelThreads) void select_ids(SelArgs a) {
   const int n_bid = n >> 2, rem = n & 3, nb = n_bid + 1;
   auto cells_of = [&](int b) -> uint32_t { return b < n_bid ? 4u : (uint32_t)rem; };
   auto key = [&](int b) -> uint32_t { return b < kKeysInLds ? keyl[b] : okey(sc[b]); };
-#pragma unroll
-  for (int j = 0; j < 4; ++j) hist[wave][lane + 64 * j] = 0;
+  for (int i = tid; i < kHistBins; i += kSelThreads) hist[i] = 0;
   __syncthreads();
 
-  // ---- 1. radix select of the threshold key: two barriers per pass ----
+  // ---- 1. radix select of the threshold key: one barrier per pass ----
   uint32_t prefix = 0, pmask = 0, need = (uint32_t)a.B;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    uint32_t* h = hist[wave];
+#pragma unroll
+  for (int pass = 0; pass < kPasses; ++pass) {
+    const int shift = kDigitShift[pass];
+    const uint32_t dmask = (uint32_t)kDigitBins[pass] - 1u;
+    uint32_t* h = hist + kHistBase[pass];
 #pragma unroll
     for (int i = 0; i < kKeysInRegs; ++i) {
       const int b = tid + kSelThreads * i;
       if (b < nb && (kr[i] & pmask) == prefix && cells_of(b))
-        atomicAdd(&h[(kr[i] >> shift) & 255u], cells_of(b));
+        atomicAdd(&h[(kr[i] >> shift) & dmask], cells_of(b));
     }
     for (int b = tid + kSelThreads * kKeysInRegs; b < nb; b += kSelThreads) {
       const uint32_t k = key(b);
-      if ((k & pmask) == prefix && cells_of(b)) atomicAdd(&h[(k >> shift) & 255u], cells_of(b));
+      if ((k & pmask) == prefix && cells_of(b)) atomicAdd(&h[(k >> shift) & dmask], cells_of(b));
     }
     __syncthreads();
-    if (tid < 256) {                     // sum the wave histograms, clear them for the next pass
-      uint32_t x = 0;
-#pragma unroll
-      for (int w = 0; w < kSelWaves; ++w) {
-        x += hist[w][tid];
-        hist[w][tid] = 0;
-      }
-      tot[tid] = x;
-    }
-    __syncthreads();
-    // every wave finds the digit itself: lane l holds digits 255-4l .. 252-4l
-    uint32_t c[4], lsum = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) { c[j] = tot[255 - 4 * lane - j]; lsum += c[j]; }
-    uint32_t above = wave_incl_scan(lsum) - lsum;   // cells in higher digits
-    uint32_t dsel = 0, nsel = 0;
-    bool found = false;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (above < need && above + c[j] >= need) {
-        found = true;
-        dsel = 255u - 4u * lane - j;
-        nsel = need - above;
-      }
-      above += c[j];
-    }
-    const uint64_t who = __ballot(found);
-    const int src = who ? __builtin_ctzll(who) : 0;
-    const uint32_t digit = who ? (uint32_t)__shfl((int)dsel, src, 64) : 0u;
-    need = who ? (uint32_t)__shfl((int)nsel, src, 64) : need;
+    uint32_t digit, left;
+    if (pass == 0)
+      find_digit<4096>(h, need, lane, digit, left);
+    else
+      find_digit<1024>(h, need, lane, digit, left);
+    need = left;
     prefix |= digit << shift;
-    pmask |= 255u << shift;
+    pmask |= dmask << shift;
   }
   const uint32_t Tk = prefix;
 
