@@ -21,9 +21,8 @@
 //   2. Emission: every thread owns a contiguous block range; one block-wide
 //      prefix sum of its counts of blocks above and at Tk gives each thread
 //      its share of the Tk blocks (in block order) and its output offset,
-//      so the ids come out ascending.  The
-//      keys come from LDS, and the ids are gathered in LDS and written to
-//      memory in one coalesced pass.
+//      so the ids come out ascending.  The keys come from LDS, and the ids
+//      are gathered in LDS and written to memory in one coalesced pass.
 // The page's kernel makes the same two phases on Apple simdgroups; here the
 // scans are wave64 DPP moves and the histogram lives in LDS.
 #include <hip/hip_runtime.h>
@@ -115,7 +114,8 @@ __device__ __forceinline__ void find_digit(const uint32_t* h, uint32_t need, int
                                            uint32_t& digit, uint32_t& left) {
   constexpr int W = BINS / 64;
   // lane l's counters are h[BINS - (l+1) W .. BINS - l W); lane l starts its
-  // walk l places in, so the lanes of one read hit different banks
+  // walk l places in, which spreads the lanes of one read over the banks
+  // (without the skew every lane would read the same bank)
   const uint32_t* mine = h + BINS - (lane + 1) * W;
   uint32_t lsum = 0;
 #pragma unroll
