@@ -176,12 +176,24 @@ __global__ __launch_bounds__(64 * NW, (attn_occupancy<D, I8, NRB>())) void attn_
   // fabric), so the index that varies fastest must carry equal work: the KV
   // head, then the sequence; the split index varies slowest, because the
   // last splits of short sequences are empty and would otherwise all land
-  // on the same XCDs.
+  // on the same XCDs.  With a.seq_fast the sequence varies fastest instead:
+  // with S a multiple of 8 every KV head of a (sequence, split) then runs on
+  // the same XCD, so the heads' reads of the same cells (int8: the scale
+  // lines they share, the neighbouring halves of each cell's K/V run) meet
+  // in one L2.
   int id = blockIdx.x;
-  const int g = id % a.Hk;
-  id /= a.Hk;
-  const int s = id % a.S;
-  id /= a.S;
+  int g, s;
+  if (a.seq_fast) {
+    s = id % a.S;
+    id /= a.S;
+    g = id % a.Hk;
+    id /= a.Hk;
+  } else {
+    g = id % a.Hk;
+    id /= a.Hk;
+    s = id % a.S;
+    id /= a.S;
+  }
   const int nu = a.nrb * (IDS ? a.T : 1);
   const int rbl = (id % nu) % a.nrb;
   const int tq = (id % nu) / a.nrb;

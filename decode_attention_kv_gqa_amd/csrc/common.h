@@ -38,6 +38,7 @@ struct AttnArgs {
   float* part_o;     // [S][T][H][P][D]
   float* part_ml;    // [S][T][H][P][2]  (running max in base-2 units, running sum)
   int S, T, Lmax, B, H, Hk, G, R, nrb, P, chunk;
+  int seq_fast;      // 1: grid order with the sequence varying fastest, else the KV head
   float qscale;      // scale * log2(e)
 };
 
