@@ -20,7 +20,11 @@ Reported (one JSON line on stdout):
                mean duration from HIP events on its stream (bursts of
                back-to-back launches), against the 8 TB/s HBM peak; `traffic` is HBM bytes per launch measured
                with rocprofv3 counters (from profiles/, null when the kernel
-               source changed since they were taken)
+               source changed since they were taken); `stream_read` is the
+               rate of a plain streaming read of the same number of bytes
+               (gqa_bench_stream_read, best of a few launch shapes), the
+               machine's practical read ceiling, and the kernel's fraction
+               of it
   cpu_baseline the fp64 oracle on the host cores over a bounded sample
 To keep back-to-back steps from hitting the 256 MB last-level cache, the
 inputs are replicated and the steps rotate through the copies, so every step
@@ -149,6 +153,59 @@ def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
     dt = (time.perf_counter() - t0) / reps
     print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "reps": reps,
                       "copy_GBps": round(2 * nbytes / dt / 1e9, 1)}), flush=True)
+
+
+def stream_read_rate(nbytes: int, dev, shapes=(256, 512, 1024, 2048), reps: int = 20):
+    """The machine's practical HBM read rate over nbytes: gqa_bench_stream_read
+    (a plain 16-byte streaming read, include/gqa_bench.h) over buffers of that
+    size rotated like the inputs, best of a few launch shapes, each timed with
+    HIP events around `reps` back-to-back launches.  Checks that the XOR of
+    the sink words equals the XOR of the buffer, i.e. that every byte was
+    read.  Returns (GB/s, workgroups, bytes read)."""
+    import torch
+    import decode_attention_kv_gqa_amd as gq
+    n = nbytes // 16 * 16
+    copies = max(2, min(8, math.ceil(3 * LLC_BYTES / n) + 1))
+    g = torch.Generator(device=dev).manual_seed(7)
+    bufs = [torch.randint(-2 ** 31, 2 ** 31 - 1, (n // 4,), dtype=torch.int32, device=dev,
+                          generator=g) for _ in range(copies)]
+    sink = torch.zeros(max(shapes), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def launch(i, wg):
+        rc = gq.gqa_bench_stream_read(bufs[i % copies].data_ptr(), n, sink.data_ptr(), wg,
+                                      stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"gqa_bench_stream_read: {gq.strerror(rc)}")
+
+    def xor_all(t):
+        t = t.view(torch.int64) if t.numel() % 2 == 0 else t
+        while t.numel() > 1:
+            if t.numel() % 2:
+                t = torch.cat([t, torch.zeros(1, dtype=t.dtype, device=t.device)])
+            t = torch.bitwise_xor(t[0::2], t[1::2])
+        return int(t.item())
+
+    best = (float("inf"), 0)
+    for wg in shapes:
+        launch(0, wg)
+        torch.cuda.synchronize()
+        want = xor_all(bufs[0].clone())
+        got = xor_all(sink[:wg].clone())
+        if (want ^ (want >> 32)) & 0xffffffff != (got ^ (got >> 32)) & 0xffffffff:
+            raise RuntimeError("gqa_bench_stream_read: sink XOR does not match the buffer")
+        for i in range(5):
+            launch(i, wg)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            launch(i, wg)
+        e1.record(stream)
+        e1.synchronize()
+        sec = e0.elapsed_time(e1) / reps / 1e3
+        best = min(best, (sec, wg))
+    del bufs
+    return n / best[0] / 1e9, best[1], n
 
 
 def bench_select(args):
@@ -466,6 +523,7 @@ def main():
 
     achieved = step_bytes / attn_mean_s / 1e9
     traffic = load_traffic(args.workload)
+    sr_gbs, sr_wg, sr_bytes = stream_read_rate(step_bytes, dev)
     res = {
         "metric": "decode-attention effective KV HBM GB/s (% of peak) and us/step, 1 MI355X",
         "value": round(step_bytes / (wall / K) / 1e9, 2),
@@ -496,7 +554,10 @@ def main():
                      "kernel": "attn_chunk",
                      "kernel_us_mean": round(attn_mean_s * 1e6, 3),
                      "kernel_us_burst_min_max": [round(float(attn_ms.min()) * 1e3, 3),
-                                                 round(float(attn_ms.max()) * 1e3, 3)]},
+                                                 round(float(attn_ms.max()) * 1e3, 3)],
+                     "stream_read": {"gbs": round(sr_gbs, 2), "bytes": sr_bytes,
+                                     "workgroups": sr_wg,
+                                     "kernel_frac_of_stream_read": round(achieved / sr_gbs, 4)}},
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the fp64 oracle on the host", file=sys.stderr, flush=True)

@@ -25,7 +25,7 @@ EXPORTED = ["gqa_decode_attn_f16", "gqa_decode_attn_i8", "gqa_decode_merge",
             "gqa_decode_merge_gated", "gqa_decode_attn_tq", "gqa_decode_merge_tq",
             "gqa_decode_select_ids", "gqa_decode_append_i8", "gqa_decode_part_bytes",
             "gqa_decode_auto_chunk",
-            "gqa_decode_strerror"]
+            "gqa_decode_strerror", "gqa_bench_stream_read"]
 
 _lib = None
 
@@ -69,6 +69,8 @@ def load() -> ctypes.CDLL:
     lib.gqa_decode_auto_chunk.restype = i32
     lib.gqa_decode_strerror.argtypes = [i32]
     lib.gqa_decode_strerror.restype = ctypes.c_char_p
+    lib.gqa_bench_stream_read.argtypes = [vp, sz, vp, i32, vp]
+    lib.gqa_bench_stream_read.restype = i32
     _lib = lib
     return lib
 
@@ -138,3 +140,10 @@ def gqa_decode_append_i8(k_new, v_new, pos, k, v, k_scales, v_scales, S, Tn, Lma
                          stream=0) -> int:
     return load().gqa_decode_append_i8(_p(k_new), _p(v_new), _p(pos), _p(k), _p(v), _p(k_scales),
                                        _p(v_scales), S, Tn, Lmax, Hk, D, _p(stream))
+
+
+def gqa_bench_stream_read(src, nbytes, sink, workgroups, stream=0) -> int:
+    """Measurement aid (include/gqa_bench.h): a plain streaming read of nbytes
+    at src by `workgroups` workgroups; sink[w] = XOR of the words workgroup w
+    read."""
+    return load().gqa_bench_stream_read(_p(src), nbytes, _p(sink), workgroups, _p(stream))

@@ -15,7 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libgqa_decode.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["gqa_decode.hip", "merge.hip", "select.hip", "append.hip", "tq.hip", "plan.cpp"]
+SOURCES = ["gqa_decode.hip", "merge.hip", "select.hip", "append.hip", "tq.hip", "plan.cpp",
+           "stream_read.hip"]
 
 # Every HIP translation unit is built for gfx950 only, with packed-fp32 VALU
 # instructions disabled (the compiler otherwise forms v_pk_*_f32 from plain

@@ -171,3 +171,12 @@ def test_append_rejects():
     assert f(*args, 1, 1, 16, 2, 96, 0) == _lib.GQA_ERR_HEAD_DIM
     assert f(*([None] + [FAKE] * 6), 1, 1, 16, 2, 64, 0) == _lib.GQA_ERR_NULL
     assert f(*([None] * 7), 1, 0, 16, 2, 64, 0) == _lib.GQA_OK      # nothing to write
+
+
+def test_stream_read_rejects():
+    f = gq.gqa_bench_stream_read
+    assert f(None, 64, FAKE, 4, 0) == _lib.GQA_ERR_NULL
+    assert f(FAKE, 64, None, 4, 0) == _lib.GQA_ERR_NULL
+    assert f(FAKE, 63, FAKE, 4, 0) == _lib.GQA_ERR_SHAPE      # not a multiple of 16 bytes
+    assert f(FAKE + 8, 64, FAKE, 4, 0) == _lib.GQA_ERR_SHAPE  # misaligned
+    assert f(FAKE, 64, FAKE, 0, 0) == _lib.GQA_ERR_SHAPE
