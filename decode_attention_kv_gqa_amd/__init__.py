@@ -109,31 +109,46 @@ class DecodeAttention:
 
 
 def _validate(q, k, v, seq_lens, k_scales, v_scales, ids):
+    """Dtypes and shapes first (the kernels address every array from the
+    shapes, so a smaller tensor would be read past its end), then device and
+    layout."""
     import torch
     tensors = [("q", q), ("k", k), ("v", v), ("seq_lens", seq_lens)]
-    if k_scales is not None:
+    if k is not None and k.dtype == torch.int8:
         tensors += [("k_scales", k_scales), ("v_scales", v_scales)]
     if ids is not None:
         tensors.append(("ids", ids))
     for name, t in tensors:
         if t is None:
             raise ValueError(f"{name} is required")
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a GPU tensor (there is no CPU path)")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
     if q.dtype != torch.float32:
         raise ValueError("q must be float32 [S][T][H][D]")
     if seq_lens.dtype != torch.int32 or (ids is not None and ids.dtype != torch.int32):
         raise ValueError("seq_lens and ids must be int32")
     if k.dtype == torch.int8:
-        if k_scales is None or v_scales is None or k_scales.dtype != torch.float16 \
-                or v_scales.dtype != torch.float16:
+        if k_scales.dtype != torch.float16 or v_scales.dtype != torch.float16:
             raise ValueError("int8 K/V need float16 k_scales and v_scales [S][Lmax][Hk][D/64]")
     elif k.dtype != torch.float16:
         raise ValueError("K/V must be float16 or int8")
     if v.dtype != k.dtype or v.shape != k.shape:
         raise ValueError("K and V must share dtype and shape")
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [S][T][H][D] and k, v [S][Lmax][Hk][D]")
+    S, T, _, D = q.shape
+    _, Lmax, Hk, Dk = k.shape
+    if Dk != D or k.shape[0] != S or tuple(seq_lens.shape) != (S,):
+        raise ValueError("shape mismatch between q, k/v and seq_lens")
+    if k.dtype == torch.int8:
+        want = (S, Lmax, Hk, D // 64)
+        if tuple(k_scales.shape) != want or tuple(v_scales.shape) != want:
+            raise ValueError(f"k_scales and v_scales must be {list(want)}")
+    if ids is not None and (ids.dim() != 3 or tuple(ids.shape[:2]) != (S, T)):
+        raise ValueError("ids must be [S][T][B]")
+    for name, t in tensors:
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor (there is no CPU path)")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
 
 
 def decode_attention(q, k, v, seq_lens, scale: Optional[float] = None, *, k_scales=None,
@@ -145,10 +160,10 @@ def decode_attention(q, k, v, seq_lens, scale: Optional[float] = None, *, k_scal
     the gate half of [query | gate] rows (a view whose last dim is contiguous
     and whose head rows are evenly strided).  Returns out [S][T][H][D]
     float32, multiplied by sigmoid(gate) when a gate is given."""
+    import torch
     _validate(q, k, v, seq_lens, k_scales, v_scales, ids)
     gate_stride = None
     if gate is not None:
-        import torch
         if not gate.is_cuda or gate.dtype != torch.float32 or tuple(gate.shape) != tuple(q.shape):
             raise ValueError("gate must be a float32 GPU tensor shaped like q")
         S_, T_, H_, D_ = gate.shape
@@ -157,13 +172,11 @@ def decode_attention(q, k, v, seq_lens, scale: Optional[float] = None, *, k_scal
             raise ValueError("gate rows must be evenly strided with a contiguous last dim")
         gate_stride = st[2]
     S, T, H, D = q.shape
-    _, Lmax, Hk, Dk = k.shape
-    if Dk != D or k.shape[0] != S or seq_lens.shape != (S,):
-        raise ValueError("shape mismatch between q, k/v and seq_lens")
+    _, Lmax, Hk, _ = k.shape
     B = 0 if ids is None else ids.shape[2]
     if scale is None:
         scale = D ** -0.5
-    kv = "i8" if str(k.dtype) == "torch.int8" else "f16"
+    kv = "i8" if k.dtype == torch.int8 else "f16"
     step = DecodeAttention(S, T, H, Hk, D, Lmax, kv, B=B, chunk=chunk, device=q.device)
     return step(q, k, v, seq_lens, scale, k_scales, v_scales, ids, gate=gate,
                 gate_stride=gate_stride).clone()
@@ -182,8 +195,12 @@ def select_ids(block_scores, seq_lens, B: int, out=None):
         raise ValueError("block_scores must be float32 and seq_lens int32")
     S, T, nbs = block_scores.shape
     Lmax = 4 * (nbs - 1)
+    if tuple(seq_lens.shape) != (S,):
+        raise ValueError("seq_lens must be [S]")
     if out is None:
         out = torch.full((S, T, B), -1, dtype=torch.int32, device=block_scores.device)
+    elif tuple(out.shape) != (S, T, B) or out.dtype != torch.int32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous int32 [S][T][B] tensor")
     st = torch.cuda.current_stream(block_scores.device).cuda_stream
     rc = gqa_decode_select_ids(block_scores.data_ptr(), seq_lens.data_ptr(), out.data_ptr(), S, T,
                                Lmax, B, st)
@@ -206,9 +223,11 @@ def append_i8(k_new, v_new, pos, k, v, k_scales, v_scales):
             or k_scales.dtype != torch.float16 or v_scales.dtype != torch.float16:
         raise ValueError("dtypes: k_new/v_new float32, pos int32, k/v int8, scales float16")
     S, Tn, Hk, D = k_new.shape
-    _, Lmax, Hk2, D2 = k.shape
-    if (Hk2, D2) != (Hk, D) or v_new.shape != k_new.shape or v.shape != k.shape:
-        raise ValueError("shape mismatch between new rows and caches")
+    S2, Lmax, Hk2, D2 = k.shape
+    if (S2, Hk2, D2) != (S, Hk, D) or v_new.shape != k_new.shape or v.shape != k.shape \
+            or tuple(pos.shape) != (S,) or tuple(k_scales.shape) != (S, Lmax, Hk, D // 64) \
+            or k_scales.shape != v_scales.shape:
+        raise ValueError("shape mismatch between new rows, positions, caches and scales")
     st = torch.cuda.current_stream(k.device).cuda_stream
     rc = gqa_decode_append_i8(k_new.data_ptr(), v_new.data_ptr(), pos.data_ptr(), k.data_ptr(),
                               v.data_ptr(), k_scales.data_ptr(), v_scales.data_ptr(), S, Tn, Lmax,
@@ -282,8 +301,8 @@ def tq_decode_attention(q_rot, q_jl, k_polar, k_jl, k_norms, v_polar, v_norms, s
     if q_rot.shape != q_jl.shape:
         raise ValueError("q_rot and q_jl must share a shape")
     S, T, H, D = q_rot.shape
-    _, Hk, Lmax, W = k_polar.shape
-    if W * 16 != D or tuple(v_polar.shape) != tuple(k_polar.shape) \
+    S2, Hk, Lmax, W = k_polar.shape
+    if S2 != S or W * 16 != D or tuple(v_polar.shape) != tuple(k_polar.shape) \
             or tuple(k_jl.shape) != (S, Hk, Lmax, D // 32) \
             or tuple(k_norms.shape) != (S, Hk, Lmax) or tuple(v_norms.shape) != (S, Hk, Lmax) \
             or tuple(signs.shape) != (D,) or tuple(seq_lens.shape) != (S,):

@@ -180,3 +180,36 @@ def test_stream_read_rejects():
     assert f(FAKE, 63, FAKE, 4, 0) == _lib.GQA_ERR_SHAPE      # not a multiple of 16 bytes
     assert f(FAKE + 8, 64, FAKE, 4, 0) == _lib.GQA_ERR_SHAPE  # misaligned
     assert f(FAKE, 64, FAKE, 0, 0) == _lib.GQA_ERR_SHAPE
+
+
+@pytest.mark.parametrize("case", ["scales_short", "scales_missing", "ids_rows", "k_heads_dim",
+                                  "lens_len", "v_shape"])
+def test_python_wrapper_checks_shapes_before_launch(case):
+    """The kernels address every array from the shapes, so the wrapper
+    rejects arrays smaller than the shapes imply (checked before the device
+    check, so this runs without a GPU)."""
+    import torch
+    S, T, H, Hk, D, Lmax = 2, 1, 8, 2, 64, 16
+    q = torch.zeros(S, T, H, D)
+    k = torch.zeros(S, Lmax, Hk, D, dtype=torch.int8)
+    v = k.clone()
+    ks = torch.zeros(S, Lmax, Hk, D // 64, dtype=torch.float16)
+    vs = ks.clone()
+    lens = torch.ones(S, dtype=torch.int32)
+    ids = None
+    if case == "scales_short":
+        vs = torch.zeros(S, Lmax - 1, Hk, D // 64, dtype=torch.float16)
+    elif case == "scales_missing":
+        vs = None
+    elif case == "ids_rows":
+        ids = torch.zeros(S, T + 1, 4, dtype=torch.int32)
+    elif case == "k_heads_dim":
+        k = torch.zeros(S, Lmax, Hk, 2 * D, dtype=torch.int8)
+        v = k.clone()
+    elif case == "lens_len":
+        lens = torch.ones(S + 1, dtype=torch.int32)
+    elif case == "v_shape":
+        v = torch.zeros(S, Lmax - 1, Hk, D, dtype=torch.int8)
+    with pytest.raises(ValueError) as e:
+        gq.decode_attention(q, k, v, lens, k_scales=ks, v_scales=vs, ids=ids)
+    assert "GPU" not in str(e.value)
