@@ -223,13 +223,13 @@ def bench_select(args):
     lens = torch.full((S,), Lmax, dtype=torch.int32, device=dev)
     out = torch.full((S, T, B), -1, dtype=torch.int32, device=dev)
     for _ in range(args.warmup):
-        gq.select_ids(bs, lens, B, out=out)
+        gq.select_ids(bs, lens, B, out=out, Lmax=Lmax)
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     stream = torch.cuda.current_stream()
     a.record(stream)
     for _ in range(args.steps):
-        gq.select_ids(bs, lens, B, out=out)
+        gq.select_ids(bs, lens, B, out=out, Lmax=Lmax)
     b.record(stream)
     torch.cuda.synchronize()
     us = a.elapsed_time(b) / args.steps * 1e3

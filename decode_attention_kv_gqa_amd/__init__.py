@@ -182,21 +182,26 @@ def decode_attention(q, k, v, seq_lens, scale: Optional[float] = None, *, k_scal
                 gate_stride=gate_stride).clone()
 
 
-def select_ids(block_scores, seq_lens, B: int, out=None):
+def select_ids(block_scores, seq_lens, B: int, out=None, Lmax: Optional[int] = None):
     """Budget selection on the GPU.  block_scores [S][T][Lmax // 4 + 1]
     float32, seq_lens [S] int32; returns ids [S][T][B] int32 whose first
     min(L_t, B) entries per token are defined (the rest keep `out`'s contents,
-    -1 for a fresh output)."""
+    -1 for a fresh output).  Lmax is the cache capacity that windows are
+    clamped to; the scores' shape fixes it only up to the last block, so pass
+    it unless it is a multiple of 4 (the default is 4 * (blocks - 1))."""
     import torch
-    for name, t in (("block_scores", block_scores), ("seq_lens", seq_lens)):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous GPU tensor")
     if block_scores.dtype != torch.float32 or seq_lens.dtype != torch.int32:
         raise ValueError("block_scores must be float32 and seq_lens int32")
     S, T, nbs = block_scores.shape
-    Lmax = 4 * (nbs - 1)
+    if Lmax is None:
+        Lmax = 4 * (nbs - 1)
+    elif Lmax < 0 or Lmax // 4 + 1 != nbs:
+        raise ValueError("block_scores must be [S][T][Lmax // 4 + 1]")
     if tuple(seq_lens.shape) != (S,):
         raise ValueError("seq_lens must be [S]")
+    for name, t in (("block_scores", block_scores), ("seq_lens", seq_lens)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
     if out is None:
         out = torch.full((S, T, B), -1, dtype=torch.int32, device=block_scores.device)
     elif tuple(out.shape) != (S, T, B) or out.dtype != torch.int32 or not out.is_contiguous():

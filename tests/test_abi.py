@@ -213,3 +213,10 @@ def test_python_wrapper_checks_shapes_before_launch(case):
     with pytest.raises(ValueError) as e:
         gq.decode_attention(q, k, v, lens, k_scales=ks, v_scales=vs, ids=ids)
     assert "GPU" not in str(e.value)
+
+
+def test_select_wrapper_checks_capacity_against_scores():
+    import torch
+    bs = torch.zeros(1, 1, 2)                      # Lmax // 4 + 1 = 2: Lmax in 4..7
+    with pytest.raises(ValueError, match="Lmax"):
+        gq.select_ids(bs, torch.ones(1, dtype=torch.int32), 8, Lmax=8)

@@ -23,16 +23,17 @@ def _need_gpu():
     import decode_attention_kv_gqa_amd  # noqa: F401
 
 
-def run_select(bs, lens, B):
+def run_select(bs, lens, B, Lmax=None):
     import decode_attention_kv_gqa_amd as gq
-    print(f"[gpu] select shape={bs.shape} B={B}", flush=True)
-    out = gq.select_ids(torch.from_numpy(bs).cuda(), torch.from_numpy(lens).cuda(), B)
+    print(f"[gpu] select shape={bs.shape} B={B} Lmax={Lmax}", flush=True)
+    out = gq.select_ids(torch.from_numpy(bs).cuda(), torch.from_numpy(lens).cuda(), B,
+                        Lmax=Lmax)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
 
 def check(bs, lens, T, Lmax, B):
-    got = run_select(bs, lens, B)
+    got = run_select(bs, lens, B, Lmax)
     ref = R.select_budget_ids(bs, lens, T, Lmax, B)
     assert np.array_equal(got, ref), np.argwhere(got != ref)[:10]
 
@@ -82,7 +83,7 @@ def test_budgeted_decode_end_to_end(chunk):
     inp = make_case(S, T, H, Hk, D, Lmax, lens, kv="i8", seed=77, scale=1.0 / 16.0)
     bs = make_block_scores(S, T, Lmax, seed=78)
     d = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
-    ids_gpu = gq.select_ids(d(bs), d(inp.seq_lens), B)
+    ids_gpu = gq.select_ids(d(bs), d(inp.seq_lens), B, Lmax=Lmax)
     out = gq.decode_attention(d(inp.q), d(inp.k), d(inp.v), d(inp.seq_lens), inp.scale,
                               k_scales=d(inp.k_scales), v_scales=d(inp.v_scales), ids=ids_gpu,
                               chunk=chunk)
@@ -92,3 +93,27 @@ def test_budgeted_decode_end_to_end(chunk):
     ref = DR.gqa_decode_ref(inp.q, inp.k, inp.v, inp.seq_lens, inp.scale, inp.k_scales,
                             inp.v_scales, ids_ref)
     assert_parity(out.cpu().numpy(), ref, f"select + gather attention chunk={chunk}")
+
+
+def _sweep_case(i):
+    rng = np.random.default_rng(7000 + i)
+    S = int(rng.integers(1, 5))
+    T = int(rng.integers(1, 4))
+    # capacities on both sides of the 28672 keys the kernel stages in LDS
+    # (114 688 cells), not always a multiple of 4
+    Lmax = int(rng.choice([rng.integers(0, 4001), rng.integers(4001, 140001)]))
+    lens = rng.integers(0, Lmax + 3, size=S).astype(np.int32)
+    B = int(rng.integers(1, 3001))
+    ties = bool(rng.random() < 0.4)
+    return S, T, Lmax, lens, B, ties
+
+
+@pytest.mark.parametrize("i", range(48))
+def test_select_random_shapes(i):
+    """Seeded random (S, T, capacity, lengths, budget, ties) combinations,
+    bit-exact against the oracle."""
+    S, T, Lmax, lens, B, ties = _sweep_case(i)
+    print(f"[gpu] select sweep {i}: S={S} T={T} Lmax={Lmax} lens={lens.tolist()} B={B} "
+          f"ties={ties}", flush=True)
+    bs = make_block_scores(S, T, Lmax, seed=7000 + i, ties=ties)
+    check(bs, lens, T, Lmax, B)

@@ -136,3 +136,28 @@ def test_tq_step_replays_under_graph_capture():
         one()
         torch.cuda.synchronize()
         assert torch.equal(step.out, eager)
+
+
+def _sweep_case(i):
+    rng = np.random.default_rng(8000 + i)
+    S = int(rng.integers(1, 5))
+    T = int(rng.integers(1, 4))
+    Hk = int(rng.integers(1, 5))
+    G = int(rng.integers(1, 13))
+    D = int(rng.choice([64, 128]))
+    Lmax = int(rng.integers(0, 801))
+    lens = [int(x) for x in rng.integers(0, Lmax + 3, size=S)]
+    chunk = 0 if rng.random() < 0.4 else int(rng.integers(1, 301))
+    return S, T, Hk, G, D, Lmax, lens, chunk
+
+
+@pytest.mark.parametrize("i", range(32))
+def test_tq_random_shapes(i):
+    """Seeded random shapes (1-4 sequences, 1-3 causal tokens, 1-4 KV heads,
+    groups of 1-12, head dim 64/128, lengths 0 to past the capacity, automatic
+    or odd splits) against the oracle."""
+    S, T, Hk, G, D, Lmax, lens, chunk = _sweep_case(i)
+    print(f"[gpu] tq sweep {i}: S={S} T={T} Hk={Hk} G={G} D={D} Lmax={Lmax} lens={lens} "
+          f"chunk={chunk}", flush=True)
+    inp = make_tq_case(S, T, G * Hk, Hk, D, Lmax, lens, seed=8000 + i)
+    assert_parity(run_tq(inp, chunk), oracle(inp), f"tq sweep {i}")
