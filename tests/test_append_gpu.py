@@ -97,3 +97,20 @@ def test_append_then_attend():
     rk, rv, rks, rvs = AR.append_i8(kn, vn, pos, inp.k, inp.v, inp.k_scales, inp.v_scales)
     ref = DR.gqa_decode_ref(inp.q, rk, rv, inp.seq_lens, inp.scale, rks, rvs)
     assert_parity(out.cpu().numpy(), ref, "append then attend")
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_append_random_shapes(i):
+    """Seeded random (S, Tn, Hk, D, capacity, positions) combinations, with
+    positions that start before the cache, inside it, and run past its end;
+    bit-exact against the oracle on every cache row."""
+    rng = np.random.default_rng(6000 + i)
+    S = int(rng.integers(1, 5))
+    Tn = int(rng.integers(1, 40))
+    Hk = int(rng.integers(1, 5))
+    D = int(64 * rng.integers(1, 5))
+    Lmax = int(rng.integers(1, 120))
+    pos = [int(x) for x in rng.integers(-Tn, Lmax + 3, size=S)]
+    print(f"[gpu] append sweep {i}: S={S} Tn={Tn} Hk={Hk} D={D} Lmax={Lmax} pos={pos}",
+          flush=True)
+    check(S, Tn, Hk, D, Lmax, pos, seed=6000 + i)
