@@ -16,6 +16,8 @@ Reported (one JSON line on stdout):
   ms_per_step  wall-clock milliseconds per step
   step_us_p10_p50_p90  percentiles of single steps (attention + merge), each
                between its own pair of HIP events
+  cold_step_us_p10_p50_p90  the same for 20 steps each preceded (outside its
+               events) by a 1 GiB streaming read that evicts every cache
   roofline     the chunk kernel alone: algorithmic bytes per launch / its
                mean duration from HIP events on its stream (bursts of
                back-to-back launches), against the 8 TB/s HBM peak; `traffic` is HBM bytes per launch measured
@@ -521,6 +523,30 @@ def main():
     torch.cuda.synchronize()
     step_us = np.array([a.elapsed_time(b) * 1e3 for a, b in sev])
 
+    # cold steps: a 1 GiB scratch buffer is read between steps (outside the
+    # events), so neither the L2s nor the 256 MB last-level cache hold
+    # anything of the step's inputs or partials.  A read, not a write: a
+    # written buffer would leave up to 256 MB of dirty lines whose write-back
+    # then competes with the step's reads.
+    ncold = 20
+    scratch = torch.zeros(1 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.empty(512, dtype=torch.int32, device=dev)
+    flush = lambda: gq.gqa_bench_stream_read(scratch.data_ptr(), scratch.numel(), sink.data_ptr(),
+                                             512, stream.cuda_stream)
+    for _ in range(2):
+        flush()
+    cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(ncold)]
+    torch.cuda.synchronize()
+    for i in range(ncold):
+        flush()
+        cev[i][0].record(stream)
+        one(i)
+        cev[i][1].record(stream)
+    torch.cuda.synchronize()
+    cold_us = np.array([a.elapsed_time(b) * 1e3 for a, b in cev])
+    del scratch
+
     achieved = step_bytes / attn_mean_s / 1e9
     traffic = load_traffic(args.workload)
     sr_gbs, sr_wg, sr_bytes = stream_read_rate(step_bytes, dev)
@@ -535,6 +561,8 @@ def main():
         "ms_per_step": round(ms_per_step, 5),
         "us_per_step": round(ms_per_step * 1e3, 2),
         "step_us_p10_p50_p90": [round(float(np.percentile(step_us, q)), 2) for q in (10, 50, 90)],
+        "cold_step_us_p10_p50_p90": [round(float(np.percentile(cold_us, q)), 2)
+                                     for q in (10, 50, 90)],
         "pct_of_hbm_peak": round(100 * step_bytes / (wall / K) / 1e9 / HBM_PEAK_GBS, 2),
         "higher_is_better": True,
         "scaling": "weak",
