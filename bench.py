@@ -135,8 +135,20 @@ def cpu_baseline(inp, budget_s: float = 12.0):
         reps += 1
         if total_t > 3 * budget_s:
             break
+    host = {"cpu_count": os.cpu_count(), "numpy": np.__version__}
+    try:
+        with open("/proc/cpuinfo") as f:
+            host["cpu_model"] = next((ln.split(":", 1)[1].strip() for ln in f
+                                      if ln.startswith("model name")), None)
+    except OSError:
+        pass
+    try:
+        blas = np.__config__.show(mode="dicts")["Build Dependencies"]["blas"]
+        host["blas"] = f"{blas.get('name')} {blas.get('version')}"
+    except Exception:
+        pass
     return {"value": round(total_b / total_t / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "host": host,
             "sample": f"{reps} run(s) of the fp64 oracle over the first {nseq} of {S} sequences "
                       f"({total_b} KV bytes, {total_t:.1f} s); numpy + OpenBLAS"}
 
