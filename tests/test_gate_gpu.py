@@ -114,3 +114,31 @@ def test_gated_equals_ungated_times_sigmoid_on_device():
     torch.cuda.synchronize()
     expect = plain.cpu().numpy().astype(np.float64) * R.sigmoid(gate)
     np.testing.assert_allclose(step.out.cpu().numpy(), expect, rtol=1e-5, atol=1e-6)
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_gated_random_shapes(i):
+    """Seeded random shapes (as the attention sweep, with or without budgeted
+    ids), the gate as its own tensor or as the second half of [query | gate]
+    rows, against the gated oracle."""
+    rng = np.random.default_rng(5000 + i)
+    S, T, Hk, G = int(rng.integers(1, 6)), int(rng.integers(1, 4)), int(rng.integers(1, 4)), \
+        int(rng.integers(1, 13))
+    D = int(rng.choice([64, 128, 256]))
+    kv = "i8" if rng.random() < 0.5 else "f16"
+    Lmax = int(rng.integers(0, 500))
+    lens = [int(x) for x in rng.integers(0, Lmax + 3, size=S)]
+    budget = int(rng.integers(1, 200)) if rng.random() < 0.3 else 0
+    chunk = 0 if rng.random() < 0.5 else int(rng.integers(1, 300))
+    rows_layout = bool(rng.random() < 0.5)
+    print(f"[gpu] gated sweep {i}: S={S} T={T} Hk={Hk} G={G} D={D} kv={kv} Lmax={Lmax} "
+          f"lens={lens} budget={budget} chunk={chunk} qg_rows={rows_layout}", flush=True)
+    inp = make_case(S, T, G * Hk, Hk, D, Lmax, lens, kv=kv, budget=budget, seed=5000 + i)
+    gate = gate_values(inp.q.shape, seed=5000 + i)
+    if rows_layout:
+        gate_t = dev(np.concatenate([inp.q, gate], axis=-1))[..., D:]
+    else:
+        gate_t = dev(gate)
+    ref = R.gqa_decode_gated_ref(inp.q, inp.k, inp.v, inp.seq_lens, inp.scale, gate,
+                                 inp.k_scales, inp.v_scales, inp.ids)
+    assert_parity(run_gated(inp, gate_t, chunk), ref, f"gated sweep {i}")
