@@ -40,8 +40,12 @@ scipy.linalg.hadamard; with a zero residual norm the whole path equals plain
 softmax attention (oracle/decode_ref.py) over keys and values decoded and
 rotated back to the original basis; the QJL correction is an unbiased
 estimate of q . r for Gaussian JL projections (Monte Carlo, a property of the
-estimator, not of this code); field and bit order and the f16 halves against
-hand-built words; one cell gives its decoded value; empty windows give 0.
+estimator, not of this code); the scores, two-cell softmax weights and
+rotated-back output of hand-built cells with unequal norm * residual norm,
+written out in closed form with and without JL bits set (this pins the
+-sum(q_jl) term of the signed sum, which the estimator's mean does not see);
+field and bit order and the f16 halves against hand-built words; one cell
+gives its decoded value; empty windows give 0.
 """
 from __future__ import annotations
 

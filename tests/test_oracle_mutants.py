@@ -68,6 +68,7 @@ GATE_MUTANTS = {
 TQ_MUTANTS = {
     "jl_sign_flipped": ("signed_sum = 2.0 * pos_sum - q_jl.sum()", "signed_sum = q_jl.sum() - 2.0 * pos_sum"),
     "jl_factor_two_dropped": ("signed_sum = 2.0 * pos_sum - q_jl.sum()", "signed_sum = pos_sum - q_jl.sum()"),
+    "jl_total_dropped": ("signed_sum = 2.0 * pos_sum - q_jl.sum()", "signed_sum = 2.0 * pos_sum"),
     "residual_norm_dropped": ("correction = norm * residual_norm * float(qjl_scale) * signed_sum",
                               "correction = norm * float(qjl_scale) * signed_sum"),
     "polar_field_order_reversed": ("idx = (w[..., :, None] >> (np.uint32(2) * k)) & np.uint32(3)",

@@ -8,7 +8,8 @@ unpacking and scipy's Hadamard), which holds exactly when the residual norm
 is zero because the rotation is orthogonal; the QJL correction against the
 unbiasedness of the QJL estimator for Gaussian projections (Monte Carlo);
 the field / bit order and the f16 halves against hand-built words; one cell;
-empty windows."""
+empty windows; and the scores and two-cell softmax of hand-built cells in
+closed form, which is what pins the -sum(q_jl) term of the signed sum."""
 import math
 
 import numpy as np
@@ -164,3 +165,65 @@ def test_residual_term_moves_scores_by_the_formula_scale():
         (inp.k_norms[0, 0, 0] >> 16).astype(np.uint16).view(np.float16)))
     expect = 2.0 * n * rn * inp.qjl_scale * inp.scale * float(inp.q_jl[0, 0, 0, 11])
     assert abs((sc[1] - sc[0]) - expect) <= 1e-12 * (1 + abs(expect))
+
+
+def _words_all_fields(index: int, D: int) -> np.ndarray:
+    """D/16 polar words whose every 2-bit field holds `index`."""
+    w = 0
+    for k in range(16):
+        w |= index << (2 * k)
+    return np.full(D // 16, w, dtype=np.uint32)
+
+
+def _norm_word(norm: float, residual: float) -> np.uint32:
+    return np.uint32(int(np.float16(norm).view(np.uint16)) |
+                     (int(np.float16(residual).view(np.uint16)) << 16))
+
+
+def test_scores_and_two_cell_softmax_in_closed_form():
+    # Two cells whose polar fields all hold one index (so the polar dot is
+    # that centroid times sum(q_rot)), with unequal norm * residual norm.  With
+    # no JL bit set the page's signed sum is -sum(q_jl); with the bits of a set
+    # A set it is sum_A q_jl - sum_(not A) q_jl.  The scores, the two-cell
+    # softmax weights and the rotated-back output are written out here from
+    # those closed forms with the math module; every quantity is exact in f16.
+    D = 32
+    cent = (-0.25, -0.125, 0.125, 0.25)
+    scale, qjl_scale = 0.5, 0.0625
+    q_rot = np.array([0.25 if d % 2 == 0 else -0.125 for d in range(D)])
+    q_jl = np.array([0.5 + 0.125 * d for d in range(D)])
+    norms = [(1.0, 0.5), (0.75, 0.25)]
+    k_norms = np.array([_norm_word(*n) for n in norms], dtype=np.uint32)
+    k_polar = np.stack([_words_all_fields(3, D), _words_all_fields(1, D)])
+    setA = [0, 5, 17, 31]
+    for bits in (None, setA):
+        k_jl = np.zeros((2, 1), dtype=np.uint32)
+        if bits is not None:
+            k_jl[1, 0] = sum(1 << d for d in bits)
+        sc = R.tq_scores(q_rot, q_jl, k_polar, k_jl, k_norms, cent, qjl_scale, scale, D)
+        sum_rot, sum_jl = math.fsum(q_rot), math.fsum(q_jl)
+        sgn = [-sum_jl, -sum_jl]
+        if bits is not None:
+            in_a = math.fsum(q_jl[d] for d in bits)
+            sgn[1] = in_a - (sum_jl - in_a)
+        for c, (idx, (n, rn)) in enumerate(zip((3, 1), norms)):
+            expect = scale * (n * cent[idx] * sum_rot + n * rn * qjl_scale * sgn[c])
+            assert abs(sc[c] - expect) <= 1e-13 * (1 + abs(expect)), (bits, c, sc[c], expect)
+        # two-cell attention: weights are the logistic of the score difference,
+        # values are constant vectors vnorm * centroid, and the Sylvester
+        # Hadamard matrix maps a constant vector a * 1 to a * D * e_0
+        vnorm = (1.5, 0.5)
+        v_polar = np.stack([_words_all_fields(0, D), _words_all_fields(2, D)])
+        v_norms = np.array([np.float16(x).view(np.uint16) for x in vnorm], dtype=np.uint32)
+        signs = np.array([-1.0] + [1.0] * (D - 1))
+        out = R.tq_attend(q_rot, q_jl, k_polar, k_jl, k_norms, v_polar, v_norms, signs, cent,
+                          qjl_scale, scale, D)
+        s0 = scale * (norms[0][0] * cent[3] * sum_rot + norms[0][0] * norms[0][1] * qjl_scale * sgn[0])
+        s1 = scale * (norms[1][0] * cent[1] * sum_rot + norms[1][0] * norms[1][1] * qjl_scale * sgn[1])
+        p0 = 1.0 / (1.0 + math.exp(s1 - s0))
+        a = p0 * vnorm[0] * cent[0] + (1.0 - p0) * vnorm[1] * cent[2]
+        expect_out = np.zeros(D)
+        expect_out[0] = -a * D / math.sqrt(D)
+        np.testing.assert_allclose(out, expect_out, rtol=0, atol=1e-13)
+        # the term moves the weights: with it dropped the softmax would differ
+        assert abs(norms[0][0] * norms[0][1] - norms[1][0] * norms[1][1]) > 0.1
