@@ -177,9 +177,30 @@ def decode_attention(q, k, v, seq_lens, scale: Optional[float] = None, *, k_scal
     if scale is None:
         scale = D ** -0.5
     kv = "i8" if k.dtype == torch.int8 else "f16"
-    step = DecodeAttention(S, T, H, Hk, D, Lmax, kv, B=B, chunk=chunk, device=q.device)
+    step = _planned_step(S, T, H, Hk, D, Lmax, kv, B, chunk, q.device)
     return step(q, k, v, seq_lens, scale, k_scales, v_scales, ids, gate=gate,
                 gate_stride=gate_stride).clone()
+
+
+# Planned steps of decode_attention(), one per shape, device and split size:
+# a repeated call reuses the resolved split, the workspace and the output
+# buffer instead of planning and allocating again.  The result handed back is
+# a copy, so it stays valid when the same shape runs again.  Calls on one
+# device share a plan's buffers, so they must be ordered (one stream, or
+# synchronised) as any reuse of a torch buffer must.
+_PLANS: "dict" = {}
+_PLANS_MAX = 16
+
+
+def _planned_step(S, T, H, Hk, D, Lmax, kv, B, chunk, device):
+    key = (S, T, H, Hk, D, Lmax, kv, B, int(chunk), str(device))
+    step = _PLANS.get(key)
+    if step is None:
+        if len(_PLANS) >= _PLANS_MAX:
+            _PLANS.pop(next(iter(_PLANS)))
+        step = _PLANS[key] = DecodeAttention(S, T, H, Hk, D, Lmax, kv, B=B, chunk=chunk,
+                                             device=device)
+    return step
 
 
 def select_ids(block_scores, seq_lens, B: int, out=None, Lmax: Optional[int] = None):

@@ -17,8 +17,12 @@
 //        from HBM into registers (lane: one cell, 8 dims per k-step), B = the
 //        query rows (registers, loaded once).  q is fp32; it is split into
 //        f16 hi + lo (hi = f16(q), lo = f16(q - hi)) and both halves are
-//        multiplied, so the product keeps ~22 bits of q.  f16 K and int8 K
-//        are exact in f16.  int8 K: one accumulator per 64-element group,
+//        multiplied, so the product keeps ~22 bits of q.  Before the split
+//        each query row is multiplied by a power of two that puts its largest
+//        |q * scale * log2 e| in [2^13, 2^15): the hi part is then a normal
+//        f16 for every element that matters, whatever the range of q, and
+//        the row's scores are multiplied back by the inverse power (exact).
+//        f16 K and int8 K are exact in f16.  int8 K: one accumulator per 64-element group,
 //        multiplied by that group's f16 scale after the dot (qsa2.metal,
 //        qsa_attn3: raw int8 dot per group, then the scale).
 //   softmax  online, per query row, base 2 (q carries scale * log2 e): the
@@ -34,6 +38,15 @@
 //        B = V read from LDS with ds_read_b64_tr_b16 / _b8, which deliver the
 //        cell-major fragments out of the row-major tile.  P is split hi + lo
 //        like q.  int8 V: the per-(cell, group) scale is folded into P.
+//        The f16 hi + lo pair resolves values only down to f16's subnormal
+//        step (2^-24), while the softmax sum l keeps every weight in fp32, so
+//        P is kept near the top of f16's range instead of near 1: f16 V takes
+//        p = 2^(s - m + 7) <= 2^15; int8 V folds a per-wave power of two 2^E
+//        into the staged scales, E set from the largest V-scale exponent seen
+//        so far, so that p * scale * 2^E <= 2^15 (the accumulators are
+//        rescaled, rarely, when a larger scale arrives).  The partial is
+//        written in the same units: (o, m - 7, l) or (o, m - E, l * 2^E),
+//        which is the same partial for the merge.
 //
 // V tiles are staged per wave in LDS with 16-byte chunks XOR-swizzled per
 // row so that both the row-major writes and the transposed reads are free of
@@ -66,11 +79,12 @@ __device__ __forceinline__ half8 i8x8_to_half8(uint32_t w0, uint32_t w1) {
   return __builtin_bit_cast(half8, r);
 }
 
-// Largest magnitude of the f16 values packed in w exceeds 255 (or is not
-// finite).
-__device__ __forceinline__ bool f16x2_above_255(uint32_t w) {
+// Largest f16 exponent field among the f16 values packed in w (their
+// magnitudes are below 2^(field - 14)).
+__device__ __forceinline__ uint32_t f16x2_max_expfield(uint32_t w) {
   const uint32_t a = w & 0x7fff7fffu;
-  return (a & 0xffffu) > 0x5bf8u || (a >> 16) > 0x5bf8u;   // 0x5bf8 = 255.0
+  const uint32_t lo = a & 0xffffu, hi = a >> 16;
+  return (lo > hi ? lo : hi) >> 10;
 }
 
 template <int D, bool I8>
@@ -120,7 +134,7 @@ struct AttnLds {
   static constexpr int VT = NW * G::TC * G::RBY;         // per-wave V tiles (and K tiles)
   static constexpr int BUF2 = NW / 2 * RB * D * 4;       // two-stage cross-wave combine buffers
   static constexpr int QB = NRB * G::KS * 2 * 64 * 16;   // query B operands, hi and lo
-  static constexpr int SC = I8 ? NW * 2 * G::TC * G::NG * 2 : 0;  // per-wave K/V scales
+  static constexpr int SC = I8 ? NW * 2 * G::NG * G::TC * 4 : 0;  // per-wave K/V scales (fp32)
   static constexpr int ML = NW * RB * 2 * 4;             // per-wave (m, l)
   static constexpr int IDSB = kMaxIdsChunk * 4;          // most the split's cell ids take
   static constexpr int CAP = 160 * 1024;                 // LDS of one compute unit
@@ -208,7 +222,7 @@ __global__ __launch_bounds__(64 * NW, (attn_occupancy<D, I8, NRB>())) void attn_
   // overlaps the sequence-length read and the first tile's K/V requests. ----
   constexpr int QSLOTS = NRB * G::KS * 64;
   constexpr int QPT = QSLOTS / NT;                // slots per thread
-  constexpr bool QPRE = QSLOTS % NT == 0 && QPT <= 4;
+  constexpr bool QPRE = QSLOTS % NT == 0 && QPT <= 8;
   auto q_load = [&](int slot, float4& u0, float4& u1) {
     const int ln = slot & 63, kks = slot >> 6;
     const int ks = kks % G::KS, k = kks / G::KS;
@@ -223,13 +237,46 @@ __global__ __launch_bounds__(64 * NW, (attn_occupancy<D, I8, NRB>())) void attn_
     u0 = *reinterpret_cast<const float4*>(qrow);
     u1 = *reinterpret_cast<const float4*>(qrow + 4);
   };
+  // Per-row max |q| of the block.  A lane's slots all belong to its rows
+  // 16k + lr; each wave reduces its slots in registers (qmx).  A one-wave
+  // workgroup of one row block then has its rows' maxima in registers;
+  // otherwise they meet in LDS, qred[wave][row] (the (m, l) area, unused
+  // until the epilogue).
+  constexpr bool QREG = NW == 1 && NRB == 1;
+  float* qred = reinterpret_cast<float*>(smem + L::MAIN + L::QB + L::SC);
+  float qmx[NRB];
+  auto row_max = [&](int row) -> float {
+    if constexpr (QREG) {
+      (void)row;
+      return qmx[0];
+    } else {
+      float m = qred[row];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) m = fmaxf(m, qred[w * RB + row]);
+      return m;
+    }
+  };
+#pragma unroll
+  for (int k = 0; k < NRB; ++k) qmx[k] = 0.f;
+  // max |q| of a slot's eight elements, over the four lane groups that hold
+  // the same row (wave-wide: every lane of the wave passes a slot)
+  auto q_note = [&](int slot, const float4& u0, const float4& u1) {
+    const int kb = (slot >> 6) / G::KS;
+    float m = fmaxf(fmaxf(fmaxf(fabsf(u0.x), fabsf(u0.y)), fmaxf(fabsf(u0.z), fabsf(u0.w))),
+                    fmaxf(fmaxf(fabsf(u1.x), fabsf(u1.y)), fmaxf(fabsf(u1.z), fabsf(u1.w))));
+    m = max_x32(max_x16(m));
+#pragma unroll
+    for (int k = 0; k < NRB; ++k) qmx[k] = (kb == k) ? fmaxf(qmx[k], m) : qmx[k];
+  };
   auto q_store = [&](int slot, const float4& u0, const float4& u1) {
     const int ln = slot & 63, kks = slot >> 6;
-    const int r = r0 + 16 * (kks / G::KS) + (ln & 15);
-    const bool real = r < a.R;
+    const int row = 16 * (kks / G::KS) + (ln & 15);
+    const bool real = r0 + row < a.R;
+    float rs_unused;
+    const float f = q_row_factor(row_max(row), a.qmant, a.qexp, &rs_unused);
     float x[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = real ? x[e] * a.qscale : 0.f;
+    for (int e = 0; e < 8; ++e) x[e] = real ? x[e] * f : 0.f;
     half8 hi, lo;
     split_hi_lo(x, hi, lo);
     u32x4* qlds = reinterpret_cast<u32x4*>(smem + L::MAIN);
@@ -275,7 +322,8 @@ __global__ __launch_bounds__(64 * NW, (attn_occupancy<D, I8, NRB>())) void attn_
   uint8_t* vt = smem + wave * TC * RBY;                       // this wave's V tile
   uint8_t* kt = smem + L::VT + wave * TC * RBY;               // this wave's K tile (L::KL)
   u32x4* qlds = reinterpret_cast<u32x4*>(smem + L::MAIN);
-  uint16_t* scl = reinterpret_cast<uint16_t*>(smem + L::MAIN + L::QB) + wave * 2 * TC * G::NG;
+  // int8: this wave's K scales [NG][TC] then V scales [NG][TC], fp32
+  float* sclf = reinterpret_cast<float*>(smem + L::MAIN + L::QB) + wave * 2 * G::NG * TC;
   float* mls = reinterpret_cast<float*>(smem + L::MAIN + L::QB + L::SC);
 
   int lim[NRB];                                  // visible limit of this lane's rows
@@ -334,11 +382,30 @@ __global__ __launch_bounds__(64 * NW, (attn_occupancy<D, I8, NRB>())) void attn_
     u32x2 ks, vs;
   };
   // Lazy rescaling: a row's reference max moves only when a tile's max
-  // exceeds it by more than kTau (base-2 units), so p <= 2^kTau.  With int8
-  // V, P' = p * (V scale) must stay in f16 range: a tile holding a V scale
-  // above 255 tracks the exact max instead (tau 0, p <= 1).
+  // exceeds it by more than kTau (base-2 units), so 2^(s - m) <= 2^kTau.
   constexpr float kTau = 8.0f;
-  float tau = kTau;
+  // f16 V: the weights are p = 2^(s - m + kPShift) <= 2^15, near the top of
+  // f16's range, so the f16 hi + lo pair resolves them down to 2^-31 of the
+  // row's largest weight.
+  constexpr float kPShift = 7.0f;
+  // int8 V: the staged V scales carry a factor 2^(21 - vexp), vexp = the
+  // largest f16 exponent field of the V scales this wave has seen (scales
+  // below 2^(vexp - 14)), so p * scale * 2^(21 - vexp) < 2^15.  vexp only
+  // grows; when it does, the accumulators are rescaled by vf = 2^(old - new)
+  // together with the next softmax correction.
+  int vexp = 0;
+  float vf = 1.0f;
+
+  f32x4 O[NRB][G::NB];
+  float m_run[NRB], l_run[NRB];
+  float rs[NRB];                                 // score factor of this lane's rows 16k+lr
+#pragma unroll
+  for (int k = 0; k < NRB; ++k) {
+    m_run[k] = -INFINITY;
+    l_run[k] = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < G::NB; ++nb) O[k][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   auto issue_k = [&](int ts, KRegs& R) {
     if constexpr (L::KL) {       // whole rows, as V
@@ -390,32 +457,30 @@ __global__ __launch_bounds__(64 * NW, (attn_occupancy<D, I8, NRB>())) void attn_
         *reinterpret_cast<u32x4*>(kt + G::lds_offk(rr, lane % G::CH)) = RK.k[u];
     }
     if constexpr (I8) {
-      bool big = f16x2_above_255(R.vs[0]);
-      if constexpr (G::NG == 4) big = big || f16x2_above_255(R.vs[1]);
-      tau = __any(big) ? 0.0f : kTau;
-      // lanes 0-31 store the K scales of cells 0-31, lanes 32-63 the V scales
-      uint16_t* dst = scl + (lane >> 5) * TC * G::NG + (lane & 31) * G::NG;
-      const u32x2 sv = lane < 32 ? R.ks : R.vs;
+      // every lane holds the scales of cell lane % 32
+      int ef = (int)f16x2_max_expfield(R.vs[0]);
       if constexpr (G::NG == 4) {
-        *reinterpret_cast<u32x2*>(dst) = sv;
-      } else if constexpr (G::NG == 2) {
-        *reinterpret_cast<uint32_t*>(dst) = sv[0];
-      } else {
-        *dst = (uint16_t)sv[0];
+        const int e1 = (int)f16x2_max_expfield(R.vs[1]);
+        ef = ef > e1 ? ef : e1;
+      }
+      if (__any(ef > vexp)) {                    // a larger V scale: fewer guard bits
+        const int vn = wave_max_u5(ef);
+        vf = __builtin_amdgcn_ldexpf(vf, vexp - vn);
+        vexp = vn;
+      }
+      // lanes 0-31 store the K scales of cells 0-31, lanes 32-63 the V
+      // scales times 2^(21 - vexp), both as fp32, group-major
+      const float fac = lane < 32 ? 1.0f : __builtin_amdgcn_ldexpf(1.0f, 21 - vexp);
+      const u32x2 sv = lane < 32 ? R.ks : R.vs;
+      float* dst = sclf + (lane >> 5) * G::NG * TC + (lane & 31);
+#pragma unroll
+      for (int gi = 0; gi < G::NG; ++gi) {
+        const uint16_t h = (uint16_t)(sv[gi >> 1] >> (16 * (gi & 1)));
+        dst[gi * TC] = (float)__builtin_bit_cast(_Float16, h) * fac;
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   };
-
-  f32x4 O[NRB][G::NB];
-  float m_run[NRB], l_run[NRB];
-#pragma unroll
-  for (int k = 0; k < NRB; ++k) {
-    m_run[k] = -INFINITY;
-    l_run[k] = 0.f;
-#pragma unroll
-    for (int nb = 0; nb < G::NB; ++nb) O[k][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
 
   // K operand fragment of lane (lr, lb) for cell block cb, 16-byte chunk
   // lb + 4j of the row: dims 8lb + 32j .. +7 (f16) or 16lb + 64j .. +15 (int8)
@@ -473,11 +538,9 @@ __global__ __launch_bounds__(64 * NW, (attn_occupancy<D, I8, NRB>())) void attn_
             C = mfma16(k1[cb], qh1, C);
             C = mfma16(k1[cb], ql1, C);
             // K scales of this lane's four output cells 16cb+4lb+i, group gi
-            const uint16_t* ks_l = scl + (16 * cb + 4 * lb) * G::NG + gi;
+            const f32x4 ksv = *reinterpret_cast<const f32x4*>(sclf + gi * TC + 16 * cb + 4 * lb);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              S[cb][k][i] = __builtin_fmaf(C[i], (float)__builtin_bit_cast(_Float16, ks_l[i * G::NG]),
-                                           S[cb][k][i]);
+            for (int i = 0; i < 4; ++i) S[cb][k][i] = __builtin_fmaf(C[i], ksv[i], S[cb][k][i]);
           }
         }
       }
@@ -503,30 +566,33 @@ __global__ __launch_bounds__(64 * NW, (attn_occupancy<D, I8, NRB>())) void attn_
           for (int i = 0; i < 4; ++i)
             if (ts + 16 * cb + 4 * lb + i >= lim[k]) x[4 * cb + i] = -INFINITY;
       }
+      // x holds the scores of the normalised query row: the score is x * rs
       float tmax = x[0];
 #pragma unroll
       for (int e = 1; e < 8; ++e) tmax = fmaxf(tmax, x[e]);
-      tmax = max_x32(max_x16(tmax));
+      tmax = max_x32(max_x16(tmax)) * rs[k];
       // The reference max m_run moves only when this tile's max exceeds it
-      // by more than tau (always on a row's first visible cell); the
+      // by more than kTau (always on a row's first visible cell); the
       // accumulators are rescaled only then.  exp2 of the reference offset is
       // exact math: (o, m, l) stays a valid partial for any reference m.
       const float mold = m_run[k];
-      const bool bump = tmax > mold + tau;
+      const bool bump = tmax > mold + kTau;
       const float mnew = bump ? tmax : mold;
       const float corr = bump && mold != -INFINITY ? __builtin_amdgcn_exp2f(mold - mnew) : 1.0f;
+      const float mref = I8 ? mnew : mnew - kPShift;
       float psum = 0.f;
       if (edge) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float pe = (x[e] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x[e] - mnew);
+          const float pe =
+              (x[e] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], rs[k], -mref));
           pr[k][e] = pe;
           psum += pe;
         }
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float pe = __builtin_amdgcn_exp2f(x[e] - mnew);
+          const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], rs[k], -mref));
           pr[k][e] = pe;
           psum += pe;
         }
@@ -535,16 +601,18 @@ __global__ __launch_bounds__(64 * NW, (attn_occupancy<D, I8, NRB>())) void attn_
       l_run[k] = l_run[k] * corr + psum;
       m_run[k] = mnew;
       // rescale the accumulator rows 16k+4lb+i by their row's correction
-      if (__any(corr != 1.0f)) {
+      // (int8: times the pending V-exponent factor)
+      if (__any(corr != 1.0f) || (I8 && vf != 1.0f)) {
         float cf[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) cf[i] = __shfl(corr, 4 * lb + i, 64);
+        for (int i = 0; i < 4; ++i) cf[i] = __shfl(corr, 4 * lb + i, 64) * (I8 ? vf : 1.0f);
 #pragma unroll
         for (int nb = 0; nb < G::NB; ++nb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) O[k][nb][i] *= cf[i];
       }
     }
+    if constexpr (I8) vf = 1.0f;
 
     // ---- PV ----
     const int lam = lane & 15;
@@ -581,17 +649,20 @@ __global__ __launch_bounds__(64 * NW, (attn_occupancy<D, I8, NRB>())) void attn_
       // cell(j) and bytes 16nb + 8h .. +7; result lane i gets 8 cells of dim i.
       const int j = lam >> 1, h = lam & 1;
       const int rr = (j < 4) ? 4 * lb + j : 16 + 4 * lb + (j - 4);
-      const uint16_t* vs_l = scl + TC * G::NG;
+      const float* vs_l = sclf + G::NG * TC;
 #pragma unroll
       for (int gi = 0; gi < G::NG; ++gi) {
+        // V scales (times 2^(21 - vexp)) of cells 4lb..4lb+3 and 16+4lb..16+4lb+3
+        const f32x4 va = *reinterpret_cast<const f32x4*>(vs_l + gi * TC + 4 * lb);
+        const f32x4 vb = *reinterpret_cast<const f32x4*>(vs_l + gi * TC + 16 + 4 * lb);
         half8 phi[NRB], plo[NRB];
 #pragma unroll
         for (int k = 0; k < NRB; ++k) {
           float pv[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int cell = (e < 4) ? 4 * lb + e : 16 + 4 * lb + (e - 4);
-            pv[e] = pr[k][e] * (float)__builtin_bit_cast(_Float16, vs_l[cell * G::NG + gi]);
+          for (int e = 0; e < 4; ++e) {
+            pv[e] = pr[k][e] * va[e];
+            pv[4 + e] = pr[k][4 + e] * vb[e];
           }
           split_hi_lo(pv, phi[k], plo[k]);
         }
@@ -627,6 +698,25 @@ __global__ __launch_bounds__(64 * NW, (attn_occupancy<D, I8, NRB>())) void attn_
     issue_k(ts, RK);
     if constexpr (QPRE) {
 #pragma unroll
+      for (int i = 0; i < QPT; ++i) q_note(tid + NT * i, qv[i][0], qv[i][1]);
+    } else {
+      for (int slot = tid; slot < QSLOTS; slot += NT) {
+        float4 u0, u1;
+        q_load(slot, u0, u1);
+        q_note(slot, u0, u1);
+      }
+    }
+    if constexpr (!QREG) {
+      if (lane < 16) {
+#pragma unroll
+        for (int k = 0; k < NRB; ++k) qred[wave * RB + 16 * k + lane] = qmx[k];
+      }
+      __syncthreads();   // row maxima of q staged
+    }
+#pragma unroll
+    for (int k = 0; k < NRB; ++k) (void)q_row_factor(row_max(16 * k + lr), a.qmant, a.qexp, &rs[k]);
+    if constexpr (QPRE) {
+#pragma unroll
       for (int i = 0; i < QPT; ++i) q_store(tid + NT * i, qv[i][0], qv[i][1]);
     } else {
       for (int slot = tid; slot < QSLOTS; slot += NT) {
@@ -651,6 +741,19 @@ __global__ __launch_bounds__(64 * NW, (attn_occupancy<D, I8, NRB>())) void attn_
       }
       softmax_pv(ts, S);
       ts = tn;
+    }
+  }
+
+  // The accumulators hold o * 2^kPShift (f16 V, whose l carries the same
+  // factor) or o * 2^(21 - vexp) (int8 V, whose l does not): written as the
+  // equivalent partial (o * 2^x, m - x, l * 2^x).
+#pragma unroll
+  for (int k = 0; k < NRB; ++k) {
+    if constexpr (I8) {
+      m_run[k] -= (float)(21 - vexp);
+      l_run[k] = __builtin_amdgcn_ldexpf(l_run[k], 21 - vexp);
+    } else {
+      m_run[k] -= kPShift;
     }
   }
 

@@ -32,6 +32,12 @@
 // accumulators, B = decoded value fragments: a lane needs one dim of eight
 // cells, so the tile's V index words are staged in LDS transposed
 // ([word][cell]) and each lane extracts its 2-bit field from eight words.
+// Ranges, as in the dense kernel: each q_rot and q_jl row is multiplied by a
+// power of two that puts its largest element in [2^13, 2^14) before its f16
+// hi + lo split (the scores take the inverse power), and p * vnorm carries a
+// per-wave factor 2^(21 - vexp), vexp the largest f16 exponent field of the
+// value norms seen so far, so that it stays below 2^15 and far above f16's
+// subnormal step; the partial is written as (o, m - x, l * 2^x).
 #pragma once
 
 #include "common.h"
@@ -191,16 +197,22 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
         u32x2{f(u & 1) | (f((u >> 1) & 1) << 16), f((u >> 2) & 1) | (f((u >> 3) & 1) << 16)};
   }
 
-  // ---- query operands: q_rot and q_jl rows as f16 hi + lo, and each row's
-  // sum of q_jl (fp32) ----
-  for (int slot = tid; slot < 2 * NRB * KS * 64; slot += NT) {
-    const int which = slot / (NRB * KS * 64);    // 0: q_rot, 1: q_jl
+  // ---- query operands: q_rot and q_jl rows as f16 hi + lo, each row
+  // normalised by a power of two (its max |element| per wave first, into
+  // qred[which][wave][row], the (m, l) area that the epilogue uses later),
+  // and each row's sum of q_jl (fp32) ----
+  float* qred = mls;
+  auto q_slot = [&](int slot, int& which, int& kks, int& row, float (&x)[8]) {
+    which = slot / (NRB * KS * 64);              // 0: q_rot, 1: q_jl
     const int sl = slot % (NRB * KS * 64);
-    const int ln = sl & 63, kks = sl >> 6;
+    const int ln = sl & 63;
+    kks = sl >> 6;
     const int ks = kks % KS, k = kks / KS;
-    const int r = r0 + 16 * k + (ln & 15);
+    row = 16 * k + (ln & 15);
+    const int r = r0 + row;
     const int d0 = (ln >> 4) * (D / 4) + 8 * ks;
-    float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = 0.f;
     if (r < a.R) {
       const float* src = (which ? a.q_jl : a.q_rot) +
                          ((size_t)(s * a.T + row_t(r)) * a.H + row_h(r)) * D + d0;
@@ -209,12 +221,58 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
       x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w;
       x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
     }
-    half8 hi, lo;
-    split_hi_lo(x, hi, lo);
-    const int base = ((which * NRB * KS + kks) * 2) * 64;
-    qlds[base + ln] = __builtin_bit_cast(u32x4, hi);
-    qlds[base + 64 + ln] = __builtin_bit_cast(u32x4, lo);
+  };
+  auto row_max = [&](int which, int row) -> float {
+    float m = qred[which * NW * RB + row];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) m = fmaxf(m, qred[(which * NW + w) * RB + row]);
+    return m;
+  };
+  {
+    float qmx[2][NRB];
+#pragma unroll
+    for (int w2 = 0; w2 < 2; ++w2)
+#pragma unroll
+      for (int k = 0; k < NRB; ++k) qmx[w2][k] = 0.f;
+    // every lane of a wave passes the same number of slots (wave-wide reductions)
+    for (int slot = tid; slot < 2 * NRB * KS * 64; slot += NT) {
+      int which, kks, row;
+      float x[8];
+      q_slot(slot, which, kks, row, x);
+      float m = fabsf(x[0]);
+#pragma unroll
+      for (int e = 1; e < 8; ++e) m = fmaxf(m, fabsf(x[e]));
+      m = max_x32(max_x16(m));
+      const int kb = kks / KS;
+#pragma unroll
+      for (int w2 = 0; w2 < 2; ++w2)
+#pragma unroll
+        for (int k = 0; k < NRB; ++k)
+          qmx[w2][k] = (which == w2 && kb == k) ? fmaxf(qmx[w2][k], m) : qmx[w2][k];
+    }
+    if (lane < 16) {
+#pragma unroll
+      for (int w2 = 0; w2 < 2; ++w2)
+#pragma unroll
+        for (int k = 0; k < NRB; ++k) qred[(w2 * NW + wave) * RB + 16 * k + lane] = qmx[w2][k];
+    }
   }
+  auto q_stage = [&]() {
+    for (int slot = tid; slot < 2 * NRB * KS * 64; slot += NT) {
+      int which, kks, row;
+      float x[8];
+      q_slot(slot, which, kks, row, x);
+      float rs_unused;
+      const float f = q_row_factor(row_max(which, row), 0.5f, 1, &rs_unused);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] *= f;
+      half8 hi, lo;
+      split_hi_lo(x, hi, lo);
+      const int base = ((which * NRB * KS + kks) * 2) * 64;
+      qlds[base + (slot & 63)] = __builtin_bit_cast(u32x4, hi);
+      qlds[base + 64 + (slot & 63)] = __builtin_bit_cast(u32x4, lo);
+    }
+  };
   if (tid < RB) {
     const int r = r0 + tid;
     float t = 0.f;
@@ -289,16 +347,23 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
   };
 
   constexpr float kTau = 8.0f;
-  float tau = kTau;
+  // p * vnorm carries 2^(21 - vexp), vexp = the largest f16 exponent field
+  // of the value norms this wave has seen (norms below 2^(vexp - 14)), so
+  // that it stays below 2^8 * 2^7 = 2^15; when vexp grows the accumulators
+  // are rescaled by vf with the next softmax correction.
+  int vexp = 0;
+  float vf = 1.0f;
   auto stage = [&](const VRegs& R) {
     const int cell = lane >> 1;
 #pragma unroll
     for (int j = 0; j < VW / 2; ++j) vtw[((lane & 1) * (VW / 2) + j) * TC + cell] = R.pol[j];
     nrm[lane] = R.nrm;
-    // p * vnorm must stay in f16 range: a tile with a value norm above 255
-    // tracks the exact max (tau 0, p <= 1)
-    const bool big = lane >= 32 && (R.nrm & 0x7fffu) > 0x5bf8u;
-    tau = __any(big) ? 0.0f : kTau;
+    const int ef = lane >= 32 ? (int)((R.nrm & 0x7fffu) >> 10) : 0;
+    if (__any(ef > vexp)) {
+      const int vn = wave_max_u5(ef);
+      vf = __builtin_amdgcn_ldexpf(vf, vexp - vn);
+      vexp = vn;
+    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   };
 
@@ -312,6 +377,7 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
     for (int nb = 0; nb < NB; ++nb) O[k][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   float qs[NRB];                                 // sum of q_jl of this lane's rows 16k + lr
+  float ra[NRB], rb2[NRB];                       // score factors of the normalised q_rot, 2 x q_jl
 
   // ---- QK: S[cb][k][i] = score (base 2) of cell ts+16cb+4lb+i for row 16k+lr ----
   auto qk = [&](const KRegs& R, f32x4 (&S)[2][NRB]) {
@@ -361,7 +427,8 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
         const float rq = f16hi(kn[i]) * a.qjl_scale;
 #pragma unroll
         for (int k = 0; k < NRB; ++k)
-          S[cb][k][i] = n * __builtin_fmaf(rq, __builtin_fmaf(2.f, Sj[cb][k][i], -qs[k]), Sp[cb][k][i]);
+          S[cb][k][i] =
+              n * __builtin_fmaf(rq, __builtin_fmaf(rb2[k], Sj[cb][k][i], -qs[k]), Sp[cb][k][i] * ra[k]);
       }
     }
   };
@@ -389,7 +456,7 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
       for (int e = 1; e < 8; ++e) tmax = fmaxf(tmax, x[e]);
       tmax = max_x32(max_x16(tmax));
       const float mold = m_run[k];
-      const bool bump = tmax > mold + tau;
+      const bool bump = tmax > mold + kTau;
       const float mnew = bump ? tmax : mold;
       const float corr = bump && mold != -INFINITY ? __builtin_amdgcn_exp2f(mold - mnew) : 1.0f;
       float psum = 0.f;
@@ -402,26 +469,28 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
       psum = sum_x32(sum_x16(psum));
       l_run[k] = l_run[k] * corr + psum;
       m_run[k] = mnew;
-      if (__any(corr != 1.0f)) {
+      if (__any(corr != 1.0f) || vf != 1.0f) {
         float cf[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) cf[i] = __shfl(corr, 4 * lb + i, 64);
+        for (int i = 0; i < 4; ++i) cf[i] = __shfl(corr, 4 * lb + i, 64) * vf;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) O[k][nb][i] *= cf[i];
       }
     }
+    vf = 1.0f;
     // P' = p * vnorm of each of this lane's eight cells (A operand k = 8 lb + e)
     half8 phi[NRB], plo[NRB];
     {
       const u32x4 va = *reinterpret_cast<const u32x4*>(nrm + TC + 4 * lb);
       const u32x4 vb = *reinterpret_cast<const u32x4*>(nrm + TC + 16 + 4 * lb);
+      const float fac = __builtin_amdgcn_ldexpf(1.0f, 21 - vexp);
       float vn[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        vn[i] = f16lo(va[i]);
-        vn[4 + i] = f16lo(vb[i]);
+        vn[i] = f16lo(va[i]) * fac;
+        vn[4 + i] = f16lo(vb[i]) * fac;
       }
 #pragma unroll
       for (int k = 0; k < NRB; ++k) {
@@ -466,9 +535,16 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
     int ts = c0 + TC * wave;
     issue_v(ts, RV);
     issue_k(ts, RK);
-    __syncthreads();                             // query operands and sums staged
+    __syncthreads();                             // row maxima, q_jl sums and tables staged
 #pragma unroll
-    for (int k = 0; k < NRB; ++k) qs[k] = qsum[16 * k + lr];
+    for (int k = 0; k < NRB; ++k) {
+      qs[k] = qsum[16 * k + lr];
+      (void)q_row_factor(row_max(0, 16 * k + lr), 0.5f, 1, &ra[k]);
+      (void)q_row_factor(row_max(1, 16 * k + lr), 0.5f, 1, &rb2[k]);
+      rb2[k] *= 2.0f;
+    }
+    q_stage();
+    __syncthreads();                             // query operands staged
 #pragma unroll 1
     while (ts < cend) {
       const int tn = ts + NW * TC;
@@ -480,6 +556,14 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
       softmax_pv(ts, S);
       ts = tn;
     }
+  }
+
+  // The accumulators hold o * 2^(21 - vexp): written as the equivalent
+  // partial (o * 2^x, m - x, l * 2^x).
+#pragma unroll
+  for (int k = 0; k < NRB; ++k) {
+    m_run[k] -= (float)(21 - vexp);
+    l_run[k] = __builtin_amdgcn_ldexpf(l_run[k], 21 - vexp);
   }
 
   // ---- combine the four waves into one partial per query row (as the

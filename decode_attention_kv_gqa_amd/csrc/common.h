@@ -40,6 +40,8 @@ struct AttnArgs {
   int S, T, Lmax, B, H, Hk, G, R, nrb, P, chunk;
   int seq_fast;      // 1: grid order with the sequence varying fastest, else the KV head
   float qscale;      // scale * log2(e)
+  float qmant;       // qscale = qmant * 2^qexp, |qmant| in [0.5, 1) (0 when qscale is 0)
+  int qexp;
 };
 
 // Arguments of the merge kernel: one output row per workgroup, P partial

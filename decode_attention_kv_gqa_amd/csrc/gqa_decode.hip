@@ -127,6 +127,7 @@ int attn_common(bool i8, const float* q, const void* k, const void* v, const uin
   a.S = S; a.T = T; a.Lmax = Lmax; a.B = sh.B; a.H = H; a.Hk = Hk; a.G = H / Hk;
   a.R = gqa::rows_per_unit(sh); a.nrb = gqa::row_blocks(sh); a.P = (int)P; a.chunk = chunk;
   a.qscale = scale * kLog2e;
+  a.qmant = std::frexp(a.qscale, &a.qexp);
   // int8 rows: the KV heads of a sequence share an XCD (sequence-fastest
   // grid) when S is a multiple of the 8 XCDs.  Measured on one MI355X: int8
   // 32K 49.1 -> 48.6 us, budgeted int8 13.9 -> 13.5 us.  f16 keeps the

@@ -31,6 +31,34 @@ __device__ __forceinline__ void split_hi_lo(const float (&x)[8], half8& hi, half
   }
 }
 
+// Power of two that normalises a query row: with m = max |q| of the row and
+// qscale = qmant * 2^qexp, q * qmant * 2^(15 - e) with e = exponent of m
+// (clamped to [-100, 128] so the factor stays a normal float) has its largest
+// magnitude in [2^13, 2^15).  Returns that factor; *rs = 2^(e + qexp - 15)
+// turns a score of normalised rows back into q . k * qscale (exponent
+// clamped to the normal range; only rows with max |q * qscale| below
+// ~2^-111, whose scores are ~0 anyway, reach the clamp).
+__device__ __forceinline__ float q_row_factor(float m, float qmant, int qexp, float* rs) {
+  int e = __builtin_amdgcn_frexp_expf(m);
+  e = e < -100 ? -100 : (e > 128 ? 128 : e);
+  int es = e + qexp - 15;
+  es = es < -126 ? -126 : (es > 127 ? 127 : es);
+  *rs = __builtin_amdgcn_ldexpf(1.0f, es);
+  return __builtin_amdgcn_ldexpf(qmant, 15 - e);
+}
+
+// Largest value of a 5-bit field (0..31) over the wave, by bisection on
+// ballots: five wave votes, no LDS round trip.
+__device__ __forceinline__ int wave_max_u5(int x) {
+  int m = 0;
+#pragma unroll
+  for (int b = 4; b >= 0; --b) {
+    const int c = m | (1 << b);
+    if (__any(x >= c)) m = c;
+  }
+  return m;
+}
+
 // Butterfly steps across lane distance 16 and 32 of a wave64 with the gfx950
 // permlane swaps (VALU, no LDS round trip).  With both operands equal,
 // permlane16_swap returns (rows 0,0,2,2) and (rows 1,1,3,3) of x, and

@@ -51,6 +51,17 @@
  *    distinct cells of the token's window [0, L_t).  An id outside [0, Lmax)
  *    is clamped into range, so a bad id yields a wrong row, never an
  *    out-of-bounds read.
+ *  - Numerics: scores, softmax sums and outputs are fp32; the products run
+ *    on the matrix cores as f16 hi + lo operand pairs (~22 bits each).  A
+ *    query row may hold any finite fp32 values: it is scaled by a power of
+ *    two before its split (scores are scaled back exactly), so rows with
+ *    max |q * scale| from ~1e-33 up to where q . k overflows fp32 keep full
+ *    precision.  The softmax weights are held near the top of f16's range
+ *    (int8 V: with a power of two taken from the largest V scale), so a
+ *    weight is resolved to within ~2^-31 of the largest weight of its wave's
+ *    cells: over the ~1e4-1e5 cells a wave streams, the output's error
+ *    stays below ~1e-4 of max |V| even when most of the softmax mass sits in
+ *    cells far below the maximum.
  */
 #ifndef GQA_DECODE_H
 #define GQA_DECODE_H

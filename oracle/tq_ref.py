@@ -54,7 +54,8 @@ import math
 import numpy as np
 
 __all__ = ["hadamard", "f16_halves", "polar_indices", "jl_bits", "decode_rot",
-           "tq_scores", "tq_attend", "tq_decode_ref"]
+           "decode_keys", "scores_decoded", "tq_scores", "attend_decoded", "tq_attend",
+           "tq_decode_ref"]
 
 
 def hadamard(D: int) -> np.ndarray:
@@ -98,18 +99,43 @@ def decode_rot(polar_words: np.ndarray, norms: np.ndarray, centroids, D: int) ->
     return norms[:, None] * c[polar_indices(polar_words, D)]
 
 
-def tq_scores(q_rot, q_jl, k_polar, k_jl, k_norms, centroids, qjl_scale, scale, D):
-    """Scores of one query row against n cells: q_rot, q_jl [D] float;
-    k_polar [n][D/16], k_jl [n][D/32], k_norms [n] uint32 -> [n] fp64."""
-    q_rot = np.asarray(q_rot, dtype=np.float64)
-    q_jl = np.asarray(q_jl, dtype=np.float64)
+def decode_keys(k_polar, k_jl, k_norms, centroids, D):
+    """The per-cell key terms of n cells: centroid values c[idx_k] [n][D],
+    JL bits [n][D] (0 / 1), norm [n] and residual norm [n], fp64."""
     c = np.asarray(centroids, dtype=np.float64)
     norm, residual_norm = f16_halves(k_norms)
-    polar_dot = c[polar_indices(k_polar, D)] @ q_rot
-    pos_sum = jl_bits(k_jl, D) @ q_jl
+    return c[polar_indices(k_polar, D)], jl_bits(k_jl, D), norm, residual_norm
+
+
+def scores_decoded(q_rot, q_jl, kc, jl, norm, residual_norm, qjl_scale, scale):
+    """Scores of one query row against cells given by their decoded key terms
+    (decode_keys) -> [n] fp64."""
+    q_rot = np.asarray(q_rot, dtype=np.float64)
+    q_jl = np.asarray(q_jl, dtype=np.float64)
+    polar_dot = kc @ q_rot
+    pos_sum = jl @ q_jl
     signed_sum = 2.0 * pos_sum - q_jl.sum()
     correction = norm * residual_norm * float(qjl_scale) * signed_sum
     return (polar_dot * norm + correction) * float(scale)
+
+
+def tq_scores(q_rot, q_jl, k_polar, k_jl, k_norms, centroids, qjl_scale, scale, D):
+    """Scores of one query row against n cells: q_rot, q_jl [D] float;
+    k_polar [n][D/16], k_jl [n][D/32], k_norms [n] uint32 -> [n] fp64."""
+    return scores_decoded(q_rot, q_jl, *decode_keys(k_polar, k_jl, k_norms, centroids, D),
+                          qjl_scale, scale)
+
+
+def attend_decoded(q_rot, q_jl, keys, v_rot, signs, qjl_scale, scale, D) -> np.ndarray:
+    """One query row over cells given by decoded key terms (decode_keys) and
+    rotated-basis values v_rot [n][D] -> output [D] fp64 in the original basis."""
+    if v_rot.shape[0] == 0:
+        return np.zeros(D, dtype=np.float64)
+    sc = scores_decoded(q_rot, q_jl, *keys, qjl_scale, scale)
+    w = np.exp(sc - sc.max())
+    p = w / w.sum()
+    acc = p @ v_rot
+    return np.asarray(signs, dtype=np.float64) * (hadamard(D) @ acc) / math.sqrt(D)
 
 
 def tq_attend(q_rot, q_jl, k_polar, k_jl, k_norms, v_polar, v_norms, signs, centroids,
@@ -118,36 +144,51 @@ def tq_attend(q_rot, q_jl, k_polar, k_jl, k_norms, v_polar, v_norms, signs, cent
     n = k_norms.shape[0]
     if n == 0:
         return np.zeros(D, dtype=np.float64)
-    sc = tq_scores(q_rot, q_jl, k_polar, k_jl, k_norms, centroids, qjl_scale, scale, D)
-    w = np.exp(sc - sc.max())
-    p = w / w.sum()
     vnorm, _ = f16_halves(v_norms)
-    acc = p @ decode_rot(v_polar, vnorm, centroids, D)
-    return np.asarray(signs, dtype=np.float64) * (hadamard(D) @ acc) / math.sqrt(D)
+    return attend_decoded(q_rot, q_jl, decode_keys(k_polar, k_jl, k_norms, centroids, D),
+                          decode_rot(v_polar, vnorm, centroids, D), signs, qjl_scale, scale, D)
 
 
 def tq_decode_ref(q_rot, q_jl, k_polar, k_jl, k_norms, v_polar, v_norms, seq_lens, signs,
                   centroids, qjl_scale, scale, rows=None) -> np.ndarray:
     """Decode output [S][T][H][D] fp64 (or, with rows = [(s, t, h), ...], the
     listed rows stacked [len(rows)][D]).  q_rot, q_jl [S][T][H][D]; caches as
-    in the module docstring; seq_lens [S]; signs [D]; centroids [4]."""
+    in the module docstring; seq_lens [S]; signs [D]; centroids [4].  The
+    cells of each (sequence, KV head) are decoded once, over the window of
+    its last token; every row reads the prefix its window covers."""
     S, T, H, D = q_rot.shape
     _, Hk, Lmax, _ = k_polar.shape
     G = H // Hk
 
-    def one(s, t, h):
-        g = h // G
+    def window(s, t):
         Lt = int(seq_lens[s]) - (T - 1 - t)
-        Lt = max(0, min(Lt, Lmax))
-        return tq_attend(q_rot[s, t, h], q_jl[s, t, h], k_polar[s, g, :Lt], k_jl[s, g, :Lt],
-                         k_norms[s, g, :Lt], v_polar[s, g, :Lt], v_norms[s, g, :Lt], signs,
-                         centroids, qjl_scale, scale, D)
+        return max(0, min(Lt, Lmax))
+
+    def slab(s, g):
+        L = window(s, T - 1)
+        keys = decode_keys(k_polar[s, g, :L], k_jl[s, g, :L], k_norms[s, g, :L], centroids, D)
+        vnorm, _ = f16_halves(v_norms[s, g, :L])
+        return keys, decode_rot(v_polar[s, g, :L], vnorm, centroids, D)
+
+    def one(s, t, h, keys, v_rot):
+        Lt = window(s, t)
+        return attend_decoded(q_rot[s, t, h], q_jl[s, t, h], tuple(x[:Lt] for x in keys),
+                              v_rot[:Lt], signs, qjl_scale, scale, D)
 
     if rows is not None:
-        return np.stack([one(s, t, h) for (s, t, h) in rows]) if rows else np.zeros((0, D))
+        rows = list(rows)
+        res = np.zeros((len(rows), D), dtype=np.float64)
+        for sg in sorted({(s, h // G) for (s, _, h) in rows}):
+            keys, v_rot = slab(*sg)
+            for i, (s, t, h) in enumerate(rows):
+                if (s, h // G) == sg:
+                    res[i] = one(s, t, h, keys, v_rot)
+        return res
     out = np.zeros((S, T, H, D), dtype=np.float64)
     for s in range(S):
-        for t in range(T):
-            for h in range(H):
-                out[s, t, h] = one(s, t, h)
+        for g in range(Hk):
+            keys, v_rot = slab(s, g)
+            for t in range(T):
+                for h in range(g * G, (g + 1) * G):
+                    out[s, t, h] = one(s, t, h, keys, v_rot)
     return out

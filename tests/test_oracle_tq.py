@@ -227,3 +227,31 @@ def test_scores_and_two_cell_softmax_in_closed_form():
         np.testing.assert_allclose(out, expect_out, rtol=0, atol=1e-13)
         # the term moves the weights: with it dropped the softmax would differ
         assert abs(norms[0][0] * norms[0][1] - norms[1][0] * norms[1][1]) > 0.1
+
+
+def test_decode_ref_rows_equal_single_row_attention_over_their_windows():
+    # tq_decode_ref decodes each (sequence, KV head) once over the last
+    # token's window; every row must equal tq_attend over exactly the cells
+    # of its own causal window, sliced here by hand
+    S, T, H, Hk, D, Lmax = 2, 3, 6, 2, 64, 40
+    inp = make_tq_case(S, T, H, Hk, D, Lmax, [40, 2], seed=21)
+    full = R.tq_decode_ref(inp.q_rot, inp.q_jl, inp.k_polar, inp.k_jl, inp.k_norms, inp.v_polar,
+                           inp.v_norms, inp.seq_lens, inp.signs, inp.centroids, inp.qjl_scale,
+                           inp.scale)
+    G = H // Hk
+    for s in range(S):
+        for t in range(T):
+            n = max(0, min(int(inp.seq_lens[s]) - (T - 1 - t), Lmax))
+            for h in range(H):
+                g = h // G
+                one = R.tq_attend(inp.q_rot[s, t, h], inp.q_jl[s, t, h], inp.k_polar[s, g, :n],
+                                  inp.k_jl[s, g, :n], inp.k_norms[s, g, :n], inp.v_polar[s, g, :n],
+                                  inp.v_norms[s, g, :n], inp.signs, inp.centroids, inp.qjl_scale,
+                                  inp.scale, D)
+                assert np.array_equal(full[s, t, h], one), (s, t, h)
+    rows = [(1, 0, 5), (0, 2, 0), (1, 2, 3)]
+    part = R.tq_decode_ref(inp.q_rot, inp.q_jl, inp.k_polar, inp.k_jl, inp.k_norms, inp.v_polar,
+                           inp.v_norms, inp.seq_lens, inp.signs, inp.centroids, inp.qjl_scale,
+                           inp.scale, rows=rows)
+    for i, (s, t, h) in enumerate(rows):
+        assert np.array_equal(part[i], full[s, t, h])

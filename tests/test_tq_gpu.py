@@ -83,19 +83,13 @@ def test_tq_large_value_norms_and_sharp_scores():
     assert_parity(run_tq(inp, 64), oracle(inp), "tq big value norms, scale 4")
 
 
-def test_tq_full_size_sampled_rows():
-    name = "tq_128k"
-    w = TQ_WORKLOADS[name]
-    inp = make_tq_inputs(name)
+def test_tq_full_size():
+    # the bench's TurboQuant workload in its launch configuration, every
+    # output element (the oracle decodes each (sequence, KV head) once)
+    inp = make_tq_inputs("tq_128k")
     got = run_tq(inp, 0)
-    assert np.isfinite(got).all()
-    S, T, H, _ = inp.q_rot.shape
-    rng = np.random.default_rng(w["index"])
-    rows = sorted({(int(rng.integers(S)), 0, int(rng.integers(H))) for _ in range(10)}
-                  | {(0, 0, 0), (S - 1, 0, H - 1)})
-    ref = oracle(inp, rows=rows)
-    g = np.stack([got[s, t, h] for (s, t, h) in rows])
-    assert_parity(g, ref, f"{name} sampled rows")
+    print("[gpu] tq_128k: oracle", flush=True)
+    assert_parity(got, oracle(inp), "tq_128k")
 
 
 def test_tq_step_replays_under_graph_capture():
