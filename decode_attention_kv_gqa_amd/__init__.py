@@ -14,15 +14,15 @@ from . import _lib
 from ._lib import (GqaDecodeError, gqa_decode_attn_f16, gqa_decode_attn_i8, gqa_decode_merge,
                    gqa_decode_merge_gated, gqa_decode_attn_tq, gqa_decode_merge_tq,
                    gqa_decode_select_ids, gqa_decode_append_i8,
-                   gqa_decode_part_bytes, gqa_decode_auto_chunk, gqa_bench_stream_read,
-                   strerror)
+                   gqa_decode_part_bytes, gqa_decode_auto_chunk, gqa_decode_step_static,
+                   gqa_bench_stream_read, strerror)
 
 __all__ = ["decode_attention", "DecodeAttention", "GqaDecodeError", "gqa_decode_attn_f16",
            "gqa_decode_attn_i8", "gqa_decode_merge", "gqa_decode_merge_gated",
            "gqa_decode_attn_tq", "gqa_decode_merge_tq", "TqDecodeAttention", "tq_decode_attention",
            "gqa_decode_select_ids", "select_ids",
            "gqa_decode_append_i8", "append_i8",
-           "gqa_decode_part_bytes",
+           "gqa_decode_part_bytes", "gqa_decode_step_static",
            "gqa_decode_auto_chunk", "gqa_bench_stream_read", "strerror"]
 
 

@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libgqa_decode.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = ["gqa_decode.hip", "merge.hip", "select.hip", "append.hip", "tq.hip", "plan.cpp",
-           "stream_read.hip"]
+           "stream_read.hip", "static_step.hip"]
 
 # Every HIP translation unit is built for gfx950 only, with packed-fp32 VALU
 # instructions disabled (the compiler otherwise forms v_pk_*_f32 from plain

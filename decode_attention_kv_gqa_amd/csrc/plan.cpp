@@ -78,6 +78,9 @@ const char* gqa_decode_strerror(int code) {
     case GQA_ERR_BUDGET: return "ids given with a budget B < 1";
     case GQA_ERR_CHUNK: return "chunk must be >= 1 (pass the resolved chunk to the merge)";
     case GQA_ERR_WORKSPACE: return "partial workspace smaller than gqa_decode_part_bytes()";
+    case GQA_ERR_STATIC_LIMIT:
+      return "the partials exceed the static buffer of gqa_decode_step_static "
+             "(GQA_STATIC_PART_BYTES); use a larger chunk or the workspace calls";
     default: return code > 0 ? "HIP launch error (hipError_t)" : "unknown error";
   }
 }

@@ -82,8 +82,13 @@ enum {
   GQA_ERR_BUDGET = -5,     /* ids given with B < 1                               */
   GQA_ERR_CHUNK = -6,      /* chunk < 1 in the merge, or a split wider than 2^31
                               bytes of K rows (chunk * Hk * D * elem >= 2^31)    */
-  GQA_ERR_WORKSPACE = -7   /* part_bytes < gqa_decode_part_bytes(...)            */
+  GQA_ERR_WORKSPACE = -7,  /* part_bytes < gqa_decode_part_bytes(...)            */
+  GQA_ERR_STATIC_LIMIT = -8 /* gqa_decode_step_static: the partials need more than
+                              GQA_STATIC_PART_BYTES                              */
 };
+
+/* Size of the static partial buffer of gqa_decode_step_static, per GPU. */
+#define GQA_STATIC_PART_BYTES ((size_t)16 << 20)
 
 /* Partial workspace size in bytes for one attention call: one partial
  * (D unnormalised output floats + running max + running sum) per query row
@@ -243,6 +248,34 @@ int gqa_decode_select_ids(const float *block_scores, const int32_t *seq_lens, in
 int gqa_decode_append_i8(const float *k_new, const float *v_new, const int32_t *pos,
                          int8_t *k, int8_t *v, uint16_t *k_scales, uint16_t *v_scales,
                          int S, int Tn, int Lmax, int Hk, int D, void *stream);
+
+/* For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): one whole decode step,
+ * gqa_decode_attn_f16 / gqa_decode_attn_i8 followed by gqa_decode_merge,
+ * with the partials in a buffer the library owns instead of a caller
+ * workspace.  The buffer is a static device array of GQA_STATIC_PART_BYTES
+ * (16 MiB), one per GPU the library runs on, held until the process ends;
+ * the call allocates and frees nothing.  Its address on the current device
+ * is looked up on the first call with that device current (the only call
+ * that may block), so a caller that captures the step should make one call
+ * first.
+ *   kv_kind   0: k, v are f16 bit patterns (k_scales, v_scales unused)
+ *             1: k, v are int8 codes with f16 k_scales, v_scales
+ *   out       [S][T][H][D] float32, as gqa_decode_merge
+ *   chunk     <= 0 selects gqa_decode_auto_chunk(..., kv_kind)
+ * Other arguments as gqa_decode_attn_f16 / _i8.  Every call on one GPU uses
+ * that GPU's one buffer: calls that overlap on a GPU (other streams, other
+ * threads, without ordering between them) race and give wrong results.
+ * Each call writes every partial slot it then reads, so nothing needs
+ * clearing between calls.  Errors: those of the two calls it makes, and
+ * GQA_ERR_STATIC_LIMIT, before anything is enqueued, when
+ * gqa_decode_part_bytes(S, T, Lmax, B or 0, H, D, resolved chunk) exceeds
+ * GQA_STATIC_PART_BYTES (use a larger chunk, or the workspace calls). */
+int gqa_decode_step_static(const float *q, const void *k, const void *v,
+                           const uint16_t *k_scales, const uint16_t *v_scales,
+                           const int32_t *ids, const int32_t *seq_lens, float *out,
+                           int S, int T, int Lmax, int B, int H, int Hk, int D,
+                           float scale, int chunk, int kv_kind, void *stream);
 
 /* Static text for a return code. */
 const char *gqa_decode_strerror(int code);

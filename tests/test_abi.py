@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_strerror_covers_codes():
-    for c in range(0, -8, -1):
+    for c in range(0, -9, -1):
         assert gq.strerror(c) not in ("", "unknown error")
     assert gq.strerror(-99) == "unknown error"
     assert "HIP" in gq.strerror(98)
@@ -220,3 +220,27 @@ def test_select_wrapper_checks_capacity_against_scores():
     bs = torch.zeros(1, 1, 2)                      # Lmax // 4 + 1 = 2: Lmax in 4..7
     with pytest.raises(ValueError, match="Lmax"):
         gq.select_ids(bs, torch.ones(1, dtype=torch.int32), 8, Lmax=8)
+
+
+def test_static_step_rejects_before_any_gpu_call():
+    # shape errors, and partials beyond the static buffer, are refused on the
+    # host before the buffer's device address is looked up
+    def step(**kw):
+        a = dict(S=8, T=1, Lmax=32768, B=0, H=24, Hk=2, D=256, chunk=0, kv_kind=1, ids=None)
+        a.update(kw)
+        return gq.gqa_decode_step_static(FAKE, FAKE, FAKE, FAKE, FAKE, a["ids"], FAKE, FAKE,
+                                         a["S"], a["T"], a["Lmax"], a["B"], a["H"], a["Hk"],
+                                         a["D"], 0.0625, a["chunk"], a["kv_kind"], 0)
+    # 8 x 24 rows x 1024 splits of 32 cells x 258 floats = 203 MB > 16 MiB
+    assert step(chunk=32) == _lib.GQA_ERR_STATIC_LIMIT
+    assert gq.gqa_decode_part_bytes(8, 1, 32768, 0, 24, 256, 32) > _lib.GQA_STATIC_PART_BYTES
+    assert step(kv_kind=2) == _lib.GQA_ERR_SHAPE
+    assert step(H=25) == _lib.GQA_ERR_GROUP
+    assert step(D=96) == _lib.GQA_ERR_HEAD_DIM
+    assert step(ids=FAKE, B=0) == _lib.GQA_ERR_BUDGET
+    for i in (0, 6, 7):                          # q, seq_lens, out
+        args = [FAKE] * 8
+        args[i] = None
+        assert gq.gqa_decode_step_static(*args, 1, 1, 16, 0, 8, 2, 64, 0.125, 0, 0, 0) == \
+            _lib.GQA_ERR_NULL
+    assert "static" in gq.strerror(_lib.GQA_ERR_STATIC_LIMIT)
