@@ -28,6 +28,12 @@ Reported (one JSON line on stdout):
                machine's practical read ceiling, and the kernel's fraction
                of it
   cpu_baseline the fp64 oracle on the host cores over a bounded sample
+  workloads    every other configuration (tiny f16, f16 batch, budgeted
+               int8, f16 multi-query causal, or int8 32K when another one is
+               named), measured the same way with at most 100 steps and no
+               CPU baseline: step and chunk-kernel us, their fractions of
+               8 TB/s and of the streaming read, HBM traffic over the
+               algorithmic bytes (from profiles/)
 To keep back-to-back steps from hitting the 256 MB last-level cache, the
 inputs are replicated and the steps rotate through the copies, so every step
 reads K/V that were last touched several hundred MB earlier.
@@ -398,72 +404,43 @@ def bench_tq(args):
         "roofline": roof}), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="i8_32k")
-    ap.add_argument("--chunk", type=int, default=-1, help="cells per split (-1: the workload's)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--gate", action="store_true",
-                    help="merge with the output gate (gate rows interleaved with the query)")
-    ap.add_argument("--copies", type=int, default=0, help="input replicas to rotate through")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run a plain 1 GiB device copy 5 times (HBM counter calibration)")
-    args = ap.parse_args()
-    if args.copy_calibration:
-        copy_calibration()
-        return
-
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the decode-attention path here is a single-GPU "
-              "kernel pair (multi-GPU sharding is a design note, not built); run with --gpus 1.",
-              file=sys.stderr)
-        sys.exit(2)
-
+def measure_attention(name, chunk, steps, warmup, dev, gate=False, copies=0, cold=20,
+                      with_stream_read=True):
+    """One attention workload on the GPU: seeded inputs resident in HBM (as
+    many copies as keep successive steps out of the last-level cache), K
+    steps of attention + merge back to back (wall clock bracketed by device
+    synchronisation), the chunk kernel alone from HIP events around bursts of
+    back-to-back launches on its stream, single steps between their own
+    events, cold steps, and a plain streaming read of the same bytes.
+    Returns (result dict, inputs)."""
     import numpy as np
     import torch
     import decode_attention_kv_gqa_amd as gq
-    from workloads import (WORKLOADS, SELECT_WORKLOADS, APPEND_WORKLOADS, TQ_WORKLOADS,
-                           make_inputs, kv_bytes)
+    from workloads import WORKLOADS, make_inputs, kv_bytes
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    if args.workload in SELECT_WORKLOADS:
-        bench_select(args)
-        return
-    if args.workload in APPEND_WORKLOADS:
-        bench_append(args)
-        return
-    if args.workload in TQ_WORKLOADS:
-        bench_tq(args)
-        return
-    w = WORKLOADS[args.workload]
-    chunk = w.chunk if args.chunk < 0 else args.chunk
+    w = WORKLOADS[name]
+    chunk = w.chunk if chunk < 0 else chunk
     t_gen = time.perf_counter()
-    inp = make_inputs(args.workload)
+    inp = make_inputs(name)
     step_bytes = kv_bytes(inp)
     sh = inp.shape
-    print(f"[bench] {args.workload}: inputs drawn in {time.perf_counter() - t_gen:.1f} s, "
+    print(f"[bench] {name}: inputs drawn in {time.perf_counter() - t_gen:.1f} s, "
           f"{step_bytes} KV bytes/step", file=sys.stderr, flush=True)
 
     # resident footprint of one copy of the inputs
     foot = sum(x.nbytes for x in (inp.q, inp.k, inp.v, inp.k_scales, inp.v_scales, inp.ids)
                if x is not None)
-    copies = args.copies or max(2, min(8, math.ceil(3 * LLC_BYTES / foot) + 1))
-    dev = torch.device("cuda:0")
+    copies = copies or max(2, min(8, math.ceil(3 * LLC_BYTES / foot) + 1))
     d = lambda x: None if x is None else torch.from_numpy(x).to(dev)
     sets = []
     gate_np = None
-    if args.gate:
+    if gate:
         # the output gate as the second half of [query | gate] rows
         gate_np = np.random.default_rng(2000 + w.index).standard_normal(inp.q.shape).astype(np.float32)
     for _ in range(copies):
         x = dict(q=d(inp.q), k=d(inp.k), v=d(inp.v), seq_lens=d(inp.seq_lens),
                  k_scales=d(inp.k_scales), v_scales=d(inp.v_scales), ids=d(inp.ids), gate=None)
-        if args.gate:
+        if gate:
             full = d(np.concatenate([inp.q, gate_np], axis=-1))
             x["q"] = full[..., :sh["D"]].contiguous()
             x["gate"] = full[..., sh["D"]:]
@@ -472,14 +449,18 @@ def main():
                               B=sh["B"], chunk=chunk, device=dev)
     stream = torch.cuda.current_stream()
 
-    def one(i):
+    def attn(i):
         x = sets[i % copies]
         step.attn(x["q"], x["k"], x["v"], x["seq_lens"], inp.scale, x["k_scales"], x["v_scales"],
                   x["ids"])
+
+    def one(i):
+        x = sets[i % copies]
+        attn(i)
         step.merge(x["seq_lens"], x["ids"], gate=x["gate"],
                    gate_stride=None if x["gate"] is None else 2 * sh["D"])
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         one(i)
     torch.cuda.synchronize()
     # The GPU's clocks take a few milliseconds of sustained load to settle; a
@@ -489,19 +470,18 @@ def main():
     t_w = time.perf_counter()
     while time.perf_counter() - t_w < SETTLE_S:
         for i in range(10):
-            one(args.warmup + extra + i)
+            one(warmup + extra + i)
         extra += 10
         torch.cuda.synchronize()
 
     # timed region: K steps back to back, wall clock bracketed by synchronisation
-    K = args.steps
+    K = steps
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
         one(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_per_step = wall / K * 1e3
 
     # chunk-kernel duration from HIP events on the launch stream, in a pass of
     # its own after the timed steps: bursts of back-to-back chunk-kernel
@@ -514,9 +494,7 @@ def main():
     for b in range(bursts):
         evs[b][0].record(stream)
         for i in range(per):
-            x = sets[(b * per + i) % copies]
-            step.attn(x["q"], x["k"], x["v"], x["seq_lens"], inp.scale, x["k_scales"],
-                      x["v_scales"], x["ids"])
+            attn(b * per + i)
         evs[b][1].record(stream)
     torch.cuda.synchronize()
     attn_ms = np.array([a.elapsed_time(b) / per for a, b in evs])
@@ -540,42 +518,121 @@ def main():
     # anything of the step's inputs or partials.  A read, not a write: a
     # written buffer would leave up to 256 MB of dirty lines whose write-back
     # then competes with the step's reads.
-    ncold = 20
-    scratch = torch.zeros(1 << 30, dtype=torch.uint8, device=dev)
-    sink = torch.empty(512, dtype=torch.int32, device=dev)
-    flush = lambda: gq.gqa_bench_stream_read(scratch.data_ptr(), scratch.numel(), sink.data_ptr(),
-                                             512, stream.cuda_stream)
-    for _ in range(2):
-        flush()
-    cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(ncold)]
-    torch.cuda.synchronize()
-    for i in range(ncold):
-        flush()
-        cev[i][0].record(stream)
-        one(i)
-        cev[i][1].record(stream)
-    torch.cuda.synchronize()
-    cold_us = np.array([a.elapsed_time(b) * 1e3 for a, b in cev])
-    del scratch
+    cold_us = None
+    if cold:
+        scratch = torch.zeros(1 << 30, dtype=torch.uint8, device=dev)
+        sink = torch.empty(512, dtype=torch.int32, device=dev)
+        flush = lambda: gq.gqa_bench_stream_read(scratch.data_ptr(), scratch.numel(),
+                                                 sink.data_ptr(), 512, stream.cuda_stream)
+        for _ in range(2):
+            flush()
+        cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(cold)]
+        torch.cuda.synchronize()
+        for i in range(cold):
+            flush()
+            cev[i][0].record(stream)
+            one(i)
+            cev[i][1].record(stream)
+        torch.cuda.synchronize()
+        cold_us = np.array([a.elapsed_time(b) * 1e3 for a, b in cev])
+        del scratch
 
     achieved = step_bytes / attn_mean_s / 1e9
-    traffic = load_traffic(args.workload)
-    sr_gbs, sr_wg, sr_bytes = stream_read_rate(step_bytes, dev)
+    traffic = load_traffic(name)
+    res = {
+        "value": round(step_bytes / (wall / K) / 1e9, 2),
+        "ms_per_step": round(wall / K * 1e3, 5),
+        "us_per_step": round(wall / K * 1e6, 2),
+        "step_us_p10_p50_p90": [round(float(np.percentile(step_us, q)), 2) for q in (10, 50, 90)],
+        "pct_of_hbm_peak": round(100 * step_bytes / (wall / K) / 1e9 / HBM_PEAK_GBS, 2),
+        "extra_warmup_steps": extra,
+        "chunk": step.chunk,
+        "kv_bytes_per_step": step_bytes,
+        "input_copies_rotated": copies,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "traffic_over_algorithmic": (round(traffic / step_bytes, 4)
+                                                  if traffic else None),
+                     "kernel": "attn_chunk",
+                     "kernel_us_mean": round(attn_mean_s * 1e6, 3),
+                     "kernel_us_burst_min_max": [round(float(attn_ms.min()) * 1e3, 3),
+                                                 round(float(attn_ms.max()) * 1e3, 3)]},
+    }
+    if cold_us is not None:
+        res["cold_step_us_p10_p50_p90"] = [round(float(np.percentile(cold_us, q)), 2)
+                                           for q in (10, 50, 90)]
+    if with_stream_read:
+        sr_gbs, sr_wg, sr_bytes = stream_read_rate(step_bytes, dev)
+        res["roofline"]["stream_read"] = {"gbs": round(sr_gbs, 2), "bytes": sr_bytes,
+                                          "workgroups": sr_wg,
+                                          "kernel_frac_of_stream_read": round(achieved / sr_gbs, 4)}
+    del sets, step
+    torch.cuda.empty_cache()
+    return res, inp
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="i8_32k")
+    ap.add_argument("--chunk", type=int, default=-1, help="cells per split (-1: the workload's)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="measure only the named workload (by default the int8 32K headline "
+                         "run also measures every other configuration, with fewer steps)")
+    ap.add_argument("--gate", action="store_true",
+                    help="merge with the output gate (gate rows interleaved with the query)")
+    ap.add_argument("--copies", type=int, default=0, help="input replicas to rotate through")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy 5 times (HBM counter calibration)")
+    args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the decode-attention path here is a single-GPU "
+              "kernel pair (multi-GPU sharding is a design note, not built); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from workloads import WORKLOADS, WORKLOAD_ORDER, SELECT_WORKLOADS, APPEND_WORKLOADS, TQ_WORKLOADS
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.workload in SELECT_WORKLOADS:
+        bench_select(args)
+        return
+    if args.workload in APPEND_WORKLOADS:
+        bench_append(args)
+        return
+    if args.workload in TQ_WORKLOADS:
+        bench_tq(args)
+        return
+    dev = torch.device("cuda:0")
+    w = WORKLOADS[args.workload]
+    m, inp = measure_attention(args.workload, args.chunk, args.steps, args.warmup, dev,
+                               gate=args.gate, copies=args.copies)
+    sh = inp.shape
     res = {
         "metric": "decode-attention effective KV HBM GB/s (% of peak) and us/step, 1 MI355X",
-        "value": round(step_bytes / (wall / K) / 1e9, 2),
+        "value": m["value"],
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "extra_warmup_steps": extra,
-        "ms_per_step": round(ms_per_step, 5),
-        "us_per_step": round(ms_per_step * 1e3, 2),
-        "step_us_p10_p50_p90": [round(float(np.percentile(step_us, q)), 2) for q in (10, 50, 90)],
-        "cold_step_us_p10_p50_p90": [round(float(np.percentile(cold_us, q)), 2)
-                                     for q in (10, 50, 90)],
-        "pct_of_hbm_peak": round(100 * step_bytes / (wall / K) / 1e9 / HBM_PEAK_GBS, 2),
+        "extra_warmup_steps": m["extra_warmup_steps"],
+        "ms_per_step": m["ms_per_step"],
+        "us_per_step": m["us_per_step"],
+        "step_us_p10_p50_p90": m["step_us_p10_p50_p90"],
+        "cold_step_us_p10_p50_p90": m["cold_step_us_p10_p50_p90"],
+        "pct_of_hbm_peak": m["pct_of_hbm_peak"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -585,23 +642,36 @@ def main():
                  else "K/V f16 N(0,1))"),
         "config": {"workload": args.workload, "S": sh["S"], "T": sh["T"], "H": sh["H"],
                    "Hk": sh["Hk"], "D": sh["D"], "Lmax": sh["Lmax"], "budget": sh["B"],
-                   "kv": inp.kv, "chunk": step.chunk, "kv_bytes_per_step": step_bytes,
-                   "input_copies_rotated": copies, "output_gate": bool(args.gate),
-                   "description": w.description},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic,
-                     "kernel": "attn_chunk",
-                     "kernel_us_mean": round(attn_mean_s * 1e6, 3),
-                     "kernel_us_burst_min_max": [round(float(attn_ms.min()) * 1e3, 3),
-                                                 round(float(attn_ms.max()) * 1e3, 3)],
-                     "stream_read": {"gbs": round(sr_gbs, 2), "bytes": sr_bytes,
-                                     "workgroups": sr_wg,
-                                     "kernel_frac_of_stream_read": round(achieved / sr_gbs, 4)}},
+                   "kv": inp.kv, "chunk": m["chunk"], "kv_bytes_per_step": m["kv_bytes_per_step"],
+                   "input_copies_rotated": m["input_copies_rotated"],
+                   "output_gate": bool(args.gate), "description": w.description},
+        "roofline": m["roofline"],
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the fp64 oracle on the host", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(inp)
+    del inp
+    if not args.no_other_workloads and not args.gate and args.chunk < 0:
+        # every other configuration, measured the same way with fewer steps
+        # (no CPU baseline); the line's value stays the named workload's
+        res["workloads"] = {}
+        for name in WORKLOAD_ORDER:
+            if name == args.workload:
+                continue
+            o, _ = measure_attention(name, -1, min(args.steps, 100), min(args.warmup, 10), dev,
+                                     cold=10)
+            r = o["roofline"]
+            res["workloads"][name] = {
+                "description": WORKLOADS[name].description, "chunk": o["chunk"],
+                "kv_bytes_per_step": o["kv_bytes_per_step"], "us_per_step": o["us_per_step"],
+                "step_us_p10_p50_p90": o["step_us_p10_p50_p90"],
+                "cold_step_us_p10_p50_p90": o["cold_step_us_p10_p50_p90"],
+                "step_GBps": o["value"], "step_frac_of_peak": round(o["value"] / HBM_PEAK_GBS, 4),
+                "kernel_us_mean": r["kernel_us_mean"], "kernel_GBps": r["achieved"],
+                "kernel_frac_of_peak": r["frac"],
+                "kernel_frac_of_stream_read": r["stream_read"]["kernel_frac_of_stream_read"],
+                "stream_read_GBps": r["stream_read"]["gbs"],
+                "traffic": r["traffic"], "traffic_over_algorithmic": r["traffic_over_algorithmic"]}
     print(json.dumps(res), flush=True)
 
 
