@@ -276,7 +276,7 @@ def test_full_size_workload(name):
     inp = make_inputs(name)
     print(f"[gpu] full-size workload {name}: oracle", flush=True)
     ref = oracle(inp)
-    chunks = [w.chunk] + ([0] if w.chunk else [])
+    chunks = [w.chunk] + ([0] if w.chunk else []) + ([32] if name == "i8_budget" else [])
     dev = to_dev(inp)
     for chunk in chunks:
         got = run_gpu(inp, chunk=chunk, dev=dev)

@@ -64,8 +64,9 @@ WORKLOADS = {
                  scale=1.0 / 16.0, chunk=0, lens="full",
                  description="int8 KV decode: 8 seqs at context 32768, 24/2 heads (group 12), hd 256"),
         Workload("i8_budget", 3, S=8, T=1, H=24, Hk=2, D=256, Lmax=65536, kv="i8",
-                 scale=1.0 / 16.0, chunk=32, lens="full", budget=2048,
-                 description="budgeted sparse int8 decode: context 65536, 2048 distinct ids per token, 32-cell chunks"),
+                 scale=1.0 / 16.0, chunk=128, lens="full", budget=2048,
+                 description="budgeted sparse int8 decode: context 65536, 2048 distinct ids per token, "
+                             "32-cell chunks, four per workgroup (one per wave), one partial per workgroup"),
         Workload("f16_mq_causal", 4, S=4, T=8, H=32, Hk=8, D=128, Lmax=131072, kv="f16",
                  scale=1.0 / math.sqrt(128.0), chunk=0, lens="full",
                  description="multi-query causal chunk: 4 seqs x 8 tokens at start 131064, context 131072, 32/8 heads, hd 128"),
