@@ -115,8 +115,9 @@ int attn_common(bool i8, const float* q, const void* k, const void* v, const uin
   if (chunk <= 0 || chunk > gqa::max_chunk(sh)) return GQA_ERR_CHUNK;
   if (ids && (int64_t)Lmax * Hk * D * (i8 ? 1 : 2) >= ((int64_t)1 << 31)) return GQA_ERR_SHAPE;
   const size_t need = gqa::part_bytes(sh, chunk);
-  if (part_bytes < need) return GQA_ERR_WORKSPACE;
   const int64_t P = gqa::num_splits(sh, chunk);
+  if (P > 0 && need == 0) return GQA_ERR_SHAPE;   // the partials would not fit any address space
+  if (part_bytes < need) return GQA_ERR_WORKSPACE;
   if (P == 0) return GQA_OK;                 // Lmax == 0: every row is empty
   if (P > 0x7fffffff) return GQA_ERR_SHAPE;
 
@@ -125,7 +126,7 @@ int attn_common(bool i8, const float* q, const void* k, const void* v, const uin
   a.part_o = part;
   a.part_ml = part + gqa::part_o_floats(sh, P);
   a.S = S; a.T = T; a.Lmax = Lmax; a.B = sh.B; a.H = H; a.Hk = Hk; a.G = H / Hk;
-  a.R = gqa::rows_per_unit(sh); a.nrb = gqa::row_blocks(sh); a.P = (int)P; a.chunk = chunk;
+  a.R = (int)gqa::rows_per_unit(sh); a.nrb = (int)gqa::row_blocks(sh); a.P = (int)P; a.chunk = chunk;
   a.qscale = scale * kLog2e;
   a.qmant = std::frexp(a.qscale, &a.qexp);
   // int8 rows: the KV heads of a sequence share an XCD (sequence-fastest

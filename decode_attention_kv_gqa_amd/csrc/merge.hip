@@ -160,6 +160,7 @@ static int merge_common(const float* part, const int32_t* seq_lens, const int32_
   if (chunk < 1) return GQA_ERR_CHUNK;
   if (gate && gate_stride < D) return GQA_ERR_SHAPE;
   const int64_t P = gqa::num_splits(sh, chunk);
+  if (P > 0 && gqa::part_bytes(sh, chunk) == 0) return GQA_ERR_SHAPE;   // no workspace could hold it
   MergeArgs a;
   a.part_o = part;
   a.part_ml = part + gqa::part_o_floats(sh, P);

@@ -1,6 +1,8 @@
 // Host-side argument checks and launch planning (no HIP calls).
 #include "plan.h"
 
+#include <cstdint>
+
 namespace gqa {
 
 int check_shape(const Shape& s) {
@@ -8,10 +10,14 @@ int check_shape(const Shape& s) {
   if (s.H % s.Hk != 0) return GQA_ERR_GROUP;
   if (s.D != 64 && s.D != 128 && s.D != 256) return GQA_ERR_HEAD_DIM;
   if (s.ids && s.B < 1) return GQA_ERR_BUDGET;
+  // The merge grid has one workgroup per output row: S * T * H of them
+  // (bounded in two steps, each product below 2^62).
+  const int64_t st = (int64_t)s.S * s.T;
+  if (st > 0x7fffffff || st * s.H > 0x7fffffff) return GQA_ERR_SHAPE;
   // The attention grid is 1-D: S * Hk * row blocks (* T when gathering)
-  // workgroups per split; the merge grid has one workgroup per output row.
+  // workgroups per split (below S * T * H + S * Hk, so no overflow here).
   const int64_t units = (int64_t)s.S * s.Hk * row_blocks(s) * (s.ids ? s.T : 1);
-  if (units > 0x7fffffff || (int64_t)s.S * s.T * s.H > 0x7fffffff) return GQA_ERR_SHAPE;
+  if (units > 0x7fffffff) return GQA_ERR_SHAPE;
   return GQA_OK;
 }
 
@@ -48,8 +54,13 @@ int auto_chunk(const Shape& s) {
 
 size_t part_bytes(const Shape& s, int chunk) {
   if (chunk < 1 || check_shape(s) != GQA_OK) return 0;
-  int64_t P = num_splits(s, chunk);
-  return (size_t)s.S * s.T * s.H * (size_t)P * (size_t)(s.D + 2) * sizeof(float);
+  const int64_t P = num_splits(s, chunk);
+  // rows (< 2^31) x splits (< 2^31) x (D + 2) floats: computed in 128 bits;
+  // a workspace beyond half the address space is refused (0), never wrapped
+  const unsigned __int128 b = (unsigned __int128)((int64_t)s.S * s.T * s.H) * (uint64_t)P *
+                              (uint64_t)(s.D + 2) * sizeof(float);
+  if (b > (unsigned __int128)(SIZE_MAX >> 1)) return 0;
+  return (size_t)b;
 }
 
 }  // namespace gqa

@@ -33,20 +33,21 @@ inline int64_t num_splits(const Shape& s, int chunk) {
   return w <= 0 ? 0 : (w + chunk - 1) / chunk;
 }
 
-// Query rows served by one (sequence, KV head[, token]) unit.
-inline int rows_per_unit(const Shape& s) {
-  int G = s.H / s.Hk;
+// Query rows served by one (sequence, KV head[, token]) unit.  64-bit: the
+// shape checks use it before they have bounded G * T (check_shape then
+// guarantees S * T * H <= 2^31 - 1, so after it the value fits an int).
+inline int64_t rows_per_unit(const Shape& s) {
+  const int64_t G = s.H / s.Hk;
   return s.ids ? G : G * s.T;
 }
 
-inline int row_blocks(const Shape& s) {
-  int R = rows_per_unit(s);
-  return (R + kMaxRowsPerBlock - 1) / kMaxRowsPerBlock;
+inline int64_t row_blocks(const Shape& s) {
+  return (rows_per_unit(s) + kMaxRowsPerBlock - 1) / kMaxRowsPerBlock;
 }
 
 // Rows per block rounded up to the kernel instance (4, 8, 16 or 32).
 inline int block_rows(const Shape& s) {
-  int R = rows_per_unit(s);
+  int64_t R = rows_per_unit(s);
   if (R > kMaxRowsPerBlock) R = kMaxRowsPerBlock;
   if (R <= 4) return 4;
   if (R <= 8) return 8;

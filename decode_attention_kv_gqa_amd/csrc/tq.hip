@@ -175,8 +175,10 @@ int gqa_decode_attn_tq(const float* q_rot, const float* q_jl, const uint32_t* k_
   if (chunk <= 0) chunk = gqa::auto_chunk(sh);
   // one split of one KV head spans chunk * D/16 words in the largest region
   if (chunk <= 0 || (int64_t)chunk * (D / 16) * 4 >= ((int64_t)1 << 31)) return GQA_ERR_CHUNK;
-  if (part_bytes < gqa::part_bytes(sh, chunk)) return GQA_ERR_WORKSPACE;
+  const size_t need = gqa::part_bytes(sh, chunk);
   const int64_t P = gqa::num_splits(sh, chunk);
+  if (P > 0 && need == 0) return GQA_ERR_SHAPE;   // the partials would not fit any address space
+  if (part_bytes < need) return GQA_ERR_WORKSPACE;
   if (P == 0) return GQA_OK;
   if (P > 0x7fffffff) return GQA_ERR_SHAPE;
 
@@ -202,7 +204,7 @@ int gqa_decode_attn_tq(const float* q_rot, const float* q_jl, const uint32_t* k_
   a.qjl_scale = qjl_scale;
   a.qscale = scale * kLog2e;
   a.S = S; a.T = T; a.Lmax = Lmax; a.H = H; a.Hk = Hk; a.G = H / Hk;
-  a.R = gqa::rows_per_unit(sh); a.nrb = gqa::row_blocks(sh); a.P = (int)P; a.chunk = chunk;
+  a.R = (int)gqa::rows_per_unit(sh); a.nrb = (int)gqa::row_blocks(sh); a.P = (int)P; a.chunk = chunk;
   const int64_t nwg = P * Hk * a.nrb * S;
   if (nwg > 0x7fffffff) return GQA_ERR_SHAPE;
   const dim3 grid((unsigned)nwg);
@@ -223,6 +225,7 @@ int gqa_decode_merge_tq(const float* part, const int32_t* seq_lens, const float*
   if (D != 64 && D != 128) return GQA_ERR_HEAD_DIM;
   if (chunk < 1) return GQA_ERR_CHUNK;
   const int64_t P = gqa::num_splits(sh, chunk);
+  if (P > 0 && gqa::part_bytes(sh, chunk) == 0) return GQA_ERR_SHAPE;   // no workspace could hold it
   const size_t rows = (size_t)S * T * H;
   if (rows > 0x7fffffffu) return GQA_ERR_SHAPE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);

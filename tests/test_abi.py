@@ -244,3 +244,14 @@ def test_static_step_rejects_before_any_gpu_call():
         assert gq.gqa_decode_step_static(*args, 1, 1, 16, 0, 8, 2, 64, 0.125, 0, 0, 0) == \
             _lib.GQA_ERR_NULL
     assert "static" in gq.strerror(_lib.GQA_ERR_STATIC_LIMIT)
+
+
+def test_workspace_size_never_wraps():
+    # 2^30 output rows x 2^30 one-cell splits x 258 floats is beyond any
+    # address space: the size is refused (0) rather than wrapped modulo 2^64,
+    # and the calls refuse the shape before looking at the workspace
+    S, H, Lmax, D = 1 << 15, 1 << 15, 1 << 30, 256
+    assert gq.gqa_decode_part_bytes(S, 1, Lmax, 0, H, D, 1) == 0
+    assert gq.gqa_decode_part_bytes(S, 1, Lmax, 0, H, D, 1 << 20) > 0
+    assert attn_f16(S=S, H=H, Hk=1, Lmax=Lmax, D=D, chunk=1, part_bytes=1 << 62) == _lib.GQA_ERR_SHAPE
+    assert gq.gqa_decode_merge(FAKE, FAKE, None, FAKE, S, 1, Lmax, 0, H, D, 1, 0) == _lib.GQA_ERR_SHAPE
