@@ -163,11 +163,12 @@ struct AttnLds {
 
 // Waves per SIMD the register budget is sized for: 2, except for the
 // instances whose accumulators and operands do not fit half the register
-// file (head_dim 256 with two row blocks or f16 K, and f16 head_dim 128 with
-// two row blocks), which get the whole file instead of spilling.
+// file (head_dim 256 with two row blocks or f16 K, f16 head_dim 128 with two
+// row blocks, and every four-block instance), which get the whole file
+// (accumulation registers included) instead of spilling.
 template <int D, bool I8, int NRB>
 constexpr int attn_occupancy() {
-  return ((D == 256 && (NRB == 2 || !I8)) || (D == 128 && NRB == 2 && !I8)) ? 1 : 2;
+  return (NRB >= 4 || (D == 256 && (NRB == 2 || !I8)) || (D == 128 && NRB == 2 && !I8)) ? 1 : 2;
 }
 
 template <int D, bool I8, bool IDS, int NRB, int NW>

@@ -88,6 +88,9 @@ hipError_t launch_attn_nw(const AttnArgs& a, bool ids, int nw, dim3 grid, hipStr
 template <int D, bool I8>
 hipError_t launch_attn(const AttnArgs& a, bool ids, int nrows, int nw, dim3 grid, hipStream_t st) {
   if (nrows <= 16) return launch_attn_nw<D, I8, 1>(a, ids, nw, grid, st);
+  if constexpr (D <= 128) {
+    if (nrows > 32) return launch_attn_nw<D, I8, 4>(a, ids, nw, grid, st);
+  }
   return launch_attn_nw<D, I8, 2>(a, ids, nw, grid, st);
 }
 

@@ -13,7 +13,10 @@ namespace gqa {
 // query rows of one KV head (all G heads of the group, times the T tokens of
 // a dense window), so K/V rows are streamed once for all of them; groups
 // with more rows than this are cut into row blocks that each stream K/V.
-constexpr int kMaxRowsPerBlock = 32;
+// 64 rows (four 16-row MFMA blocks) for head_dim 64 and 128, whose
+// accumulators fit one wave per SIMD; 32 for head_dim 256 and the
+// TurboQuant kernel.
+constexpr int kMaxRowsPerBlock = 64;
 
 struct Shape {
   int S, T, Lmax, B, H, Hk, D;
@@ -21,6 +24,8 @@ struct Shape {
   bool i8;    // int8 rows with f16 group scales
   bool tq = false;   // TurboQuant-compressed cache (gqa_decode_attn_tq)
 };
+
+inline int max_rows_per_block(const Shape& s) { return (!s.tq && s.D <= 128) ? 64 : 32; }
 
 // Positions a split can cover: min(B, Lmax) with ids, else Lmax.
 inline int64_t width_cap(const Shape& s) {
@@ -42,17 +47,19 @@ inline int64_t rows_per_unit(const Shape& s) {
 }
 
 inline int64_t row_blocks(const Shape& s) {
-  return (rows_per_unit(s) + kMaxRowsPerBlock - 1) / kMaxRowsPerBlock;
+  const int m = max_rows_per_block(s);
+  return (rows_per_unit(s) + m - 1) / m;
 }
 
-// Rows per block rounded up to the kernel instance (4, 8, 16 or 32).
+// Rows per block rounded up to the kernel instance (4, 8, 16, 32 or 64).
 inline int block_rows(const Shape& s) {
   int64_t R = rows_per_unit(s);
-  if (R > kMaxRowsPerBlock) R = kMaxRowsPerBlock;
+  if (R > max_rows_per_block(s)) R = max_rows_per_block(s);
   if (R <= 4) return 4;
   if (R <= 8) return 8;
   if (R <= 16) return 16;
-  return 32;
+  if (R <= 32) return 32;
+  return 64;
 }
 
 // Largest split the kernels accept: one split's K (or V) rows of a KV head

@@ -53,9 +53,10 @@
  *    out-of-bounds read.
  *  - K/V traffic: one workgroup serves every query row of a KV head (the
  *    H / Hk heads of the group, times the T tokens of a dense window), so
- *    each K/V row is read once per split, up to 32 rows per KV head.  More
- *    rows are cut into blocks of 32 that each read the KV head's rows again
- *    (with ids: one token per block, each token's own cells).
+ *    each K/V row is read once per split, up to 64 rows per KV head for
+ *    head_dim 64 and 128 and up to 32 for head_dim 256.  More rows are cut
+ *    into blocks of that size that each read the KV head's rows again (with
+ *    ids: one token per block, each token's own cells).
  *  - Numerics: scores, softmax sums and outputs are fp32; the products run
  *    on the matrix cores as f16 hi + lo operand pairs (~22 bits each).  A
  *    query row may hold any finite fp32 values: it is scaled by a power of

@@ -37,7 +37,8 @@ static void check_shape_case(int S, int T, int Lmax, int B, int H, int Hk, int D
     return;
   }
   const i128 G = H / Hk, R = ids ? G : G * T;
-  const i128 nrb = (R + 31) / 32;
+  const i128 rows_per_block = D <= 128 ? 64 : 32;    // four 16-row blocks up to head_dim 128
+  const i128 nrb = (R + rows_per_block - 1) / rows_per_block;
   const i128 units = (i128)S * Hk * nrb * (ids ? T : 1);
   const bool grid_ok = units <= 0x7fffffff && (i128)S * T * H <= 0x7fffffff;
   CHECK((rc == GQA_OK) == grid_ok, "S=%d T=%d H=%d Hk=%d grid check rc=%d", S, T, H, Hk, rc);

@@ -281,3 +281,25 @@ def test_full_size_workload(name):
     for chunk in chunks:
         got = run_gpu(inp, chunk=chunk, dev=dev)
         assert_parity(got, ref, f"{name} chunk={chunk}")
+
+
+@pytest.mark.parametrize("kv", ["f16", "i8"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("G,T", [(8, 8), (10, 4), (16, 5)])
+def test_rows_up_to_64_per_kv_head(kv, D, G, T):
+    # 64, 40 and 80 query rows per KV head: one 64-row block (head_dim 64 and
+    # 128 serve up to 64 rows from one workgroup, so K/V rows are read once),
+    # a ragged block of 40, and two blocks for 80; one- and four-wave splits
+    inp = make_case(3, T, G * 2, 2, D, 400, [400, 2, 333], kv=kv, seed=G * 10 + T + D)
+    ref = oracle(inp)
+    for chunk in (48, 0):
+        assert_parity(run_gpu(inp, chunk=chunk), ref, f"rows={G * T} D={D} kv={kv} chunk={chunk}")
+
+
+@pytest.mark.parametrize("kv", ["f16", "i8"])
+def test_64_heads_per_kv_head_with_ids(kv):
+    # gather mode holds one token's G query heads per workgroup: G = 64
+    inp = make_case(2, 2, 64, 1, 128, 600, [600, 350], kv=kv, budget=100, seed=64)
+    ref = oracle(inp)
+    for chunk in (32, 0):
+        assert_parity(run_gpu(inp, chunk=chunk), ref, f"G=64 ids kv={kv} chunk={chunk}")
