@@ -22,22 +22,23 @@
 // rows.  Lane group lb (lanes 16 lb .. 16 lb + 15) owns dims [lb D/4, (lb+1)
 // D/4) of every cell -- D/64 polar words and D/4 sign bits -- and covers
 // 8 of them per k-step; the query operands use the same dim assignment.
-//   polar:  each pair of 2-bit indices looks up the f16 high and low parts
-//           of its two centroids in a 16-entry LDS table, so q_rot . c[idx]
-//           keeps ~22 bits: hi*hi + hi*lo + lo*hi.
-//   QJL:    each nibble of sign bits looks up four f16 0 / 1 values; the
-//           MFMA gives the sum over set bits, and the signed sum is
-//           2 * that - sum_d q_jl[d] (the page's form).
+//   polar:  each byte of an index word (four 2-bit indices) looks up the f16
+//           high and low parts of its four centroids in 256-entry LDS
+//           tables, so q_rot . c[idx] keeps ~22 bits: hi*hi + hi*lo + lo*hi.
+//   QJL:    each byte of sign bits looks up eight f16 2 / 0 values; the MFMA,
+//           its accumulator started at -sum_d q_jl[d], gives the page's
+//           signed sum 2 * (sum over set bits) - sum_d q_jl[d] directly.
 // PV on the same MFMA: A = p * vnorm (f16 hi + lo) straight from the score
 // accumulators, B = decoded value fragments: a lane needs one dim of eight
 // cells, so the tile's V index words are staged in LDS transposed
 // ([word][cell]) and each lane extracts its 2-bit field from eight words.
-// Ranges, as in the dense kernel: each q_rot and q_jl row is multiplied by a
-// power of two that puts its largest element in [2^13, 2^14) before its f16
-// hi + lo split (the scores take the inverse power), and p * vnorm carries a
-// per-wave factor 2^(21 - vexp), vexp the largest f16 exponent field of the
-// value norms seen so far, so that it stays below 2^15 and far above f16's
-// subnormal step; the partial is written as (o, m - x, l * 2^x).
+// Ranges, as in the dense kernel: each query row (q_rot and q_jl together)
+// is multiplied by a power of two that puts its largest element in
+// [2^13, 2^14) before its f16 hi + lo split (the scores take the inverse
+// power inside the exponent), and p * vnorm carries a per-wave factor
+// 2^(21 - vexp), vexp the largest f16 exponent field of the value norms seen
+// so far, so that it stays below 2^15 and far above f16's subnormal step;
+// the partial is written as (o, m - x, l * 2^x).
 #pragma once
 
 #include "common.h"
@@ -72,7 +73,7 @@ struct TqLds {
   static constexpr int KS = D / 32;
   static constexpr int VW = D / 16;                          // V index words per cell
   static constexpr int VT = NW * VW * TC * 4;                // per-wave transposed V words
-  static constexpr int NM = NW * 2 * TC * 4;                 // per-wave K and V norm words
+  static constexpr int NM = NW * 3 * TC * 4;                 // per-wave (n, rq) per cell and value norms
   static constexpr int QB = 2 * NRB * KS * 2 * 64 * 16;      // q_rot and q_jl operands, hi + lo
   static constexpr int QS = RB * 4;                          // per-row sum of q_jl
   static constexpr int ML = NW * RB * 2 * 4;
@@ -82,8 +83,9 @@ struct TqLds {
 };
 
 // Decoding goes through 16-entry tables in the kernel's static LDS (at fixed
-// addresses, so a lookup's address is the extracted field scaled to the entry
-// size), built once per workgroup; a lookup replaces the bit arithmetic:
+// addresses, so a lookup's address is a 4-bit group of the cache word scaled
+// to the entry size), built once per workgroup; a lookup replaces the bit
+// arithmetic:
 //   chi[u], u = (b << 2) | a for two 2-bit indices a, b: the f16 high parts
 //           of centroids a and b (one dword of the MFMA operand);
 //   clo[u]  their f16 low parts -- 1028 bytes after chi: farther than a
@@ -91,23 +93,62 @@ struct TqLds {
 //           compiler cannot fuse a chi and a clo read into one two-dword read
 //           (whose two results land in adjacent registers and then need a move
 //           each into the hi and lo operand registers);
-//   jtab[u], u = four sign bits: four f16 values 0 / 1.
+//   jtab[u], u = four sign bits: four f16 values, 2 where the bit is set and
+//           0 elsewhere.
 // Each table's entries sit in distinct banks, so a wave's lookups never
-// conflict (equal entries broadcast).
+// conflict (equal entries broadcast; larger tables indexed by a whole byte
+// would conflict on random codes).  The address of a 4-bit group is the
+// group moved to bits 2-5 (chi, clo) or 3-6 (jtab) of a byte and masked: each
+// word is shifted once per direction, after which every group of it sits at
+// those bits of some byte of one of the two shifted copies, and one masked
+// byte select gives its address.
 constexpr int kTqCtabHi = 0, kTqJtab = 64, kTqCtabLo = 1028, kTqTabBytes = 1104;
 
 __device__ __forceinline__ uint32_t lds_u32(const uint8_t* base, uint32_t byte) {
   return *reinterpret_cast<const uint32_t*>(base + byte);
 }
 
-// Eight 2-bit indices (bits off .. off+15 of w) -> f16 high and low parts of
-// their centroids.
-__device__ __forceinline__ void tq_polar8(uint32_t w, int off, const uint8_t* tab, half8& hi,
-                                          half8& lo) {
+// x & m restricted to byte b of x (b a compile-time constant after
+// unrolling): one VALU operation with an SDWA byte select, which this compiler
+// does not form by itself from a shift and a mask.
+__device__ __forceinline__ uint32_t and_byte(uint32_t x, uint32_t m, int b) {
+  uint32_t r;
+  switch (b) {
+    case 0: r = x & m; break;
+    case 1:
+      asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1"
+          : "=v"(r) : "v"(m), "v"(x));
+      break;
+    case 2:
+      asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2"
+          : "=v"(r) : "v"(m), "v"(x));
+      break;
+    default:
+      asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3"
+          : "=v"(r) : "v"(m), "v"(x));
+      break;
+  }
+  return r;
+}
+
+// A polar word prepared for lookups: e = w << 2 holds the even 4-bit groups
+// (index pairs 0, 2, 4, 6) at bits 2-5 of bytes 0..3, o = w >> 2 the odd ones.
+struct PolarWord {
+  uint32_t e, o;
+};
+__device__ __forceinline__ PolarWord polar_word(uint32_t w) { return PolarWord{w << 2, w >> 2}; }
+__device__ __forceinline__ uint32_t polar_addr(const PolarWord& p, int i) {   // group i = 0..7
+  return and_byte((i & 1) ? p.o : p.e, 0x3Cu, i >> 1);
+}
+
+// Eight 2-bit indices (4-bit groups g0 .. g0+3 of the word) -> f16 high and
+// low parts of their centroids.
+__device__ __forceinline__ void tq_polar8(const PolarWord& p, int g0, const uint8_t* tab,
+                                          half8& hi, half8& lo) {
   u32x4 h, l;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const uint32_t a4 = __builtin_amdgcn_ubfe(w, off + 4 * j, 4) << 2;
+    const uint32_t a4 = polar_addr(p, g0 + j);
     h[j] = lds_u32(tab + kTqCtabHi, a4);
     l[j] = lds_u32(tab + kTqCtabLo, a4);
   }
@@ -115,10 +156,17 @@ __device__ __forceinline__ void tq_polar8(uint32_t w, int off, const uint8_t* ta
   lo = __builtin_bit_cast(half8, l);
 }
 
-// Eight sign bits (bits off .. off+7 of w) -> f16 1.0 where set, 0 elsewhere.
-__device__ __forceinline__ half8 tq_bits8(uint32_t w, int off, const uint8_t* tab) {
-  const uint32_t a0 = __builtin_amdgcn_ubfe(w, off, 4) << 3;
-  const uint32_t a1 = __builtin_amdgcn_ubfe(w, off + 4, 4) << 3;
+// A sign word prepared for lookups: lo = w << 3 holds the low 4 bits of each
+// byte at bits 3-6 of that byte, hi = w >> 1 the high 4 bits.
+struct SignWord {
+  uint32_t lo, hi;
+};
+__device__ __forceinline__ SignWord sign_word(uint32_t w) { return SignWord{w << 3, w >> 1}; }
+
+// Eight sign bits (byte b of the word) -> f16 2.0 where set, 0 elsewhere.
+__device__ __forceinline__ half8 tq_bits8(const SignWord& p, int b, const uint8_t* tab) {
+  const uint32_t a0 = and_byte(p.lo, 0x78u, b);
+  const uint32_t a1 = and_byte(p.hi, 0x78u, b);
   const u32x2 e0 = *reinterpret_cast<const u32x2*>(tab + kTqJtab + a0);
   const u32x2 e1 = *reinterpret_cast<const u32x2*>(tab + kTqJtab + a1);
   const u32x4 r = {e0[0], e0[1], e1[0], e1[1]};
@@ -179,7 +227,10 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
 
   uint8_t* work = smem;
   uint32_t* vtw = reinterpret_cast<uint32_t*>(work) + wave * VW * TC;          // [VW][TC]
-  uint32_t* nrm = reinterpret_cast<uint32_t*>(work + L::VT) + wave * 2 * TC;   // K norms, V norms
+  // per cell of this wave's tile: (n, rq) = (key norm * qscale, residual norm
+  // * qjl_scale), then the value norm times 2^(21 - vexp)
+  float* knf = reinterpret_cast<float*>(work + L::VT) + wave * 3 * TC;
+  float* vnf = knf + 2 * TC;
   u32x4* qlds = reinterpret_cast<u32x4*>(work + L::VT + L::NM);
   const int tail = L::MAIN > L::BUF ? L::MAIN : L::BUF;
   float* qsum = reinterpret_cast<float*>(work + tail);
@@ -192,15 +243,15 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
     reinterpret_cast<uint32_t*>(tab + kTqCtabLo)[tid] = __builtin_amdgcn_perm(a.clo_hi, a.clo_lo, sel);
   } else if (tid < 32) {
     const uint32_t u = (uint32_t)(tid - 16);
-    auto f = [](uint32_t bit) -> uint32_t { return bit ? 0x3C00u : 0u; };
+    auto f = [](uint32_t bit) -> uint32_t { return bit ? 0x4000u : 0u; };   // f16 2.0
     reinterpret_cast<u32x2*>(tab + kTqJtab)[u] =
         u32x2{f(u & 1) | (f((u >> 1) & 1) << 16), f((u >> 2) & 1) | (f((u >> 3) & 1) << 16)};
   }
 
-  // ---- query operands: q_rot and q_jl rows as f16 hi + lo, each row
-  // normalised by a power of two (its max |element| per wave first, into
-  // qred[which][wave][row], the (m, l) area that the epilogue uses later),
-  // and each row's sum of q_jl (fp32) ----
+  // ---- query operands: q_rot and q_jl rows as f16 hi + lo, both parts of a
+  // row normalised by one power of two (the max |element| of each part per
+  // wave first, into qred[which][wave][row], the (m, l) area that the
+  // epilogue uses later), and each row's sum of q_jl (fp32) ----
   float* qred = mls;
   auto q_slot = [&](int slot, int& which, int& kks, int& row, float (&x)[8]) {
     which = slot / (NRB * KS * 64);              // 0: q_rot, 1: q_jl
@@ -222,10 +273,10 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
       x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
     }
   };
-  auto row_max = [&](int which, int row) -> float {
-    float m = qred[which * NW * RB + row];
+  auto row_max = [&](int row) -> float {       // over both parts and all waves
+    float m = qred[row];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) m = fmaxf(m, qred[(which * NW + w) * RB + row]);
+    for (int w = 1; w < 2 * NW; ++w) m = fmaxf(m, qred[w * RB + row]);
     return m;
   };
   {
@@ -263,7 +314,7 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
       float x[8];
       q_slot(slot, which, kks, row, x);
       float rs_unused;
-      const float f = q_row_factor(row_max(which, row), 0.5f, 1, &rs_unused);
+      const float f = q_row_factor(row_max(row), 0.5f, 1, &rs_unused);
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] *= f;
       half8 hi, lo;
@@ -341,9 +392,12 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
       R.pol[0] = w[0];
       R.pol[1] = w[1];
     }
+    // both norm words of cell l % 32 in every lane (a lane-dependent choice
+    // of resource would need a loop over the distinct resources)
     const uint32_t nc = (uint32_t)(ts + (lane & 31) - c0);
-    R.nrm = lane < 32 ? __builtin_amdgcn_raw_buffer_load_b32(rkn, nc * 4, 0, 0)
-                      : __builtin_amdgcn_raw_buffer_load_b32(rvn, nc * 4, 0, 0);
+    const uint32_t kn = __builtin_amdgcn_raw_buffer_load_b32(rkn, nc * 4, 0, 0);
+    const uint32_t vn = __builtin_amdgcn_raw_buffer_load_b32(rvn, nc * 4, 0, 0);
+    R.nrm = lane < 32 ? kn : vn;
   };
 
   constexpr float kTau = 8.0f;
@@ -357,12 +411,17 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
     const int cell = lane >> 1;
 #pragma unroll
     for (int j = 0; j < VW / 2; ++j) vtw[((lane & 1) * (VW / 2) + j) * TC + cell] = R.pol[j];
-    nrm[lane] = R.nrm;
     const int ef = lane >= 32 ? (int)((R.nrm & 0x7fffu) >> 10) : 0;
     if (__any(ef > vexp)) {
       const int vn = wave_max_u5(ef);
       vf = __builtin_amdgcn_ldexpf(vf, vexp - vn);
       vexp = vn;
+    }
+    if (lane < 32) {
+      knf[2 * lane] = f16lo(R.nrm) * a.qscale;
+      knf[2 * lane + 1] = f16hi(R.nrm) * a.qjl_scale;
+    } else {
+      vnf[lane - 32] = __builtin_amdgcn_ldexpf(f16lo(R.nrm), 21 - vexp);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   };
@@ -376,10 +435,11 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) O[k][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  float qs[NRB];                                 // sum of q_jl of this lane's rows 16k + lr
-  float ra[NRB], rb2[NRB];                       // score factors of the normalised q_rot, 2 x q_jl
+  float qs[NRB];                                 // normalised sum of q_jl of this lane's rows 16k + lr
+  float rs[NRB];                                 // inverse of the rows' normalising factor
 
-  // ---- QK: S[cb][k][i] = score (base 2) of cell ts+16cb+4lb+i for row 16k+lr ----
+  // ---- QK: S[cb][k][i] = score (base 2) of cell ts+16cb+4lb+i for row 16k+lr,
+  // times the row's normalising factor ----
   auto qk = [&](const KRegs& R, f32x4 (&S)[2][NRB]) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     f32x4 Sp[2][NRB], Sj[2][NRB];
@@ -388,16 +448,25 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
 #pragma unroll
       for (int k = 0; k < NRB; ++k) {
         Sp[cb][k] = f32x4{0.f, 0.f, 0.f, 0.f};
-        Sj[cb][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+        Sj[cb][k] = f32x4{-qs[k], -qs[k], -qs[k], -qs[k]};
       }
+    PolarWord pw[2][KW];
+    SignWord sw[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+#pragma unroll
+      for (int w = 0; w < KW; ++w) pw[cb][w] = polar_word(R.pol[cb][w]);
+      // D = 64: the lane group's 16 sign bits are the low or high half of the word
+      sw[cb] = sign_word(D == 64 ? R.jl[cb] >> (16 * (lb & 1)) : R.jl[cb]);
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       half8 ch[2], cl[2], jb[2];
       const int dl = 8 * ks;                     // dim offset inside the lane group's span
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
-        tq_polar8(R.pol[cb][dl / 16], 2 * (dl % 16), tab, ch[cb], cl[cb]);
-        jb[cb] = tq_bits8(R.jl[cb], (lb * (D / 4) + dl) % 32, tab);
+        tq_polar8(pw[cb][dl / 16], (dl % 16) / 2, tab, ch[cb], cl[cb]);
+        jb[cb] = tq_bits8(sw[cb], dl / 8, tab);
       }
 #pragma unroll
       for (int k = 0; k < NRB; ++k) {
@@ -417,19 +486,18 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
         }
       }
     }
-    // score = qscale * norm * (polar + residual * qjl_scale * (2 pos - sum q_jl))
+    // score = qscale * norm * (polar + residual * qjl_scale * signed sum)
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
-      const u32x4 kn = *reinterpret_cast<const u32x4*>(nrm + 16 * cb + 4 * lb);
+      const f32x4 f0 = *reinterpret_cast<const f32x4*>(knf + 2 * (16 * cb + 4 * lb));
+      const f32x4 f1 = *reinterpret_cast<const f32x4*>(knf + 2 * (16 * cb + 4 * lb) + 4);
+      const float n[4] = {f0[0], f0[2], f1[0], f1[2]};
+      const float rq[4] = {f0[1], f0[3], f1[1], f1[3]};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float n = f16lo(kn[i]) * a.qscale;
-        const float rq = f16hi(kn[i]) * a.qjl_scale;
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int k = 0; k < NRB; ++k)
-          S[cb][k][i] =
-              n * __builtin_fmaf(rq, __builtin_fmaf(rb2[k], Sj[cb][k][i], -qs[k]), Sp[cb][k][i] * ra[k]);
-      }
+          S[cb][k][i] = n[i] * __builtin_fmaf(rq[i], Sj[cb][k][i], Sp[cb][k][i]);
     }
   };
 
@@ -454,15 +522,18 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
       float tmax = x[0];
 #pragma unroll
       for (int e = 1; e < 8; ++e) tmax = fmaxf(tmax, x[e]);
-      tmax = max_x32(max_x16(tmax));
+      tmax = max_x32(max_x16(tmax)) * rs[k];
       const float mold = m_run[k];
       const bool bump = tmax > mold + kTau;
       const float mnew = bump ? tmax : mold;
       const float corr = bump && mold != -INFINITY ? __builtin_amdgcn_exp2f(mold - mnew) : 1.0f;
+      // a row with no visible cell yet has every x = -inf: any finite
+      // reference gives its weights exp2(-inf) = 0
+      const float mref = mnew == -INFINITY ? 0.f : mnew;
       float psum = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float pe = (x[e] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x[e] - mnew);
+        const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], rs[k], -mref));
         pr[k][e] = pe;
         psum += pe;
       }
@@ -483,14 +554,13 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
     // P' = p * vnorm of each of this lane's eight cells (A operand k = 8 lb + e)
     half8 phi[NRB], plo[NRB];
     {
-      const u32x4 va = *reinterpret_cast<const u32x4*>(nrm + TC + 4 * lb);
-      const u32x4 vb = *reinterpret_cast<const u32x4*>(nrm + TC + 16 + 4 * lb);
-      const float fac = __builtin_amdgcn_ldexpf(1.0f, 21 - vexp);
+      const f32x4 va = *reinterpret_cast<const f32x4*>(vnf + 4 * lb);
+      const f32x4 vb = *reinterpret_cast<const f32x4*>(vnf + 16 + 4 * lb);
       float vn[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        vn[i] = f16lo(va[i]) * fac;
-        vn[4 + i] = f16lo(vb[i]) * fac;
+        vn[i] = va[i];
+        vn[4 + i] = vb[i];
       }
 #pragma unroll
       for (int k = 0; k < NRB; ++k) {
@@ -537,12 +607,8 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
     issue_k(ts, RK);
     __syncthreads();                             // row maxima, q_jl sums and tables staged
 #pragma unroll
-    for (int k = 0; k < NRB; ++k) {
-      qs[k] = qsum[16 * k + lr];
-      (void)q_row_factor(row_max(0, 16 * k + lr), 0.5f, 1, &ra[k]);
-      (void)q_row_factor(row_max(1, 16 * k + lr), 0.5f, 1, &rb2[k]);
-      rb2[k] *= 2.0f;
-    }
+    for (int k = 0; k < NRB; ++k)
+      qs[k] = qsum[16 * k + lr] * q_row_factor(row_max(16 * k + lr), 0.5f, 1, &rs[k]);
     q_stage();
     __syncthreads();                             // query operands staged
 #pragma unroll 1
