@@ -65,7 +65,7 @@ struct TqArgs {
 };
 
 // LDS of one TurboQuant workgroup (four waves).
-template <int D, int NRB>
+template <int D, int NRB, bool PK>
 struct TqLds {
   static constexpr int NW = 4;
   static constexpr int TC = 32;
@@ -74,7 +74,10 @@ struct TqLds {
   static constexpr int VW = D / 16;                          // V index words per cell
   static constexpr int VT = NW * VW * TC * 4;                // per-wave transposed V words
   static constexpr int NM = NW * 3 * TC * 4;                 // per-wave (n, rq) per cell and value norms
-  static constexpr int QB = 2 * NRB * KS * 2 * 64 * 16;      // q_rot and q_jl operands, hi + lo
+  // q_rot and q_jl operands: hi and lo separately, or (packed) hi parts in
+  // columns 0-7 and lo parts in 8-15, q_rot as two operands per k-step laid
+  // out against keys whose hi and lo pairs alternate
+  static constexpr int QB = (PK ? 3 * KS : 2 * NRB * KS * 2) * 64 * 16;
   static constexpr int QS = RB * 4;                          // per-row sum of q_jl
   static constexpr int ML = NW * RB * 2 * 4;
   static constexpr int BUF = NW / 2 * RB * D * 4;            // cross-wave combine (aliases VT, NM, QB)
@@ -94,15 +97,18 @@ struct TqLds {
 //           (whose two results land in adjacent registers and then need a move
 //           each into the hi and lo operand registers);
 //   jtab[u], u = four sign bits: four f16 values, 2 where the bit is set and
-//           0 elsewhere.
+//           0 elsewhere;
+//   chl[u]  chi[u] and clo[u] side by side, one two-dword read for both
+//           (the packed instances, whose other operand is laid out to take
+//           hi and lo pairs alternately).
 // Each table's entries sit in distinct banks, so a wave's lookups never
 // conflict (equal entries broadcast; larger tables indexed by a whole byte
 // would conflict on random codes).  The address of a 4-bit group is the
-// group moved to bits 2-5 (chi, clo) or 3-6 (jtab) of a byte and masked: each
+// group moved to bits 2-5 (chi, clo) or 3-6 (jtab, chl) of a byte and masked: each
 // word is shifted once per direction, after which every group of it sits at
 // those bits of some byte of one of the two shifted copies, and one masked
 // byte select gives its address.
-constexpr int kTqCtabHi = 0, kTqJtab = 64, kTqCtabLo = 1028, kTqTabBytes = 1104;
+constexpr int kTqCtabHi = 0, kTqJtab = 64, kTqCtabHL = 192, kTqCtabLo = 1028, kTqTabBytes = 1104;
 
 __device__ __forceinline__ uint32_t lds_u32(const uint8_t* base, uint32_t byte) {
   return *reinterpret_cast<const uint32_t*>(base + byte);
@@ -173,16 +179,40 @@ __device__ __forceinline__ half8 tq_bits8(const SignWord& p, int b, const uint8_
   return __builtin_bit_cast(half8, r);
 }
 
+// Eight 2-bit indices (4-bit groups g0 .. g0+3 of a polar word prepared like
+// a sign word, so that each group's address is the group scaled by 8) -> two
+// operands whose dwords alternate the f16 high and low parts of the centroid
+// pairs: a = [hi lo] of groups g0 and g0 + 1, b = [hi lo] of groups g0 + 2
+// and g0 + 3.
+__device__ __forceinline__ void tq_polar8_hl(const SignWord& p, int g0, const uint8_t* tab,
+                                             half8& a, half8& b) {
+  u32x2 e[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int g = g0 + j;
+    const uint32_t a8 = and_byte((g & 1) ? p.hi : p.lo, 0x78u, g >> 1);
+    e[j] = *reinterpret_cast<const u32x2*>(tab + kTqCtabHL + a8);
+  }
+  a = __builtin_bit_cast(half8, u32x4{e[0][0], e[0][1], e[1][0], e[1][1]});
+  b = __builtin_bit_cast(half8, u32x4{e[2][0], e[2][1], e[3][0], e[3][1]});
+}
+
+// x of lane l ^ 8 (a rotation by 8 within each row of 16 lanes, DPP).
+__device__ __forceinline__ float ror8(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ float f16lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu)); }
 __device__ __forceinline__ float f16hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
 
-template <int D, int NRB>
+template <int D, int NRB, bool PK>
 __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
-  using L = TqLds<D, NRB>;
+  using L = TqLds<D, NRB, PK>;
   constexpr int NW = L::NW, NT = 64 * NW, TC = L::TC, RB = L::RB, KS = L::KS, VW = L::VW;
   constexpr int NB = D / 16;                     // 16-dim output blocks
   constexpr int KW = D / 64;                     // polar words per lane group and cell
   static_assert(D == 64 || D == 128, "head_dim");
+  static_assert(!PK || NRB == 1, "packed operands hold at most 8 rows");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ __attribute__((aligned(16))) uint8_t tab[kTqTabBytes];
 
@@ -239,8 +269,11 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
     // entry u = (b << 2) | a: the byte selector [2a, 2a+1, 2b, 2b+1] picks
     // the two f16 halves of centroids a and b out of each 8-byte table
     const uint32_t sel = ((uint32_t)(tid & 3) | ((uint32_t)(tid >> 2) << 16)) * 0x0202u + 0x01000100u;
-    reinterpret_cast<uint32_t*>(tab + kTqCtabHi)[tid] = __builtin_amdgcn_perm(a.chi_hi, a.chi_lo, sel);
-    reinterpret_cast<uint32_t*>(tab + kTqCtabLo)[tid] = __builtin_amdgcn_perm(a.clo_hi, a.clo_lo, sel);
+    const uint32_t h = __builtin_amdgcn_perm(a.chi_hi, a.chi_lo, sel);
+    const uint32_t l = __builtin_amdgcn_perm(a.clo_hi, a.clo_lo, sel);
+    reinterpret_cast<uint32_t*>(tab + kTqCtabHi)[tid] = h;
+    reinterpret_cast<uint32_t*>(tab + kTqCtabLo)[tid] = l;
+    reinterpret_cast<u32x2*>(tab + kTqCtabHL)[tid] = u32x2{h, l};
   } else if (tid < 32) {
     const uint32_t u = (uint32_t)(tid - 16);
     auto f = [](uint32_t bit) -> uint32_t { return bit ? 0x4000u : 0u; };   // f16 2.0
@@ -253,13 +286,17 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
   // wave first, into qred[which][wave][row], the (m, l) area that the
   // epilogue uses later), and each row's sum of q_jl (fp32) ----
   float* qred = mls;
+  // the row of the block that MFMA column (or row) c = 0..15 carries: with
+  // packed operands columns 0-7 hold the hi parts of rows 0-7 and columns
+  // 8-15 their lo parts
+  auto crow = [](int c) -> int { return PK ? (c & 7) : c; };
   auto q_slot = [&](int slot, int& which, int& kks, int& row, float (&x)[8]) {
     which = slot / (NRB * KS * 64);              // 0: q_rot, 1: q_jl
     const int sl = slot % (NRB * KS * 64);
     const int ln = sl & 63;
     kks = sl >> 6;
     const int ks = kks % KS, k = kks / KS;
-    row = 16 * k + (ln & 15);
+    row = 16 * k + crow(ln & 15);
     const int r = r0 + row;
     const int d0 = (ln >> 4) * (D / 4) + 8 * ks;
 #pragma unroll
@@ -319,9 +356,22 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
       for (int e = 0; e < 8; ++e) x[e] *= f;
       half8 hi, lo;
       split_hi_lo(x, hi, lo);
-      const int base = ((which * NRB * KS + kks) * 2) * 64;
-      qlds[base + (slot & 63)] = __builtin_bit_cast(u32x4, hi);
-      qlds[base + 64 + (slot & 63)] = __builtin_bit_cast(u32x4, lo);
+      if constexpr (PK) {
+        const bool hic = (slot & 15) < 8;        // column of a hi part
+        const u32x4 h = __builtin_bit_cast(u32x4, hi), l = __builtin_bit_cast(u32x4, lo);
+        if (which == 0) {
+          // against keys [hi lo hi lo] of dims (0,1), (2,3) and of (4,5),
+          // (6,7): hi columns give (c_hi + c_lo) q_hi, lo columns c_hi q_lo
+          qlds[(2 * kks) * 64 + (slot & 63)] = hic ? u32x4{h[0], h[0], h[1], h[1]} : u32x4{l[0], 0u, l[1], 0u};
+          qlds[(2 * kks + 1) * 64 + (slot & 63)] = hic ? u32x4{h[2], h[2], h[3], h[3]} : u32x4{l[2], 0u, l[3], 0u};
+        } else {
+          qlds[(2 * KS + kks) * 64 + (slot & 63)] = hic ? h : l;
+        }
+      } else {
+        const int base = ((which * NRB * KS + kks) * 2) * 64;
+        qlds[base + (slot & 63)] = __builtin_bit_cast(u32x4, hi);
+        qlds[base + 64 + (slot & 63)] = __builtin_bit_cast(u32x4, lo);
+      }
     }
   };
   if (tid < RB) {
@@ -341,7 +391,7 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
   int lim[NRB];
 #pragma unroll
   for (int k = 0; k < NRB; ++k) {
-    const int wr = width_of(r0 + 16 * k + lr);
+    const int wr = width_of(r0 + 16 * k + crow(lr));
     lim[k] = wr < cend ? wr : cend;
   }
 
@@ -435,11 +485,14 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) O[k][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  float qs[NRB];                                 // normalised sum of q_jl of this lane's rows 16k + lr
+  float qs[NRB];                                 // normalised sum of q_jl of this lane's rows 16k + crow(lr)
   float rs[NRB];                                 // inverse of the rows' normalising factor
 
-  // ---- QK: S[cb][k][i] = score (base 2) of cell ts+16cb+4lb+i for row 16k+lr,
-  // times the row's normalising factor ----
+  // ---- QK: S[cb][k][i] = score (base 2) of cell ts+16cb+4lb+i for row
+  // 16k+crow(lr), times the row's normalising factor.  Packed: the hi and lo
+  // parts of a row's query land in columns c and c + 8 of the accumulators,
+  // which one rotation of each 16-lane row adds up (lanes c and c + 8 then
+  // hold the same row) ----
   auto qk = [&](const KRegs& R, f32x4 (&S)[2][NRB]) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     f32x4 Sp[2][NRB], Sj[2][NRB];
@@ -447,15 +500,20 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
       for (int k = 0; k < NRB; ++k) {
+        const float q0 = (!PK || lr < 8) ? -qs[k] : 0.f;
         Sp[cb][k] = f32x4{0.f, 0.f, 0.f, 0.f};
-        Sj[cb][k] = f32x4{-qs[k], -qs[k], -qs[k], -qs[k]};
+        Sj[cb][k] = f32x4{q0, q0, q0, q0};
       }
     PolarWord pw[2][KW];
+    SignWord pw8[2][KW];                         // packed: polar groups scaled by 8
     SignWord sw[2];
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
 #pragma unroll
-      for (int w = 0; w < KW; ++w) pw[cb][w] = polar_word(R.pol[cb][w]);
+      for (int w = 0; w < KW; ++w) {
+        if constexpr (PK) pw8[cb][w] = sign_word(R.pol[cb][w]);
+        else pw[cb][w] = polar_word(R.pol[cb][w]);
+      }
       // D = 64: the lane group's 16 sign bits are the low or high half of the word
       sw[cb] = sign_word(D == 64 ? R.jl[cb] >> (16 * (lb & 1)) : R.jl[cb]);
     }
@@ -465,26 +523,51 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
       const int dl = 8 * ks;                     // dim offset inside the lane group's span
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
-        tq_polar8(pw[cb][dl / 16], (dl % 16) / 2, tab, ch[cb], cl[cb]);
+        if constexpr (PK)                        // ch, cl: [hi lo hi lo] of dims 0-3 and of 4-7
+          tq_polar8_hl(pw8[cb][dl / 16], (dl % 16) / 2, tab, ch[cb], cl[cb]);
+        else
+          tq_polar8(pw[cb][dl / 16], (dl % 16) / 2, tab, ch[cb], cl[cb]);
         jb[cb] = tq_bits8(sw[cb], dl / 8, tab);
       }
-#pragma unroll
-      for (int k = 0; k < NRB; ++k) {
-        const int br = ((0 * NRB * KS + k * KS + ks) * 2) * 64;
-        const int bj = ((1 * NRB * KS + k * KS + ks) * 2) * 64;
-        const half8 qh = __builtin_bit_cast(half8, qlds[br + lane]);
-        const half8 ql = __builtin_bit_cast(half8, qlds[br + 64 + lane]);
-        const half8 jh = __builtin_bit_cast(half8, qlds[bj + lane]);
-        const half8 jl = __builtin_bit_cast(half8, qlds[bj + 64 + lane]);
+      if constexpr (PK) {
+        // columns 0-7: hi parts, 8-15: lo parts
+        const half8 qa = __builtin_bit_cast(half8, qlds[(2 * ks) * 64 + lane]);
+        const half8 qb = __builtin_bit_cast(half8, qlds[(2 * ks + 1) * 64 + lane]);
+        const half8 jp = __builtin_bit_cast(half8, qlds[(2 * KS + ks) * 64 + lane]);
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
-          Sp[cb][k] = mfma16(ch[cb], qh, Sp[cb][k]);
-          Sp[cb][k] = mfma16(ch[cb], ql, Sp[cb][k]);
-          Sp[cb][k] = mfma16(cl[cb], qh, Sp[cb][k]);
-          Sj[cb][k] = mfma16(jb[cb], jh, Sj[cb][k]);
-          Sj[cb][k] = mfma16(jb[cb], jl, Sj[cb][k]);
+          Sp[cb][0] = mfma16(ch[cb], qa, Sp[cb][0]);
+          Sp[cb][0] = mfma16(cl[cb], qb, Sp[cb][0]);
+          Sj[cb][0] = mfma16(jb[cb], jp, Sj[cb][0]);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < NRB; ++k) {
+          const int br = ((0 * NRB * KS + k * KS + ks) * 2) * 64;
+          const int bj = ((1 * NRB * KS + k * KS + ks) * 2) * 64;
+          const half8 qh = __builtin_bit_cast(half8, qlds[br + lane]);
+          const half8 ql = __builtin_bit_cast(half8, qlds[br + 64 + lane]);
+          const half8 jh = __builtin_bit_cast(half8, qlds[bj + lane]);
+          const half8 jl = __builtin_bit_cast(half8, qlds[bj + 64 + lane]);
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb) {
+            Sp[cb][k] = mfma16(ch[cb], qh, Sp[cb][k]);
+            Sp[cb][k] = mfma16(ch[cb], ql, Sp[cb][k]);
+            Sp[cb][k] = mfma16(cl[cb], qh, Sp[cb][k]);
+            Sj[cb][k] = mfma16(jb[cb], jh, Sj[cb][k]);
+            Sj[cb][k] = mfma16(jb[cb], jl, Sj[cb][k]);
+          }
         }
       }
+    }
+    if constexpr (PK) {
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          Sp[cb][0][i] += ror8(Sp[cb][0][i]);
+          Sj[cb][0][i] += ror8(Sj[cb][0][i]);
+        }
     }
     // score = qscale * norm * (polar + residual * qjl_scale * signed sum)
 #pragma unroll
@@ -543,7 +626,7 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
       if (__any(corr != 1.0f) || vf != 1.0f) {
         float cf[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) cf[i] = __shfl(corr, 4 * lb + i, 64) * vf;
+        for (int i = 0; i < 4; ++i) cf[i] = __shfl(corr, crow(4 * lb + i), 64) * vf;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -572,27 +655,56 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
     }
     // value fragments: lane (dim 16 nb + lr, k-group lb) takes field lr of the
     // index words of cells 4lb .. 4lb+3 and 16+4lb .. 16+4lb+3
+    if constexpr (PK) {
+      // values as [hi lo hi lo] of cell pairs (4lb, 4lb+1), (4lb+2, 4lb+3)
+      // and of the same pairs 16 cells on; the weights against them: rows
+      // 0-7 (hi parts of rows 0-7) [hi hi hi hi] of the pairs, giving
+      // p_hi (v_hi + v_lo), rows 8-15 (their lo parts) [lo 0 lo 0], giving
+      // p_lo v_hi
+      const u32x4 ph = __builtin_bit_cast(u32x4, phi[0]), pl = __builtin_bit_cast(u32x4, plo[0]);
+      const bool hir = lr < 8;
+      const half8 pa = __builtin_bit_cast(half8, hir ? u32x4{ph[0], ph[0], ph[1], ph[1]} : u32x4{pl[0], 0u, pl[1], 0u});
+      const half8 pb = __builtin_bit_cast(half8, hir ? u32x4{ph[2], ph[2], ph[3], ph[3]} : u32x4{pl[2], 0u, pl[3], 0u});
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const u32x4 wa = *reinterpret_cast<const u32x4*>(vtw + nb * TC + 4 * lb);
-      const u32x4 wb = *reinterpret_cast<const u32x4*>(vtw + nb * TC + 16 + 4 * lb);
-      const uint32_t w[8] = {wa[0], wa[1], wa[2], wa[3], wb[0], wb[1], wb[2], wb[3]};
-      u32x4 h, l;
+      for (int nb = 0; nb < NB; ++nb) {
+        const u32x4 wa = *reinterpret_cast<const u32x4*>(vtw + nb * TC + 4 * lb);
+        const u32x4 wb = *reinterpret_cast<const u32x4*>(vtw + nb * TC + 16 + 4 * lb);
+        const uint32_t w[8] = {wa[0], wa[1], wa[2], wa[3], wb[0], wb[1], wb[2], wb[3]};
+        u32x2 e[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t ia = __builtin_amdgcn_ubfe(w[2 * j], 2 * lr, 2);
-        const uint32_t ib = __builtin_amdgcn_ubfe(w[2 * j + 1], 2 * lr, 2);
-        const uint32_t a4 = (ia << 2) | (ib << 4);
-        h[j] = lds_u32(tab + kTqCtabHi, a4);
-        l[j] = lds_u32(tab + kTqCtabLo, a4);
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t ia = __builtin_amdgcn_ubfe(w[2 * j], 2 * lr, 2);
+          const uint32_t ib = __builtin_amdgcn_ubfe(w[2 * j + 1], 2 * lr, 2);
+          e[j] = *reinterpret_cast<const u32x2*>(tab + kTqCtabHL + ((ia << 3) | (ib << 5)));
+        }
+        const half8 va = __builtin_bit_cast(half8, u32x4{e[0][0], e[0][1], e[1][0], e[1][1]});
+        const half8 vb = __builtin_bit_cast(half8, u32x4{e[2][0], e[2][1], e[3][0], e[3][1]});
+        O[0][nb] = mfma16(pa, va, O[0][nb]);
+        O[0][nb] = mfma16(pb, vb, O[0][nb]);
       }
-      const half8 vh = __builtin_bit_cast(half8, h);
-      const half8 vl = __builtin_bit_cast(half8, l);
+    } else {
 #pragma unroll
-      for (int k = 0; k < NRB; ++k) {
-        O[k][nb] = mfma16(phi[k], vh, O[k][nb]);
-        O[k][nb] = mfma16(plo[k], vh, O[k][nb]);
-        O[k][nb] = mfma16(phi[k], vl, O[k][nb]);
+      for (int nb = 0; nb < NB; ++nb) {
+        const u32x4 wa = *reinterpret_cast<const u32x4*>(vtw + nb * TC + 4 * lb);
+        const u32x4 wb = *reinterpret_cast<const u32x4*>(vtw + nb * TC + 16 + 4 * lb);
+        const uint32_t w[8] = {wa[0], wa[1], wa[2], wa[3], wb[0], wb[1], wb[2], wb[3]};
+        u32x4 h, l;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t ia = __builtin_amdgcn_ubfe(w[2 * j], 2 * lr, 2);
+          const uint32_t ib = __builtin_amdgcn_ubfe(w[2 * j + 1], 2 * lr, 2);
+          const uint32_t a4 = (ia << 2) | (ib << 4);
+          h[j] = lds_u32(tab + kTqCtabHi, a4);
+          l[j] = lds_u32(tab + kTqCtabLo, a4);
+        }
+        const half8 vh = __builtin_bit_cast(half8, h);
+        const half8 vl = __builtin_bit_cast(half8, l);
+#pragma unroll
+        for (int k = 0; k < NRB; ++k) {
+          O[k][nb] = mfma16(phi[k], vh, O[k][nb]);
+          O[k][nb] = mfma16(plo[k], vh, O[k][nb]);
+          O[k][nb] = mfma16(phi[k], vl, O[k][nb]);
+        }
       }
     }
   };
@@ -608,7 +720,7 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
     __syncthreads();                             // row maxima, q_jl sums and tables staged
 #pragma unroll
     for (int k = 0; k < NRB; ++k)
-      qs[k] = qsum[16 * k + lr] * q_row_factor(row_max(16 * k + lr), 0.5f, 1, &rs[k]);
+      qs[k] = qsum[16 * k + crow(lr)] * q_row_factor(row_max(16 * k + crow(lr)), 0.5f, 1, &rs[k]);
     q_stage();
     __syncthreads();                             // query operands staged
 #pragma unroll 1
@@ -630,6 +742,20 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
   for (int k = 0; k < NRB; ++k) {
     m_run[k] -= (float)(21 - vexp);
     l_run[k] = __builtin_amdgcn_ldexpf(l_run[k], 21 - vexp);
+  }
+  if constexpr (PK) {
+    // packed: accumulator rows 0-7 hold the hi-weight sums of rows 0-7 (lane
+    // groups 0, 1), rows 8-15 the lo-weight sums of the same rows (groups 2,
+    // 3); their sum is the row's o, left in both halves so that rows 8-15
+    // stay copies of rows 0-7 with the same (m, l)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float u, v;
+        swap32(O[0][nb][i], u, v);
+        O[0][nb][i] = u + v;
+      }
   }
 
   // ---- combine the four waves into one partial per query row (as the

@@ -142,11 +142,11 @@ __global__ __launch_bounds__(kMergeThreads) void merge_rows_tq(TqMergeArgs a) {
   for (int e = 0; e < V; ++e) out[e] = x[e] * inv * a.signs[lane * V + e];
 }
 
-template <int D, int NRB>
+template <int D, int NRB, bool PK = false>
 hipError_t launch_tq(const TqArgs& a, dim3 grid, hipStream_t st) {
-  using L = gqa_kern::TqLds<D, NRB>;
+  using L = gqa_kern::TqLds<D, NRB, PK>;
   static_assert(L::BYTES <= 65536, "TurboQuant LDS budget");
-  hipLaunchKernelGGL((gqa_kern::attn_tq<D, NRB>), grid, dim3(256), L::BYTES, st, a);
+  hipLaunchKernelGGL((gqa_kern::attn_tq<D, NRB, PK>), grid, dim3(256), L::BYTES, st, a);
   return hipGetLastError();
 }
 
@@ -209,10 +209,15 @@ int gqa_decode_attn_tq(const float* q_rot, const float* q_jl, const uint32_t* k_
   if (nwg > 0x7fffffff) return GQA_ERR_SHAPE;
   const dim3 grid((unsigned)nwg);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  // up to 8 rows per KV head: hi and lo query parts share one MFMA operand
+  // (3 instead of 5 MFMAs per k-step of QK, 2 instead of 3 per PV block)
+  const bool packed = a.R <= 8;
   const bool two = gqa::block_rows(sh) > 16;
   hipError_t e;
-  if (D == 64) e = two ? launch_tq<64, 2>(a, grid, st) : launch_tq<64, 1>(a, grid, st);
-  else e = two ? launch_tq<128, 2>(a, grid, st) : launch_tq<128, 1>(a, grid, st);
+  if (D == 64)
+    e = packed ? launch_tq<64, 1, true>(a, grid, st) : two ? launch_tq<64, 2>(a, grid, st) : launch_tq<64, 1>(a, grid, st);
+  else
+    e = packed ? launch_tq<128, 1, true>(a, grid, st) : two ? launch_tq<128, 2>(a, grid, st) : launch_tq<128, 1>(a, grid, st);
   return e == hipSuccess ? GQA_OK : (int)e;
 }
 
