@@ -72,7 +72,10 @@ struct TqLds {
   static constexpr int RB = 16 * NRB;
   static constexpr int KS = D / 32;
   static constexpr int VW = D / 16;                          // V index words per cell
-  static constexpr int VT = NW * VW * TC * 4;                // per-wave transposed V words
+  // per-wave V index words, transposed ([word][cell]), or (packed) as
+  // lookup addresses, VS dwords per word (see the staging)
+  static constexpr int VS = 2 * TC + 16 / VW;                 // (VW / 2) VS = 8 mod 32
+  static constexpr int VT = NW * VW * (PK ? VS : TC) * 4;
   static constexpr int NM = NW * 3 * TC * 4;                 // per-wave (n, rq) per cell and value norms
   // q_rot and q_jl operands: hi and lo separately, or (packed) hi parts in
   // columns 0-7 and lo parts in 8-15, q_rot as two operands per k-step laid
@@ -199,7 +202,7 @@ __device__ __forceinline__ void tq_polar8_hl(const SignWord& p, int g0, const ui
 
 // x of lane l ^ 8 (a rotation by 8 within each row of 16 lanes, DPP).
 __device__ __forceinline__ float ror8(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x128, 0xF, 0xF, true));
 }
 
 __device__ __forceinline__ float f16lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu)); }
@@ -256,7 +259,7 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
   const int lim_lo = width_of(r0) < cend ? width_of(r0) : cend;
 
   uint8_t* work = smem;
-  uint32_t* vtw = reinterpret_cast<uint32_t*>(work) + wave * VW * TC;          // [VW][TC]
+  uint32_t* vtw = reinterpret_cast<uint32_t*>(work) + wave * VW * (PK ? L::VS : TC);
   // per cell of this wave's tile: (n, rq) = (key norm * qscale, residual norm
   // * qjl_scale), then the value norm times 2^(21 - vexp)
   float* knf = reinterpret_cast<float*>(work + L::VT) + wave * 3 * TC;
@@ -459,8 +462,36 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
   float vf = 1.0f;
   auto stage = [&](const VRegs& R) {
     const int cell = lane >> 1;
+    if constexpr (PK) {
+      // A value lookup takes field f (dim 16 nb + f) of the words of two
+      // cells (2i, 2i+1).  Interleave the two words so that 4-bit group m
+      // holds field 2m + t of both cells (t = f's parity; the even cell's
+      // field in the low bits): the group is the lookup's index.  The even
+      // cell's lane builds t = 0 from its word and the odd cell's (lane ^ 2),
+      // the odd cell's lane t = 1: a rotation of the other word by 2 bits and
+      // a bit-field select.  Each result is stored as two words whose bytes
+      // hold the even and the odd groups scaled by 8 (the entry size), so
+      // that one byte extract gives a lookup's address.  Layout per word:
+      // [pair / 8][parity][half][pair % 8], VS dwords apart with VS VW / 2 =
+      // 8 mod 32, so that the stores of a wave and the two-dword reads of
+      // the lookups each fall in distinct banks of the 32.
+      const bool odd = cell & 1;
+      const uint32_t msk = odd ? 0xCCCCCCCCu : 0x33333333u;
 #pragma unroll
-    for (int j = 0; j < VW / 2; ++j) vtw[((lane & 1) * (VW / 2) + j) * TC + cell] = R.pol[j];
+      for (int j = 0; j < VW / 2; ++j) {
+        const uint32_t w = R.pol[j];
+        const uint32_t p = (uint32_t)__builtin_amdgcn_mov_dpp((int)w, 0x4E, 0xF, 0xF, true);   // lane ^ 2
+        const uint32_t rot = __builtin_amdgcn_alignbit(p, p, odd ? 2 : 30);
+        const uint32_t x = (w & msk) | (rot & ~msk);
+        const int pr = cell >> 1;                  // cell pair
+        uint32_t* dst = vtw + ((lane & 1) * (VW / 2) + j) * L::VS + (pr >> 3) * 32 + (cell & 1) * 16 + (pr & 7);
+        dst[0] = (x << 3) & 0x78787878u;           // groups 0, 2, 4, 6
+        dst[8] = (x >> 1) & 0x78787878u;           // groups 1, 3, 5, 7
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < VW / 2; ++j) vtw[((lane & 1) * (VW / 2) + j) * TC + cell] = R.pol[j];
+    }
     const int ef = lane >= 32 ? (int)((R.nrm & 0x7fffu) >> 10) : 0;
     if (__any(ef > vexp)) {
       const int vn = wave_max_u5(ef);
@@ -665,18 +696,18 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
       const bool hir = lr < 8;
       const half8 pa = __builtin_bit_cast(half8, hir ? u32x4{ph[0], ph[0], ph[1], ph[1]} : u32x4{pl[0], 0u, pl[1], 0u});
       const half8 pb = __builtin_bit_cast(half8, hir ? u32x4{ph[2], ph[2], ph[3], ph[3]} : u32x4{pl[2], 0u, pl[3], 0u});
+      // field lr: parity lr & 1, group lr >> 1 -> half (lr >> 1) & 1, byte lr >> 2
+      const uint32_t* vsrc = vtw + (lr & 1) * 16 + ((lr >> 1) & 1) * 8 + 2 * lb;
+      const uint32_t boff = 8 * (lr >> 2);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const u32x4 wa = *reinterpret_cast<const u32x4*>(vtw + nb * TC + 4 * lb);
-        const u32x4 wb = *reinterpret_cast<const u32x4*>(vtw + nb * TC + 16 + 4 * lb);
-        const uint32_t w[8] = {wa[0], wa[1], wa[2], wa[3], wb[0], wb[1], wb[2], wb[3]};
+        const u32x2 x0 = *reinterpret_cast<const u32x2*>(vsrc + nb * L::VS);        // pairs 2lb, 2lb+1
+        const u32x2 x1 = *reinterpret_cast<const u32x2*>(vsrc + nb * L::VS + 32);   // pairs 8+2lb, 9+2lb
+        const uint32_t xs[4] = {x0[0], x0[1], x1[0], x1[1]};
         u32x2 e[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t ia = __builtin_amdgcn_ubfe(w[2 * j], 2 * lr, 2);
-          const uint32_t ib = __builtin_amdgcn_ubfe(w[2 * j + 1], 2 * lr, 2);
-          e[j] = *reinterpret_cast<const u32x2*>(tab + kTqCtabHL + ((ia << 3) | (ib << 5)));
-        }
+        for (int j = 0; j < 4; ++j)
+          e[j] = *reinterpret_cast<const u32x2*>(tab + kTqCtabHL + __builtin_amdgcn_ubfe(xs[j], boff, 8));
         const half8 va = __builtin_bit_cast(half8, u32x4{e[0][0], e[0][1], e[1][0], e[1][1]});
         const half8 vb = __builtin_bit_cast(half8, u32x4{e[2][0], e[2][1], e[3][0], e[3][1]});
         O[0][nb] = mfma16(pa, va, O[0][nb]);
