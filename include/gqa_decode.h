@@ -202,7 +202,9 @@ int gqa_decode_merge_gated(const float *part, const int32_t *seq_lens, const int
  *   c0 .. c3     the four centroids; qjl_scale (the page uses
  *                sqrt(pi/2) / head_dim); scale the score scale
  * D must be 64 or 128 (the page: at most 128); no ids.  Workspace, chunk,
- * stream and errors as gqa_decode_attn_f16. */
+ * stream and errors as gqa_decode_attn_f16.  Numerics as for the other
+ * calls; a row's q_rot and q_jl are scaled together by one power of two
+ * before their f16 hi + lo split. */
 int gqa_decode_attn_tq(const float *q_rot, const float *q_jl, const uint32_t *k_polar,
                        const uint32_t *k_jl, const uint32_t *k_norms, const uint32_t *v_polar,
                        const uint32_t *v_norms, const int32_t *seq_lens,
