@@ -65,6 +65,17 @@ def test_tq_lengths_around_tiles(L):
         assert_parity(run_tq(inp, chunk), ref, f"tq L={L} chunk={chunk}")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("G,T", [(8, 1), (4, 2), (3, 3), (9, 1)])
+def test_tq_rows_around_the_packing_limit(D, G, T):
+    # up to 8 rows per KV head share MFMA operands (hi parts in columns 0-7,
+    # lo parts in 8-15); 9 rows take the unpacked instance
+    inp = make_tq_case(2, T, 2 * G, 2, D, 260, [260, 97], seed=500 + D + 10 * G + T)
+    ref = oracle(inp)
+    for chunk in (64, 0):
+        assert_parity(run_tq(inp, chunk), ref, f"tq rows G={G} T={T} D={D} chunk={chunk}")
+
+
 def test_tq_two_row_blocks_and_many_rows():
     # 12 query heads per KV head x 2 tokens = 24 rows: two 16-row MFMA blocks;
     # 40 query heads per KV head: two workgroup row blocks
