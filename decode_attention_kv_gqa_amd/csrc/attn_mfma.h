@@ -290,6 +290,14 @@ __global__ __launch_bounds__(64 * NW, (attn_occupancy<D, I8, NRB>())) void attn_
     for (int i = 0; i < QPT; ++i) q_load(tid + NT * i, qv[i][0], qv[i][1]);
   }
 
+  // Gather mode: the split's first NT cell ids do not depend on the
+  // sequence length, so they are requested with it and the two reads
+  // overlap (the staging below takes them from here).
+  int id_first = 0;
+  if constexpr (IDS) {
+    const int64_t pos = (int64_t)p * a.chunk + tid;
+    if (tid < a.chunk && pos < a.B) id_first = a.ids[((size_t)s * a.T + tq) * a.B + pos];
+  }
   const int seq_len = a.seq_lens[s];
 
   auto width_of = [&](int r) -> int {   // r: row index within the unit
@@ -360,7 +368,8 @@ __global__ __launch_bounds__(64 * NW, (attn_occupancy<D, I8, NRB>())) void attn_
   if constexpr (IDS) {
     const int32_t* idrow = a.ids + ((size_t)s * a.T + tq) * a.B;
     for (int i = tid; i < cend - c0; i += NT) {
-      int c = idrow[c0 + i];
+      // position c0 + tid < cend <= B and tid < chunk: id_first holds it
+      int c = i == tid ? id_first : idrow[c0 + i];
       idl[i] = c < 0 ? 0 : (c >= a.Lmax ? a.Lmax - 1 : c);
     }
   }
