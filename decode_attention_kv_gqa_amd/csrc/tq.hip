@@ -36,8 +36,10 @@ struct TqMergeArgs {
 // row's partials as in the other merge, then the inverse randomized Hadamard
 // rotation by wave 0 -- lane l holds dims l*V .. l*V+V-1 (V = D/64), so a
 // butterfly at stride s < V stays inside the lane and one at s >= V pairs
-// lane l with lane l ^ (s / V).
-template <int D>
+// lane l with lane l ^ (s / V).  U splits per wave have their loads in
+// flight together (4 waves x U covers up to 16, 32 or 64 splits in one round
+// trip).
+template <int D, int U>
 __global__ __launch_bounds__(kMergeThreads) void merge_rows_tq(TqMergeArgs a) {
   constexpr int V = D / 64;
   __shared__ float red_o[4][D];
@@ -52,7 +54,6 @@ __global__ __launch_bounds__(kMergeThreads) void merge_rows_tq(TqMergeArgs a) {
   float acc[V];
 #pragma unroll
   for (int e = 0; e < V; ++e) acc[e] = 0.f;
-  constexpr int U = 4;                         // splits per wave with their loads in flight together
   for (int j0 = wave; j0 < a.P; j0 += 4 * U) {
     float mj[U], lj[U], oj[U][V];
 #pragma unroll
@@ -150,6 +151,12 @@ hipError_t launch_tq(const TqArgs& a, dim3 grid, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int U>
+void launch_merge_tq(const TqMergeArgs& a, int D, dim3 grid, hipStream_t st) {
+  if (D == 64) hipLaunchKernelGGL((merge_rows_tq<64, U>), grid, dim3(kMergeThreads), 0, st, a);
+  else hipLaunchKernelGGL((merge_rows_tq<128, U>), grid, dim3(kMergeThreads), 0, st, a);
+}
+
 uint16_t f16_bits(_Float16 h) {
   uint16_t b;
   std::memcpy(&b, &h, 2);
@@ -241,8 +248,9 @@ int gqa_decode_merge_tq(const float* part, const int32_t* seq_lens, const float*
   a.out = out;
   a.P = (int)P;
   const dim3 grid((unsigned)rows);
-  if (D == 64) hipLaunchKernelGGL(merge_rows_tq<64>, grid, dim3(kMergeThreads), 0, st, a);
-  else hipLaunchKernelGGL(merge_rows_tq<128>, grid, dim3(kMergeThreads), 0, st, a);
+  if (P <= 16) launch_merge_tq<4>(a, D, grid, st);
+  else if (P <= 32) launch_merge_tq<8>(a, D, grid, st);
+  else launch_merge_tq<16>(a, D, grid, st);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? GQA_OK : (int)e;
 }
