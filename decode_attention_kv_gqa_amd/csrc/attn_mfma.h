@@ -54,6 +54,8 @@
 // registers while the current tile is computed.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 #include "mfma_util.h"
 
@@ -132,7 +134,12 @@ struct AttnLds {
   using G = TileGeom<D, I8>;
   static constexpr int RB = 16 * NRB;
   static constexpr int VT = NW * G::TC * G::RBY;         // per-wave V tiles (and K tiles)
-  static constexpr int BUF2 = NW / 2 * RB * D * 4;       // two-stage cross-wave combine buffers
+  // Combine buffers hold rows of RS = D + 4 floats: the accumulators are
+  // parked with one lane per dim, four rows per lane group, and a row stride
+  // of 4 mod 8 dwords puts the two lane groups of a half-wave in different
+  // halves of the 32 banks (a stride of D put them in the same banks).
+  static constexpr int RS = D + 4;
+  static constexpr int BUF2 = NW / 2 * RB * RS * 4;      // two-stage cross-wave combine buffers
   static constexpr int QB = NRB * G::KS * 2 * 64 * 16;   // query B operands, hi and lo
   static constexpr int SC = I8 ? NW * 2 * G::NG * G::TC * 4 : 0;  // per-wave K/V scales (fp32)
   static constexpr int ML = NW * RB * 2 * 4;             // per-wave (m, l)
@@ -153,7 +160,7 @@ struct AttnLds {
   // buffers) when NW buffers fit beside everything else; otherwise in two
   // (half the waves park, the other half add, then the sums are added).
   // The buffers alias the tiles either way.
-  static constexpr int BUF1 = NW * RB * D * 4;
+  static constexpr int BUF1 = NW * RB * RS * 4;
   static constexpr bool ONE_PASS =
       NW > 1 && (TILES > BUF1 ? TILES : BUF1) + QB + SC + ML + IDSB <= CAP;
   static constexpr int BUF = ONE_PASS ? BUF1 : BUF2;     // cross-wave combine buffers (alias tiles)
@@ -736,21 +743,32 @@ __global__ __launch_bounds__(64 * NW, (attn_occupancy<D, I8, NRB>())) void attn_
       }
     }
     __syncthreads();   // query operands staged
-#pragma unroll 1
-    while (ts < cend) {
-      const int tn = ts + NW * TC;
+    // One tile; MORE: request the wave's next tile (the last tile requests
+    // nothing, so the combine's barrier does not wait on loads past the
+    // split).  Two copies of the body rather than a branch around the
+    // requests, which would leave the loop head's wait counts inexact.
+    auto step = [&](int t0, auto more) {
+      constexpr bool MORE = decltype(more)::value;
+      const int tn = t0 + NW * TC;
       stage(RV, RK);
-      issue_v(tn, RV);     // past the split's end: no memory traffic
+      if constexpr (MORE) issue_v(tn, RV);
       f32x4 S[2][NRB];
       if constexpr (L::KL) {
-        issue_k(tn, RK);
+        if constexpr (MORE) issue_k(tn, RK);
         qk(RK, S);
       } else {
         qk(RK, S);
-        issue_k(tn, RK);
+        if constexpr (MORE) issue_k(tn, RK);
       }
-      softmax_pv(ts, S);
-      ts = tn;
+      softmax_pv(t0, S);
+    };
+    if (ts < cend) {
+#pragma unroll 1
+      while (ts + NW * TC < cend) {
+        step(ts, std::integral_constant<bool, true>{});
+        ts += NW * TC;
+      }
+      step(ts, std::integral_constant<bool, false>{});
     }
   }
 
@@ -804,15 +822,17 @@ __global__ __launch_bounds__(64 * NW, (attn_occupancy<D, I8, NRB>())) void attn_
         mls[(wave * RB + 16 * k + lr) * 2 + 1] = l_run[k];
       }
     }
-    float* bw = reinterpret_cast<float*>(smem) + wave * RB * D;
+    constexpr int RS = L::RS;
+    float* bw = reinterpret_cast<float*>(smem) + wave * RB * RS;
 #pragma unroll
     for (int k = 0; k < NRB; ++k)
 #pragma unroll
       for (int nb = 0; nb < G::NB; ++nb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) bw[(16 * k + 4 * lb + i) * D + 16 * nb + lr] = O[k][nb][i];
+        for (int i = 0; i < 4; ++i) bw[(16 * k + 4 * lb + i) * RS + 16 * nb + lr] = O[k][nb][i];
     __syncthreads();
     const float* b0 = reinterpret_cast<const float*>(smem);
+#pragma unroll
     for (int idx = tid; idx < RB * D / 4; idx += NT) {
       const int row = idx / (D / 4);
       const int d4 = idx % (D / 4);
@@ -828,7 +848,7 @@ __global__ __launch_bounds__(64 * NW, (attn_occupancy<D, I8, NRB>())) void attn_
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
           const float f = (mw[w] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw[w] - M);
-          const float4 y = *reinterpret_cast<const float4*>(b0 + w * RB * D + row * D + 4 * d4);
+          const float4 y = *reinterpret_cast<const float4*>(b0 + w * RB * RS + row * RS + 4 * d4);
           x.x = __builtin_fmaf(f, y.x, x.x);
           x.y = __builtin_fmaf(f, y.y, x.y);
           x.z = __builtin_fmaf(f, y.z, x.z);
@@ -843,6 +863,7 @@ __global__ __launch_bounds__(64 * NW, (attn_occupancy<D, I8, NRB>())) void attn_
     // the upper half of the waves parks them in LDS, the lower half adds
     // theirs, and the NW/2 sums are added while the partial is written.
     constexpr int HALF = NW / 2 > 0 ? NW / 2 : 1;
+    constexpr int RS = L::RS;
     __syncthreads();
     if (lb == 0) {
 #pragma unroll
@@ -868,24 +889,24 @@ __global__ __launch_bounds__(64 * NW, (attn_occupancy<D, I8, NRB>())) void attn_
       }
     }
     if (wave >= HALF) {
-      float* b = buf + (wave - HALF) * RB * D;
+      float* b = buf + (wave - HALF) * RB * RS;
 #pragma unroll
       for (int k = 0; k < NRB; ++k)
 #pragma unroll
         for (int nb = 0; nb < G::NB; ++nb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) b[(16 * k + 4 * lb + i) * D + 16 * nb + lr] = O[k][nb][i];
+          for (int i = 0; i < 4; ++i) b[(16 * k + 4 * lb + i) * RS + 16 * nb + lr] = O[k][nb][i];
     }
     __syncthreads();
     if (wave < HALF) {
-      float* b = buf + wave * RB * D;
+      float* b = buf + wave * RB * RS;
 #pragma unroll
       for (int k = 0; k < NRB; ++k)
 #pragma unroll
         for (int nb = 0; nb < G::NB; ++nb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            float* x = b + (16 * k + 4 * lb + i) * D + 16 * nb + lr;
+            float* x = b + (16 * k + 4 * lb + i) * RS + 16 * nb + lr;
             *x = *x + O[k][nb][i];
           }
     }
@@ -895,10 +916,10 @@ __global__ __launch_bounds__(64 * NW, (attn_occupancy<D, I8, NRB>())) void attn_
       const int d4 = idx % (D / 4);
       const int r = r0 + row;
       if (r < a.R) {
-        float4 x = *reinterpret_cast<const float4*>(buf + row * D + 4 * d4);
+        float4 x = *reinterpret_cast<const float4*>(buf + row * RS + 4 * d4);
 #pragma unroll
         for (int w = 1; w < HALF; ++w) {
-          const float4 y = *reinterpret_cast<const float4*>(buf + w * RB * D + row * D + 4 * d4);
+          const float4 y = *reinterpret_cast<const float4*>(buf + w * RB * RS + row * RS + 4 * d4);
           x.x += y.x; x.y += y.y; x.z += y.z; x.w += y.w;
         }
         const size_t prow = ((size_t)(s * a.T + row_t(r)) * a.H + row_h(r)) * a.P + p;

@@ -89,7 +89,11 @@ struct TqLds {
   static constexpr int QB = (PK ? 3 * KS : 2 * NRB * KS * 2) * 64 * 16;
   static constexpr int QS = RB * 4;                          // per-row sum of q_jl
   static constexpr int ML = NW * RB * 2 * 4;
-  static constexpr int BUF = NW / 2 * RB * D * 4;            // cross-wave combine (aliases VT, NM, QB)
+  // cross-wave combine (aliases VT, NM, QB), rows of RS = D + 4 floats: a
+  // stride of 4 mod 8 dwords keeps the parking stores of a half-wave's two
+  // lane groups in different halves of the 32 banks
+  static constexpr int RS = D + 4;
+  static constexpr int BUF = NW / 2 * RB * RS * 4;
   static constexpr int MAIN = VT + NM + QB;
   static constexpr int BYTES = (MAIN > BUF ? MAIN : BUF) + QS + ML;
 };
@@ -824,25 +828,26 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
       for (int nb = 0; nb < NB; ++nb) O[k][nb][i] *= f;
     }
   }
+  constexpr int RS = L::RS;
   if (wave >= HALF) {
-    float* b = buf + (wave - HALF) * RB * D;
+    float* b = buf + (wave - HALF) * RB * RS;
 #pragma unroll
     for (int k = 0; k < NRB; ++k)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) b[(16 * k + 4 * lb + i) * D + 16 * nb + lr] = O[k][nb][i];
+        for (int i = 0; i < 4; ++i) b[(16 * k + 4 * lb + i) * RS + 16 * nb + lr] = O[k][nb][i];
   }
   __syncthreads();
   if (wave < HALF) {
-    float* b = buf + wave * RB * D;
+    float* b = buf + wave * RB * RS;
 #pragma unroll
     for (int k = 0; k < NRB; ++k)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float* x = b + (16 * k + 4 * lb + i) * D + 16 * nb + lr;
+          float* x = b + (16 * k + 4 * lb + i) * RS + 16 * nb + lr;
           *x = *x + O[k][nb][i];
         }
   }
@@ -852,10 +857,10 @@ __global__ __launch_bounds__(256, 2) void attn_tq(TqArgs a) {
     const int d4 = idx % (D / 4);
     const int r = r0 + row;
     if (r < a.R) {
-      float4 x = *reinterpret_cast<const float4*>(buf + row * D + 4 * d4);
+      float4 x = *reinterpret_cast<const float4*>(buf + row * RS + 4 * d4);
 #pragma unroll
       for (int w = 1; w < HALF; ++w) {
-        const float4 y = *reinterpret_cast<const float4*>(buf + w * RB * D + row * D + 4 * d4);
+        const float4 y = *reinterpret_cast<const float4*>(buf + w * RB * RS + row * RS + 4 * d4);
         x.x += y.x; x.y += y.y; x.z += y.z; x.w += y.w;
       }
       const size_t prow = ((size_t)(s * a.T + row_t(r)) * a.H + row_h(r)) * a.P + p;
