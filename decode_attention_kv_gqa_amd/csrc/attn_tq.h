@@ -22,11 +22,11 @@
 // rows.  Lane group lb (lanes 16 lb .. 16 lb + 15) owns dims [lb D/4, (lb+1)
 // D/4) of every cell -- D/64 polar words and D/4 sign bits -- and covers
 // 8 of them per k-step; the query operands use the same dim assignment.
-//   polar:  each byte of an index word (four 2-bit indices) looks up the f16
-//           high and low parts of its four centroids in 256-entry LDS
-//           tables, so q_rot . c[idx] keeps ~22 bits: hi*hi + hi*lo + lo*hi.
-//   QJL:    each byte of sign bits looks up eight f16 2 / 0 values; the MFMA,
-//           its accumulator started at -sum_d q_jl[d], gives the page's
+//   polar:  each pair of 2-bit indices looks up the f16 high and low parts
+//           of its two centroids in 16-entry LDS tables, so q_rot . c[idx]
+//           keeps ~22 bits: hi*hi + hi*lo + lo*hi.
+//   QJL:    each nibble of sign bits looks up four f16 2 / 0 values; the
+//           MFMA, its accumulator started at -sum_d q_jl[d], gives the page's
 //           signed sum 2 * (sum over set bits) - sum_d q_jl[d] directly.
 // PV on the same MFMA: A = p * vnorm (f16 hi + lo) straight from the score
 // accumulators, B = decoded value fragments: a lane needs one dim of eight
