@@ -17,6 +17,7 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
 N_CASES = 128
+N_LONG = 32
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -26,26 +27,27 @@ def _need_gpu():
     import decode_attention_kv_gqa_amd  # noqa: F401
 
 
-def draw_case(i):
-    rng = np.random.default_rng(9000 + i)
+def draw_case(i, long=False):
+    """Case i of the sweep; long: windows of 700-4000 cells, budgets up to
+    1200 and splits up to 1500, so that waves run several tiles each."""
+    seed = (21000 if long else 9000) + i
+    rng = np.random.default_rng(seed)
     S = int(rng.choice([1, 2, 3, 5, 8]))
     T = int(rng.integers(1, 5))
     Hk = int(rng.integers(1, 5))
     G = int(rng.integers(1, 21))
     D = int(rng.choice([64, 128, 256]))
     kv = "i8" if rng.random() < 0.5 else "f16"
-    Lmax = int(rng.integers(0, 701))
+    Lmax = int(rng.integers(700, 4001)) if long else int(rng.integers(0, 701))
     lens = rng.integers(0, Lmax + 4, size=S)          # past Lmax clamps to the capacity
-    budget = int(rng.integers(1, 301)) if rng.random() < 0.35 else 0
-    chunk = 0 if rng.random() < 0.4 else int(rng.integers(1, 401))
+    budget = int(rng.integers(1, 1201 if long else 301)) if rng.random() < 0.35 else 0
+    chunk = 0 if rng.random() < 0.4 else int(rng.integers(1, 1501 if long else 401))
     return dict(S=S, T=T, Hk=Hk, G=G, D=D, kv=kv, Lmax=Lmax, lens=[int(x) for x in lens],
-                budget=budget, chunk=chunk, seed=9000 + i)
+                budget=budget, chunk=chunk, seed=seed)
 
 
-@pytest.mark.parametrize("i", range(N_CASES))
-def test_random_shape(i):
+def run_case(c, i):
     import decode_attention_kv_gqa_amd as gq
-    c = draw_case(i)
     inp = make_case(c["S"], c["T"], c["G"] * c["Hk"], c["Hk"], c["D"], c["Lmax"], c["lens"],
                     kv=c["kv"], budget=c["budget"], seed=c["seed"])
     print(f"[gpu] sweep case {i}: {c}", flush=True)
@@ -57,3 +59,15 @@ def test_random_shape(i):
     ref = R.gqa_decode_ref(inp.q, inp.k, inp.v, inp.seq_lens, inp.scale, inp.k_scales,
                            inp.v_scales, inp.ids)
     assert_parity(out.cpu().numpy(), ref, f"sweep case {i} {c}")
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_shape(i):
+    run_case(draw_case(i), i)
+
+
+@pytest.mark.parametrize("i", range(N_LONG))
+def test_random_long_window(i):
+    """Windows of 700-4000 cells: several tiles per wave, the last one
+    requesting nothing past the split."""
+    run_case(draw_case(i, long=True), i)

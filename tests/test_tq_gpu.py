@@ -143,16 +143,18 @@ def test_tq_step_replays_under_graph_capture():
         assert torch.equal(step.out, eager)
 
 
-def _sweep_case(i):
-    rng = np.random.default_rng(8000 + i)
+def _sweep_case(i, long=False):
+    """Case i of the sweep; long: windows of 800-4000 cells and splits up to
+    1500, so that waves run several tiles each."""
+    rng = np.random.default_rng((31000 if long else 8000) + i)
     S = int(rng.integers(1, 5))
     T = int(rng.integers(1, 4))
     Hk = int(rng.integers(1, 5))
     G = int(rng.integers(1, 13))
     D = int(rng.choice([64, 128]))
-    Lmax = int(rng.integers(0, 801))
+    Lmax = int(rng.integers(800, 4001)) if long else int(rng.integers(0, 801))
     lens = [int(x) for x in rng.integers(0, Lmax + 3, size=S)]
-    chunk = 0 if rng.random() < 0.4 else int(rng.integers(1, 301))
+    chunk = 0 if rng.random() < 0.4 else int(rng.integers(1, 1501 if long else 301))
     return S, T, Hk, G, D, Lmax, lens, chunk
 
 
@@ -166,3 +168,13 @@ def test_tq_random_shapes(i):
           f"chunk={chunk}", flush=True)
     inp = make_tq_case(S, T, G * Hk, Hk, D, Lmax, lens, seed=8000 + i)
     assert_parity(run_tq(inp, chunk), oracle(inp), f"tq sweep {i}")
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_tq_random_long_window(i):
+    """Windows of 800-4000 cells against the oracle (several tiles per wave)."""
+    S, T, Hk, G, D, Lmax, lens, chunk = _sweep_case(i, long=True)
+    print(f"[gpu] tq long sweep {i}: S={S} T={T} Hk={Hk} G={G} D={D} Lmax={Lmax} lens={lens} "
+          f"chunk={chunk}", flush=True)
+    inp = make_tq_case(S, T, G * Hk, Hk, D, Lmax, lens, seed=31000 + i)
+    assert_parity(run_tq(inp, chunk), oracle(inp), f"tq long sweep {i}")
