@@ -185,6 +185,24 @@ def test_unsorted_ids_and_multi_token_ids():
     assert_parity(run_gpu(inp, chunk=16), oracle(inp), "unsorted ids, 3 tokens")
 
 
+@pytest.mark.parametrize("kv", ["f16", "i8"])
+def test_out_of_range_ids_are_clamped(kv):
+    # ids must lie in [0, L_t) (the header's precondition); one outside
+    # [0, Lmax) is clamped on the device, so it reads cell 0 or Lmax - 1 and
+    # never an address past the cache: the output equals the oracle's over
+    # the clamped ids
+    inp = make_case(2, 2, 8, 2, 128, 300, [300, 120], kv=kv, budget=64, seed=41)
+    bad = inp.ids.copy()
+    bad[0, 0, 3] = -5
+    bad[0, 1, 10] = 300
+    bad[1, 1, 7] = 1 << 30
+    bad[1, 0, 0] = -(1 << 30)
+    inp.ids = bad
+    got = run_gpu(inp, chunk=16)
+    inp.ids = np.clip(bad, 0, 299).astype(np.int32)
+    assert_parity(got, oracle(inp), f"clamped ids kv={kv}")
+
+
 def test_large_scores_stay_finite():
     inp = make_case(1, 1, 8, 2, 128, 500, [500], kv="f16", seed=3, scale=4.0)
     got = run_gpu(inp, chunk=64)
