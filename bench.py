@@ -573,6 +573,71 @@ def measure_attention(name, chunk, steps, warmup, dev, gate=False, copies=0, col
     return res, inp
 
 
+def launch_floor():
+    """How long a launch takes that does the int8 32K merge's memory work and
+    no arithmetic: gqa_bench_stream_read over 3 MiB with 192 workgroups (the
+    merge reads 192 rows x 16 partials of 1 KB), and over 16 KiB with one
+    workgroup.  Each shape is timed one launch at a time (HIP events around a
+    single launch, synchronised between launches; median of 200) and back to
+    back (mean over 200).  Then runs the int8 32K merge alone and attention +
+    merge steps, for a kernel trace to compare."""
+    import statistics
+    import torch
+    import decode_attention_kv_gqa_amd as gq
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, nbytes, wg in (("merge_shape", 3 << 20, 192), ("one_workgroup", 16 << 10, 1)):
+        buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+        sink = torch.zeros(wg, dtype=torch.int32, device=dev)
+
+        def launch():
+            rc = gq.gqa_bench_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), wg,
+                                          stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"gqa_bench_stream_read: {gq.strerror(rc)}")
+        for _ in range(50):
+            launch()
+        torch.cuda.synchronize()
+        single = []
+        for _ in range(200):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            launch()
+            e1.record(stream)
+            e1.synchronize()
+            single.append(e0.elapsed_time(e1) * 1e3)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(200):
+            launch()
+        e1.record(stream)
+        e1.synchronize()
+        res[name] = {"bytes": nbytes, "workgroups": wg,
+                     "us_single_p50": round(statistics.median(single), 3),
+                     "us_back_to_back": round(e0.elapsed_time(e1) * 1e3 / 200, 3)}
+    # the int8 32K merge on its own, 300 times over one set of partials, then
+    # 100 attention + merge steps: a kernel trace of this run gives the
+    # merge's duration on partials it has read before and right after the
+    # attention launch that wrote them
+    from workloads import make_inputs
+    inp = make_inputs("i8_32k")
+    dd = lambda x: None if x is None else torch.from_numpy(x).to(dev)
+    q, k, v, ks, vs, sl = (dd(inp.q), dd(inp.k), dd(inp.v), dd(inp.k_scales), dd(inp.v_scales),
+                           dd(inp.seq_lens))
+    S, T, H, D = inp.q.shape
+    step = gq.DecodeAttention(S, T, H, inp.k.shape[2], D, inp.k.shape[1], "i8")
+    for _ in range(20):
+        step(q, k, v, sl, inp.scale, ks, vs)
+    torch.cuda.synchronize()
+    for _ in range(300):
+        step.merge(sl)
+    for _ in range(100):
+        step(q, k, v, sl, inp.scale, ks, vs)
+    torch.cuda.synchronize()
+    print(json.dumps({"launch_floor": res}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -589,9 +654,15 @@ def main():
     ap.add_argument("--copies", type=int, default=0, help="input replicas to rotate through")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (HBM counter calibration)")
+    ap.add_argument("--launch-floor", action="store_true",
+                    help="only time a streaming read doing the int8 32K merge's memory work "
+                         "(and a one-workgroup read): the cost of a launch that reads memory")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.launch_floor:
+        launch_floor()
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
