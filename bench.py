@@ -313,28 +313,35 @@ def bench_append(args):
 
 
 def bench_tq(args):
+    """Decode step over a TurboQuant-compressed cache: one JSON line."""
+    import torch
+    print(json.dumps(measure_tq(args.workload, args.chunk, args.steps, args.warmup,
+                                torch.device("cuda:0"), args.copies)), flush=True)
+
+
+def measure_tq(workload, chunk, steps, warmup, dev, copies_arg=0):
     """Decode step over a TurboQuant-compressed cache (gqa_decode_attn_tq +
     gqa_decode_merge_tq): compressed cache resident in HBM, copies rotated so
     no step finds its cache in the last-level cache; K steps timed by wall
-    clock, the chunk kernel alone by HIP events over bursts.  One JSON line."""
+    clock, the chunk kernel alone by HIP events over bursts.  Returns the
+    result dict."""
     import numpy as np
     import torch
     import decode_attention_kv_gqa_amd as gq
-    from workloads import TQ_WORKLOADS, make_tq_inputs, tq_bytes
-    inp = make_tq_inputs(args.workload)
+    from workloads import make_tq_inputs, tq_bytes
+    inp = make_tq_inputs(workload)
     sh = inp.shape
     nbytes = tq_bytes(inp)
-    dev = torch.device("cuda:0")
     d = lambda x: torch.from_numpy(np.ascontiguousarray(x.view(np.int32) if x.dtype == np.uint32
                                                         else x)).to(dev)
     foot = sum(x.nbytes for x in (inp.k_polar, inp.k_jl, inp.k_norms, inp.v_polar, inp.v_norms))
-    copies = args.copies or max(2, min(8, math.ceil(3 * LLC_BYTES / foot) + 1))
+    copies = copies_arg or max(2, min(8, math.ceil(3 * LLC_BYTES / foot) + 1))
     sets = [dict(q_rot=d(inp.q_rot), q_jl=d(inp.q_jl), k_polar=d(inp.k_polar), k_jl=d(inp.k_jl),
                  k_norms=d(inp.k_norms), v_polar=d(inp.v_polar), v_norms=d(inp.v_norms))
             for _ in range(copies)]
     lens, signs = d(inp.seq_lens), d(inp.signs)
     step = gq.TqDecodeAttention(sh["S"], sh["T"], sh["H"], sh["Hk"], sh["D"], sh["Lmax"],
-                                chunk=max(0, args.chunk), device=dev)
+                                chunk=max(0, chunk), device=dev)
 
     def attn(i):
         x = sets[i % copies]
@@ -345,7 +352,7 @@ def bench_tq(args):
         attn(i)
         step.merge(lens, signs)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         one(i)
     torch.cuda.synchronize()
     t_w, extra = time.perf_counter(), 0
@@ -354,7 +361,7 @@ def bench_tq(args):
             one(i)
         extra += 10
         torch.cuda.synchronize()
-    K = args.steps
+    K = steps
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
@@ -379,7 +386,7 @@ def bench_tq(args):
     # x 2.4 GHz / 4 cycles per instruction = 614.4 G/s.  The instruction count
     # per launch comes from the rocprofv3 SQ_INSTS_VALU run kept in profiles/
     # (null once the kernel source changes); the HBM view is reported beside it.
-    rec = load_traffic_record(args.workload, "tq")
+    rec = load_traffic_record(workload, "tq")
     valu = rec.get("valu_wave_instructions_per_launch") if rec else None
     hbm = {"achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
            "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -393,15 +400,15 @@ def bench_tq(args):
     if valu:
         roof["achieved"] = round(valu / kern_s / 1e9, 2)
         roof["frac"] = round(valu / kern_s / 1e9 / VALU_ISSUE_PEAK_G, 4)
-    print(json.dumps({
+    return {
         "metric": "TurboQuant-cache decode effective cache GB/s and us/step, 1 MI355X",
         "value": round(nbytes / (wall / K) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
-        "warmup": args.warmup, "extra_warmup_steps": extra, "us_per_step": round(wall / K * 1e6, 2),
+        "warmup": warmup, "extra_warmup_steps": extra, "us_per_step": round(wall / K * 1e6, 2),
         "higher_is_better": True, "dtype": "2-bit polar + 1-bit QJL codes, f16 norms",
         "data": "synthetic (seeded numpy: uniform codes, f16 norms, N(0,1) rotated queries)",
-        "config": {"workload": args.workload, **sh, "chunk": step.chunk,
+        "config": {"workload": workload, **sh, "chunk": step.chunk,
                    "cache_bytes_per_step": nbytes, "input_copies_rotated": copies},
-        "roofline": roof}), flush=True)
+        "roofline": roof}
 
 
 def measure_attention(name, chunk, steps, warmup, dev, gate=False, copies=0, cold=20,
@@ -743,6 +750,21 @@ def main():
                 "kernel_frac_of_stream_read": r["stream_read"]["kernel_frac_of_stream_read"],
                 "stream_read_GBps": r["stream_read"]["gbs"],
                 "traffic": r["traffic"], "traffic_over_algorithmic": r["traffic_over_algorithmic"]}
+        # the decode over a TurboQuant-compressed cache (its own metric: GB/s
+        # of codes; bound by instruction issue, so the VALU fraction beside)
+        for name in TQ_WORKLOADS:
+            o = measure_tq(name, -1, min(args.steps, 100), min(args.warmup, 10), dev)
+            r = o["roofline"]
+            res["workloads"][name] = {
+                "description": "TurboQuant-compressed cache: 4 seqs at context 131072, 32/8 heads, "
+                               "hd 128, 2-bit polar keys/values + 1-bit QJL signs",
+                "chunk": o["config"]["chunk"],
+                "cache_bytes_per_step": o["config"]["cache_bytes_per_step"],
+                "us_per_step": o["us_per_step"], "step_GBps": o["value"],
+                "step_frac_of_peak": round(o["value"] / HBM_PEAK_GBS, 4),
+                "kernel_us_mean": r["kernel_us_mean"], "kernel_GBps": r["hbm_view"]["achieved"],
+                "kernel_frac_of_peak": r["hbm_view"]["frac"],
+                "kernel_valu_frac_of_issue_peak": r["frac"], "traffic": r["traffic"]}
     print(json.dumps(res), flush=True)
 
 
