@@ -229,51 +229,60 @@ def stream_read_rate(nbytes: int, dev, shapes=(256, 512, 1024, 2048), reps: int 
 
 
 def bench_select(args):
+    """Budget-selection kernel alone: one JSON line."""
+    print(json.dumps(measure_select(args.workload, args.steps, args.warmup)), flush=True)
+
+
+def measure_select(workload, steps, warmup):
     """Budget-selection kernel alone (gqa_decode_select_ids) on a selection
     workload: block scores resident in HBM, K launches timed with HIP events
-    after W warm-up launches.  One JSON line."""
-    import numpy as np
+    after W warm-up launches.  Returns the result dict."""
     import torch
     import decode_attention_kv_gqa_amd as gq
     from workloads import SELECT_WORKLOADS, make_block_scores
-    w = SELECT_WORKLOADS[args.workload]
+    w = SELECT_WORKLOADS[workload]
     S, T, Lmax, B = w["S"], w["T"], w["Lmax"], w["B"]
     dev = torch.device("cuda:0")
     bs = torch.from_numpy(make_block_scores(S, T, Lmax, seed=1000 + w["index"])).to(dev)
     lens = torch.full((S,), Lmax, dtype=torch.int32, device=dev)
     out = torch.full((S, T, B), -1, dtype=torch.int32, device=dev)
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         gq.select_ids(bs, lens, B, out=out, Lmax=Lmax)
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     stream = torch.cuda.current_stream()
     a.record(stream)
-    for _ in range(args.steps):
+    for _ in range(steps):
         gq.select_ids(bs, lens, B, out=out, Lmax=Lmax)
     b.record(stream)
     torch.cuda.synchronize()
-    us = a.elapsed_time(b) / args.steps * 1e3
+    us = a.elapsed_time(b) / steps * 1e3
     nbytes = S * T * ((Lmax // 4 + 1) * 4 + B * 4)    # scores read once + ids written
-    print(json.dumps({
+    return {
         "metric": "budget selection us per call", "value": round(us, 3), "unit": "us",
-        "higher_is_better": False, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "higher_is_better": False, "n_gpus": 1, "steps": steps, "warmup": warmup,
         "dtype": "f32 keys", "data": "synthetic (seeded numpy: block scores N(0,1) fp32)",
-        "config": {"workload": args.workload, "S": S, "T": T, "Lmax": Lmax, "budget": B,
+        "config": {"workload": workload, "S": S, "T": T, "Lmax": Lmax, "budget": B,
                    "algorithmic_bytes": nbytes},
         "roofline": {"bound": "hbm", "achieved": round(nbytes / us / 1e3, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 5), "traffic": None,
-                     "note": "one workgroup per token; latency-bound at this size"}}), flush=True)
+                     "note": "one workgroup per token; latency-bound at this size"}}
 
 
 def bench_append(args):
+    """Quantize-on-append kernel alone: one JSON line."""
+    print(json.dumps(measure_append(args.workload, args.steps, args.warmup)), flush=True)
+
+
+def measure_append(workload, steps, warmup):
     """Quantize-on-append kernel alone (gqa_decode_append_i8): new fp32 rows
     and the int8 cache resident in HBM, K launches timed with HIP events
-    after W warm-up launches.  One JSON line."""
+    after W warm-up launches.  Returns the result dict."""
     import torch
     import decode_attention_kv_gqa_amd as gq
     from workloads import APPEND_WORKLOADS, make_append_rows
-    w = APPEND_WORKLOADS[args.workload]
+    w = APPEND_WORKLOADS[workload]
     S, Tn, Hk, D, Lmax = w["S"], w["Tn"], w["Hk"], w["D"], w["Lmax"]
     dev = torch.device("cuda:0")
     rows = make_append_rows(S, Tn, Hk, D, seed=1000 + w["index"])
@@ -286,30 +295,30 @@ def bench_append(args):
     v = torch.zeros_like(k)
     ks = torch.zeros((S, Lmax, Hk, D // 64), dtype=torch.float16, device=dev)
     vs = torch.zeros_like(ks)
-    for i in range(args.warmup):
+    for i in range(warmup):
         gq.append_i8(*sets[i % copies], pos, k, v, ks, vs)
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     stream = torch.cuda.current_stream()
     a.record(stream)
-    for i in range(args.steps):
+    for i in range(steps):
         gq.append_i8(*sets[i % copies], pos, k, v, ks, vs)
     b.record(stream)
     torch.cuda.synchronize()
-    us = a.elapsed_time(b) / args.steps * 1e3
+    us = a.elapsed_time(b) / steps * 1e3
     elems = 2 * S * Tn * Hk * D
     nbytes = elems * 4 + elems + elems // 64 * 2           # fp32 read, codes + scales written
     achieved = nbytes / us / 1e3
-    print(json.dumps({
+    return {
         "metric": "quantize-on-append GB/s", "value": round(achieved, 2), "unit": "GB/s",
-        "higher_is_better": True, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "higher_is_better": True, "n_gpus": 1, "steps": steps, "warmup": warmup,
         "us_per_call": round(us, 3), "dtype": "f32 -> i8",
         "data": "synthetic (seeded numpy: new rows N(0,1) fp32)",
-        "config": {"workload": args.workload, "S": S, "Tn": Tn, "Hk": Hk, "D": D, "Lmax": Lmax,
+        "config": {"workload": workload, "S": S, "Tn": Tn, "Hk": Hk, "D": D, "Lmax": Lmax,
                    "algorithmic_bytes": nbytes, "input_copies_rotated": copies},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": load_traffic(args.workload, "append")}}), flush=True)
+                     "traffic": load_traffic(workload, "append")}}
 
 
 def bench_tq(args):
@@ -765,6 +774,18 @@ def main():
                 "kernel_us_mean": r["kernel_us_mean"], "kernel_GBps": r["hbm_view"]["achieved"],
                 "kernel_frac_of_peak": r["hbm_view"]["frac"],
                 "kernel_valu_frac_of_issue_peak": r["frac"], "traffic": r["traffic"]}
+        # the two kernels beside the decode: budget selection and
+        # quantize-on-append (each alone, HIP events around 200 launches)
+        for name in SELECT_WORKLOADS:
+            o = measure_select(name, 200, 20)
+            res["workloads"][name] = {"kernel": "select_ids", "us_per_call": o["value"],
+                                      "config": o["config"], "GBps": o["roofline"]["achieved"]}
+        for name in APPEND_WORKLOADS:
+            o = measure_append(name, 200, 20)
+            res["workloads"][name] = {"kernel": "append_i8", "us_per_call": o["us_per_call"],
+                                      "config": o["config"], "GBps": o["value"],
+                                      "frac_of_peak": o["roofline"]["frac"],
+                                      "traffic": o["roofline"]["traffic"]}
     print(json.dumps(res), flush=True)
 
 
