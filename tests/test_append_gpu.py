@@ -76,6 +76,66 @@ def test_append_half_way_codes():
     assert np.array_equal(got[0], ref[0]) and list(got[0][0, 1, 0, :9]) == [127, 0, 2, 2, 0, -2, -2, 126, -126]
 
 
+def _append_exact(x, Lmax=4, pos=1):
+    """Append x [S][Tn][Hk][D] as both K and V; codes and scales must equal
+    the oracle's bit for bit."""
+    S, Tn, Hk, D = x.shape
+    k = np.zeros((S, Lmax, Hk, D), dtype=np.int8)
+    ks = np.zeros((S, Lmax, Hk, D // 64), dtype=np.float16)
+    p = np.full(S, pos, dtype=np.int32)
+    got = run_append(x, x, p, k, k.copy(), ks, ks.copy())
+    ref = AR.append_i8(x, x, p, k, k.copy(), ks, ks.copy())
+    for name, g, r in zip(("k", "v", "k_scales", "v_scales"), got, ref):
+        assert np.array_equal(g.view(np.uint8 if g.dtype == np.int8 else np.uint16),
+                              r.view(np.uint8 if r.dtype == np.int8 else np.uint16)), name
+    return got
+
+
+def test_append_quotients_next_to_half_integers():
+    # x / d within a few ulp of k + 1/2 for many k and scales: the codes
+    # still follow the IEEE quotient rounded half to even
+    rng = np.random.default_rng(77)
+    rows = []
+    for scale in (1.0, 0.37, 3.1e-3, 7.7e4, 1.3e-20):
+        m = np.float32(127.0 * scale)
+        d = np.float32(m / np.float32(127.0))
+        for _ in range(8):
+            ks = rng.integers(-127, 127, size=63) + 0.5
+            x = (ks * np.float64(d)).astype(np.float32)
+            steps = rng.integers(-3, 4, size=63)
+            x = np.array([np.float32(v) if t == 0 else
+                          np.nextafter(np.float32(v), np.float32(np.sign(t) * np.inf), dtype=np.float32)
+                          if abs(t) == 1 else
+                          (np.float32(v) + np.float32(t) * np.spacing(np.float32(v))).astype(np.float32)
+                          for v, t in zip(x, steps)], dtype=np.float32)
+            x = np.clip(x, -m, m)
+            rows.append(np.concatenate([[m], x]).astype(np.float32))
+    x = np.stack(rows).reshape(1, len(rows), 1, 64)
+    got = _append_exact(x, Lmax=len(rows) + 2, pos=1)
+    assert np.count_nonzero(got[0]) > 0
+
+
+def test_append_tiny_and_subnormal_groups():
+    # groups whose max |x| is subnormal, at and around 2^-100, and normal
+    rng = np.random.default_rng(78)
+    mags = np.array([1e-45, 3e-42, 1e-40, 1.1754942e-38, 2.0 ** -126, 2.0 ** -101,
+                     2.0 ** -100 * (1 - 2.0 ** -23), 2.0 ** -100, 2.0 ** -100 * (1 + 2.0 ** -23),
+                     1e-30, 1.0, 1e37], dtype=np.float64)
+    x = (rng.standard_normal((1, len(mags), 1, 128)) * mags[None, :, None, None])
+    x = x.astype(np.float32)
+    assert np.isfinite(x).all()                    # finite inputs only (the contract)
+    x[0, 0, 0, :3] = [1e-45, -1e-45, 0.0]          # the smallest subnormals
+    _append_exact(x, Lmax=len(mags) + 1, pos=0)
+
+
+def test_append_bench_shape():
+    # the quantize-on-append workload as the bench times it: 8 sequences x
+    # 4096 new rows, 2 KV heads, head_dim 256, into a 32768-cell cache at 16384
+    w = APPEND_WORKLOADS["append_i8"]
+    check(w["S"], w["Tn"], w["Hk"], w["D"], w["Lmax"], [w["pos"]] * w["S"],
+          seed=1000 + w["index"])
+
+
 def test_append_workload_full_size():
     w = APPEND_WORKLOADS["append_i8"]
     S, Tn, Hk, D, Lmax = w["S"], 512, w["Hk"], w["D"], 2048   # the workload's rows, a smaller cache
