@@ -18,11 +18,12 @@
 //      wave finds the digit itself (lane sums of 64 or 16 counters, a wave
 //      prefix sum to find the lane, a second one over that lane's counters).
 //      Up to 16 keys per thread stay in registers across the passes.
-//   2. Emission: every thread owns a contiguous block range; one block-wide
-//      prefix sum of its counts of blocks above and at Tk gives each thread
-//      its share of the Tk blocks (in block order) and its output offset,
-//      so the ids come out ascending.  The keys come from LDS, and the ids
-//      are gathered in LDS and written to memory in one coalesced pass.
+//   2. Emission: every thread owns a contiguous block range and marks, one
+//      bit per block, the blocks above and at Tk; popcounts of the two masks
+//      and one block-wide prefix sum give each thread its share of the Tk
+//      blocks (in block order) and its output offset, so the ids come out
+//      ascending.  The keys come from LDS, and the ids are gathered in LDS
+//      and written to memory in one coalesced pass.
 // The page's kernel makes the same two phases on Apple simdgroups; here the
 // scans are wave64 DPP moves and the histogram lives in LDS.
 #include <hip/hip_runtime.h>
@@ -113,13 +114,20 @@ template <int BINS>
 __device__ __forceinline__ void find_digit(const uint32_t* h, uint32_t need, int lane,
                                            uint32_t& digit, uint32_t& left) {
   constexpr int W = BINS / 64;
-  // lane l's counters are h[BINS - (l+1) W .. BINS - l W); lane l starts its
-  // walk l places in, which spreads the lanes of one read over the banks
-  // (without the skew every lane would read the same bank)
+  // lane l's counters are h[BINS - (l+1) W .. BINS - l W), read four at a
+  // time (16-byte reads); lane l starts its walk l (or l / 2) chunks in, so
+  // that any eight consecutive lanes of one read cover all 32 banks (without
+  // the skew every lane would read the same bank)
   const uint32_t* mine = h + BINS - (lane + 1) * W;
+  constexpr int NC = W / 4;
+  const int sk = NC >= 8 ? lane : (lane >> 1);
   uint32_t lsum = 0;
 #pragma unroll
-  for (int j = 0; j < W; ++j) lsum += mine[(j + lane) & (W - 1)];
+  for (int j = 0; j < NC; ++j) {
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+    const u4 v = *reinterpret_cast<const u4*>(mine + 4 * ((j + sk) & (NC - 1)));
+    lsum += v[0] + v[1] + v[2] + v[3];
+  }
   const uint32_t above = wave_incl_scan(lsum) - lsum;   // cells in higher digits
   const uint64_t hit = __ballot(above < need && above + lsum >= need);
   const int L = hit ? __builtin_ctzll(hit) : 0;
@@ -148,14 +156,21 @@ __global__ __launch_bounds__(kSelThreads) void select_ids(SelArgs a) {
 
   // Keys: 16 blocks per thread (b = tid + 1024 i) in registers for the radix
   // passes, and the first kKeysInLds blocks also in LDS for the emission;
-  // blocks past both are re-read from memory.  The loads cover the whole
-  // score row and do not wait for the sequence length, so the two memory
-  // round trips overlap; keys past the window are never counted.
+  // blocks past both are re-read from memory.  The 16 loads are unconditional
+  // (indices clamped to the row), so all are in flight at once; they cover
+  // the whole score row and do not wait for the sequence length, so the two
+  // memory round trips overlap; keys past the window are never counted.
   uint32_t kr[kKeysInRegs];
+  float kv[kKeysInRegs];
+#pragma unroll
+  for (int i = 0; i < kKeysInRegs; ++i) {   // unconditional (clamped) loads, all in flight
+    const int b = tid + kSelThreads * i;
+    kv[i] = sc[b < a.nbs ? b : a.nbs - 1];
+  }
 #pragma unroll
   for (int i = 0; i < kKeysInRegs; ++i) {
     const int b = tid + kSelThreads * i;
-    kr[i] = b < a.nbs ? okey(sc[b]) : 0u;
+    kr[i] = b < a.nbs ? okey(kv[i]) : 0u;
     if (b < a.nbs && b < kKeysInLds) keyl[b] = kr[i];
   }
   for (int b = tid + kSelThreads * kKeysInRegs; b < a.nbs && b < kKeysInLds; b += kSelThreads)
@@ -217,20 +232,33 @@ __global__ __launch_bounds__(kSelThreads) void select_ids(SelArgs a) {
   };
   if (staged && nb <= kKeysInLds) {
     // every key is in LDS, a thread's range has at most kMaxPer blocks, and
-    // the ids go to LDS.  The counting loop has a fixed length and no
-    // branches (a range's reads may run up to kMaxPer - 1 keys past the last
-    // block, into the kKeyPad padding; those keys count no cells); it also
-    // marks the blocks with a key >= Tk, and the writing loop visits only
-    // those -- a few per thread when B is a small part of the window.
-    uint32_t gt = 0, eq = 0, cand = 0;
-#pragma unroll
-    for (int i = 0; i < kMaxPer; ++i) {
-      const int b = b0 + i;
-      const uint32_t k = keyl[b];
-      const uint32_t cells = b < b1 ? cells_of(b) : 0u;
-      gt += k > Tk ? cells : 0u;
-      eq += k == Tk ? cells : 0u;
-      cand |= (k >= Tk && cells) ? 1u << i : 0u;
+    // the ids go to LDS.  The counting loop runs `per` times for every thread
+    // (a range's reads may run up to per - 1 keys past the last block, into
+    // the kKeyPad padding; the `valid` mask drops them) and only sets bits;
+    // the counts are popcounts, and the writing loop visits only the blocks
+    // with a key >= Tk -- a few per thread when B is a small part of the
+    // window.
+    // bit i of cand / eqm: block b0 + i has a key >= Tk / == Tk; per is
+    // uniform, so the loop is a scalar loop with no divergence
+    uint32_t cand = 0, eqm = 0;
+#pragma unroll 4
+    for (int i = 0; i < per; ++i) {
+      const uint32_t k = keyl[b0 + i];
+      cand |= (k >= Tk ? 1u : 0u) << i;
+      eqm |= (k == Tk ? 1u : 0u) << i;
+    }
+    const int cnt = b1 - b0;
+    const uint32_t valid = cnt >= 32 ? ~0u : ((1u << cnt) - 1u);
+    cand &= valid;
+    eqm &= valid;
+    uint32_t gt = 4u * (uint32_t)__builtin_popcount(cand & ~eqm);
+    uint32_t eq = 4u * (uint32_t)__builtin_popcount(eqm);
+    if (n_bid >= b0 && n_bid < b1) {     // this range holds the partial block n_bid (rem cells)
+      const uint32_t bit = 1u << (n_bid - b0);
+      const uint32_t d = 4u - (uint32_t)rem;
+      if (cand & ~eqm & bit) gt -= d;
+      if (eqm & bit) eq -= d;
+      if (rem == 0) { cand &= ~bit; eqm &= ~bit; }   // no cells: never emitted
     }
     uint32_t gt_before, eq_before;
     block_excl_scan2(gt, eq, wsum, tid, gt_before, eq_before);
