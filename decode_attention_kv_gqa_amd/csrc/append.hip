@@ -138,9 +138,10 @@ extern "C" int gqa_decode_append_i8(const float* k_new, const float* v_new, cons
   a.gps = (int64_t)Tn * Hk * (D / 64);
   a.S = S; a.Tn = Tn; a.Lmax = Lmax; a.Hk = Hk; a.D = D;
   const int64_t bps = (a.gps + kAppGroupsPerBlock - 1) / kAppGroupsPerBlock;
-  if (bps > 0x7fffffff || 2 * S * bps > 0x7fffffff) return GQA_ERR_SHAPE;
+  const int64_t blocks = (int64_t)2 * S * bps;    // K and V, every sequence
+  if (bps > 0x7fffffff || blocks > 0x7fffffff) return GQA_ERR_SHAPE;
   a.bps = (int)bps;
-  hipLaunchKernelGGL(append_i8, dim3((unsigned)(2 * S * bps)), dim3(64), 0,
+  hipLaunchKernelGGL(append_i8, dim3((unsigned)blocks), dim3(64), 0,
                      reinterpret_cast<hipStream_t>(stream), a);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? GQA_OK : (int)e;

@@ -171,6 +171,10 @@ def test_append_rejects():
     assert f(*args, 1, 1, 16, 2, 96, 0) == _lib.GQA_ERR_HEAD_DIM
     assert f(*([None] + [FAKE] * 6), 1, 1, 16, 2, 64, 0) == _lib.GQA_ERR_NULL
     assert f(*([None] * 7), 1, 0, 16, 2, 64, 0) == _lib.GQA_OK      # nothing to write
+    # a grid past 2^31 - 1 workgroups (8 groups each, K and V): refused
+    # before any launch; S = 2^30 overflows a 32-bit 2 * S
+    assert f(*args, 1 << 30, 1, 16, 1, 64, 0) == _lib.GQA_ERR_SHAPE
+    assert f(*args, 1, 1 << 30, 16, 8, 64, 0) == _lib.GQA_ERR_SHAPE
 
 
 def test_stream_read_rejects():
