@@ -68,6 +68,17 @@ def test_select_long_windows(Lmax):
     check(bs, np.array([Lmax, Lmax - 3], dtype=np.int32), 1, Lmax, 2048)
 
 
+@pytest.mark.parametrize("Lmax,B,ties", [(65536, 4096, True), (65536, 4097, False),
+                                         (65536, 5000, True), (131072, 9000, False),
+                                         (131072, 4097, True)])
+def test_select_budgets_past_the_lds_staging(Lmax, B, ties):
+    # budgets above 4096 write their ids straight to memory instead of
+    # through LDS; 131072 cells also exceed the keys the kernel keeps in LDS
+    bs = make_block_scores(2, 2, Lmax, seed=Lmax + B, ties=ties)
+    lens = np.array([Lmax, Lmax - 5], dtype=np.int32)
+    check(bs, lens, 2, Lmax, B)
+
+
 def test_select_workload_full_size():
     w = SELECT_WORKLOADS["select_64k"]
     bs = make_block_scores(w["S"], w["T"], w["Lmax"], seed=1000 + w["index"])
