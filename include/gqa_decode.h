@@ -251,8 +251,11 @@ int gqa_decode_select_ids(const float *block_scores, const int32_t *seq_lens, in
  *                       [0, Lmax) are skipped (a bad position only truncates)
  *   k, v                [S][Lmax][Hk][D] int8 caches (rows written in place)
  *   k_scales, v_scales  [S][Lmax][Hk][D/64] f16 bits (written in place)
- * Tn == 0 or Lmax == 0 enqueues nothing.  Errors: GQA_ERR_NULL, _SHAPE,
- * _HEAD_DIM (D not a positive multiple of 64). */
+ * The new rows must be finite (codes and scales of a group holding inf or
+ * NaN are unspecified).  Tn == 0 or Lmax == 0 enqueues nothing.  Errors:
+ * GQA_ERR_NULL, _SHAPE (also when the 2 S Tn Hk D/64 groups need more than
+ * 2^31 - 1 eight-group workgroups), _HEAD_DIM (D not a positive multiple of
+ * 64). */
 int gqa_decode_append_i8(const float *k_new, const float *v_new, const int32_t *pos,
                          int8_t *k, int8_t *v, uint16_t *k_scales, uint16_t *v_scales,
                          int S, int Tn, int Lmax, int Hk, int D, void *stream);
