@@ -324,7 +324,8 @@ def measure_append(workload, steps, warmup):
 def bench_tq(args):
     """Decode step over a TurboQuant-compressed cache: one JSON line."""
     import torch
-    print(json.dumps(measure_tq(args.workload, args.chunk, args.steps, args.warmup,
+    chunk = -1 if args.chunk is None else args.chunk
+    print(json.dumps(measure_tq(args.workload, chunk, args.steps, args.warmup,
                                 torch.device("cuda:0"), args.copies)), flush=True)
 
 
@@ -435,7 +436,7 @@ def measure_attention(name, chunk, steps, warmup, dev, gate=False, copies=0, col
     from workloads import WORKLOADS, make_inputs, kv_bytes
 
     w = WORKLOADS[name]
-    chunk = w.chunk if chunk < 0 else chunk
+    chunk = w.chunk if chunk is None else chunk
     t_gen = time.perf_counter()
     inp = make_inputs(name)
     step_bytes = kv_bytes(inp)
@@ -660,7 +661,11 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="i8_32k")
-    ap.add_argument("--chunk", type=int, default=-1, help="cells per split (-1: the workload's)")
+    ap.add_argument("--chunk", type=int, default=None,
+                    help="cells per split (default: the workload's); 0: the library's choice")
+    ap.add_argument("--pieces", type=int, default=0,
+                    help="balanced partition: the batch's windows cut into P pieces per KV head "
+                         "(dense workloads; overrides --chunk)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="measure only the named workload (by default the int8 32K headline "
@@ -704,7 +709,8 @@ def main():
         return
     dev = torch.device("cuda:0")
     w = WORKLOADS[args.workload]
-    m, inp = measure_attention(args.workload, args.chunk, args.steps, args.warmup, dev,
+    chunk = -args.pieces if args.pieces > 0 else args.chunk
+    m, inp = measure_attention(args.workload, chunk, args.steps, args.warmup, dev,
                                gate=args.gate, copies=args.copies)
     sh = inp.shape
     res = {
@@ -738,14 +744,14 @@ def main():
         print("[bench] timing the fp64 oracle on the host", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(inp)
     del inp
-    if not args.no_other_workloads and not args.gate and args.chunk < 0:
+    if not args.no_other_workloads and not args.gate and chunk is None:
         # every other configuration, measured the same way with fewer steps
         # (no CPU baseline); the line's value stays the named workload's
         res["workloads"] = {}
         for name in WORKLOAD_ORDER:
             if name == args.workload:
                 continue
-            o, _ = measure_attention(name, -1, min(args.steps, 100), min(args.warmup, 10), dev,
+            o, _ = measure_attention(name, None, min(args.steps, 100), min(args.warmup, 10), dev,
                                      cold=10)
             r = o["roofline"]
             res["workloads"][name] = {

@@ -42,10 +42,13 @@ class DecodeAttention:
     hipStream_t).  The per-call path is argument marshalling only."""
 
     def __init__(self, S, T, H, Hk, D, Lmax, kv: str, B: int = 0, chunk: int = 0, device="cuda"):
+        """chunk: cells per split; 0 picks one (gqa_decode_auto_chunk); -P
+        cuts the dense windows of the whole batch, laid end to end, into P
+        equal pieces per KV head (the balanced partition)."""
         import torch
         self.S, self.T, self.H, self.Hk, self.D, self.Lmax, self.B = S, T, H, Hk, D, Lmax, B
         self.kv = kv
-        if chunk <= 0:
+        if chunk == 0:
             chunk = gqa_decode_auto_chunk(S, T, Lmax, B, H, Hk, D, kv == "i8")
             if chunk <= 0:
                 raise GqaDecodeError("gqa_decode_auto_chunk", chunk)

@@ -178,72 +178,81 @@ constexpr int attn_occupancy() {
   return (NRB >= 4 || (D == 256 && (NRB == 2 || !I8)) || (D == 128 && NRB == 2 && !I8)) ? 1 : 2;
 }
 
-template <int D, bool I8, bool IDS, int NRB, int NW>
-__global__ __launch_bounds__(64 * NW, (attn_occupancy<D, I8, NRB>())) void attn_mfma(AttnArgs a) {
+// Query-operand slots (row block x k-step x lane) of one row block, and how
+// many each thread of an NW-wave workgroup holds.  When they divide evenly
+// (at most eight per thread) a caller can request a unit's query rows before
+// it knows the unit's window, so their latency overlaps that read.
+template <int D, int NRB, int NW>
+struct QSlots {
+  static constexpr int QSLOTS = NRB * (D / 32) * 64;
+  static constexpr int NT = 64 * NW;
+  static constexpr int QPT = QSLOTS / NT;
+  static constexpr bool QPRE = QSLOTS % NT == 0 && QPT <= 8;
+  static constexpr int N = QPRE ? QPT : 1;
+};
+
+// Eight fp32 query elements of operand slot `slot` (slot = (row block k,
+// k-step ks, lane ln) of the MFMA B-operand layout) of the row block whose
+// first unit row is r0, in unit (sequence s, KV head g[, token tq]).  Rows
+// past the unit's last read that last row (always valid; they are zeroed
+// when stored).
+template <int D, bool I8, bool IDS>
+__device__ __forceinline__ void q_load_slot(const AttnArgs& a, int s, int g, int tq, int r0,
+                                            int slot, float4& u0, float4& u1) {
+  using G = TileGeom<D, I8>;
+  const int ln = slot & 63, kks = slot >> 6;
+  const int ks = kks % G::KS, k = kks / G::KS;
+  const int r = r0 + 16 * k + (ln & 15);
+  // dims of k-step ks held by lane group ln / 16 (must match the K loads)
+  const int lb2 = ln >> 4;
+  const int d0 = I8 ? (64 * (ks >> 1) + 16 * lb2 + 8 * (ks & 1)) : (32 * ks + 8 * lb2);
+  const int rc = r < a.R ? r : a.R - 1;
+  const int t = IDS ? tq : rc / a.G;
+  const int h = g * a.G + (IDS ? rc : rc % a.G);
+  const float* qrow = a.q + ((size_t)(s * a.T + t) * a.H + h) * D + d0;
+  u0 = *reinterpret_cast<const float4*>(qrow);
+  u1 = *reinterpret_cast<const float4*>(qrow + 4);
+}
+
+// One unit's split: every query row of row block rbl of (sequence s, KV head
+// g[, token tq]) against the cells [c0l, min(cap_end, window)) of its
+// window, written as partial slot p of each row.  seq_len is seq_lens[s];
+// id_first (gather mode) the split's first NT cell ids as requested by the
+// caller; qv the block's query slots when QSlots::QPRE (requested by the
+// caller).  Called by every thread of the workgroup; returns with the
+// partial written (LDS may be reused after a barrier).
+template <int D, bool I8, bool IDS, int NRB, int NW, bool IN_LOOP = false>
+__device__ __forceinline__ void attn_unit(const AttnArgs& a, int g, int s, int rbl, int tq, int p,
+                                          int64_t c0l, int64_t cap_end, int seq_len,
+                                          int id_first,
+                                          const float4 (&qv)[QSlots<D, NRB, NW>::N][2]) {
   using G = TileGeom<D, I8>;
   using L = AttnLds<D, I8, NRB, NW>;
+  using Q = QSlots<D, NRB, NW>;
   constexpr int NT = 64 * NW;                    // threads per workgroup
   constexpr int RB = 16 * NRB;
   constexpr int TC = G::TC;
   constexpr int RBY = G::RBY;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
-  const int tid = threadIdx.x;
+  int tid = threadIdx.x;
+  // Called in a loop: the lane index is made opaque at each call, so the
+  // compiler cannot hoist the body's lane-dependent addressing out of the
+  // loop and hold it in registers across the whole body.
+  if constexpr (IN_LOOP) asm volatile("" : "+v"(tid));
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int lr = lane & 15, lb = lane >> 4;
-
-  // 1-D grid, XCD-aware order.  Consecutive workgroups are dispatched to
-  // different XCDs (8 of them, each with its own L2 and its own share of the
-  // fabric), so the index that varies fastest must carry equal work: the KV
-  // head, then the sequence; the split index varies slowest, because the
-  // last splits of short sequences are empty and would otherwise all land
-  // on the same XCDs.  With a.seq_fast the sequence varies fastest instead:
-  // with S a multiple of 8 every KV head of a (sequence, split) then runs on
-  // the same XCD, so the heads' reads of the same cells (int8: the scale
-  // lines they share, the neighbouring halves of each cell's K/V run) meet
-  // in one L2.
-  int id = blockIdx.x;
-  int g, s;
-  if (a.seq_fast) {
-    s = id % a.S;
-    id /= a.S;
-    g = id % a.Hk;
-    id /= a.Hk;
-  } else {
-    g = id % a.Hk;
-    id /= a.Hk;
-    s = id % a.S;
-    id /= a.S;
-  }
-  const int nu = a.nrb * (IDS ? a.T : 1);
-  const int rbl = (id % nu) % a.nrb;
-  const int tq = (id % nu) / a.nrb;
-  const int p = id / nu;
   auto row_t = [&](int r) -> int { return IDS ? tq : r / a.G; };
   auto row_h = [&](int r) -> int { return g * a.G + (IDS ? r : r % a.G); };
   const int r0 = rbl * RB;                       // first unit row of this block
 
-  // ---- query rows as MFMA B operands (f16 hi + lo), staged once in LDS.
-  // Slot = (row block k, k-step ks, lane ln) of the operand layout.  Their
-  // loads are issued before anything waits on memory, so their latency
-  // overlaps the sequence-length read and the first tile's K/V requests. ----
-  constexpr int QSLOTS = NRB * G::KS * 64;
-  constexpr int QPT = QSLOTS / NT;                // slots per thread
-  constexpr bool QPRE = QSLOTS % NT == 0 && QPT <= 8;
+  // ---- query rows as MFMA B operands (f16 hi + lo), staged once in LDS. ----
+  constexpr int QSLOTS = Q::QSLOTS;
+  constexpr int QPT = Q::QPT;
+  constexpr bool QPRE = Q::QPRE;
   auto q_load = [&](int slot, float4& u0, float4& u1) {
-    const int ln = slot & 63, kks = slot >> 6;
-    const int ks = kks % G::KS, k = kks / G::KS;
-    const int r = r0 + 16 * k + (ln & 15);
-    // dims of k-step ks held by lane group ln / 16 (must match the K loads)
-    const int lb2 = ln >> 4;
-    const int d0 = I8 ? (64 * (ks >> 1) + 16 * lb2 + 8 * (ks & 1)) : (32 * ks + 8 * lb2);
-    // rows past the unit's last read that last row (always valid) and are
-    // zeroed when stored
-    const int rc = r < a.R ? r : a.R - 1;
-    const float* qrow = a.q + ((size_t)(s * a.T + row_t(rc)) * a.H + row_h(rc)) * D + d0;
-    u0 = *reinterpret_cast<const float4*>(qrow);
-    u1 = *reinterpret_cast<const float4*>(qrow + 4);
+    q_load_slot<D, I8, IDS>(a, s, g, tq, r0, slot, u0, u1);
   };
   // Per-row max |q| of the block.  A lane's slots all belong to its rows
   // 16k + lr; each wave reduces its slots in registers (qmx).  A one-wave
@@ -291,21 +300,6 @@ __global__ __launch_bounds__(64 * NW, (attn_occupancy<D, I8, NRB>())) void attn_
     qlds[(kks * 2 + 0) * 64 + ln] = __builtin_bit_cast(u32x4, hi);
     qlds[(kks * 2 + 1) * 64 + ln] = __builtin_bit_cast(u32x4, lo);
   };
-  float4 qv[QPRE ? QPT : 1][2];
-  if constexpr (QPRE) {
-#pragma unroll
-    for (int i = 0; i < QPT; ++i) q_load(tid + NT * i, qv[i][0], qv[i][1]);
-  }
-
-  // Gather mode: the split's first NT cell ids do not depend on the
-  // sequence length, so they are requested with it and the two reads
-  // overlap (the staging below takes them from here).
-  int id_first = 0;
-  if constexpr (IDS) {
-    const int64_t pos = (int64_t)p * a.chunk + tid;
-    if (tid < a.chunk && pos < a.B) id_first = a.ids[((size_t)s * a.T + tq) * a.B + pos];
-  }
-  const int seq_len = a.seq_lens[s];
 
   auto width_of = [&](int r) -> int {   // r: row index within the unit
     if (r >= a.R) return 0;
@@ -318,7 +312,6 @@ __global__ __launch_bounds__(64 * NW, (attn_occupancy<D, I8, NRB>())) void attn_
 
   const int rlast = (a.R - 1 < r0 + RB - 1) ? a.R - 1 : r0 + RB - 1;
   const int wmax = width_of(rlast);
-  const int64_t c0l = (int64_t)p * a.chunk;
   if (c0l >= wmax) {
     // nothing visible in this split for any row of the block: its partials
     // carry weight 0 (m = -inf, l = 0), and the merge skips their o
@@ -331,7 +324,7 @@ __global__ __launch_bounds__(64 * NW, (attn_occupancy<D, I8, NRB>())) void attn_
     return;
   }
   const int c0 = (int)c0l;
-  const int cend = (int)((c0l + a.chunk < wmax) ? c0l + a.chunk : wmax);
+  const int cend = (int)((cap_end < wmax) ? cap_end : wmax);
   // Tiles ending at or before lim_lo are fully visible to every real row.
   const int lim_lo = width_of(r0) < cend ? width_of(r0) : cend;
 
@@ -942,6 +935,139 @@ __global__ __launch_bounds__(64 * NW, (attn_occupancy<D, I8, NRB>())) void attn_
     const size_t prow = ((size_t)(s * a.T + row_t(r)) * a.H + row_h(r)) * a.P + p;
     a.part_ml[prow * 2] = M;
     a.part_ml[prow * 2 + 1] = Ls;
+  }
+}
+
+
+// Split grid: one workgroup per (split p, KV head [, row block] [, token],
+// sequence), 1-D and XCD-aware.  Consecutive workgroups are dispatched to
+// different XCDs (8 of them, each with its own L2 and its own share of the
+// fabric), so the index that varies fastest must carry equal work: the KV
+// head, then the sequence; the split index varies slowest, because the last
+// splits of short sequences are empty and would otherwise all land on the
+// same XCDs.  With a.seq_fast the sequence varies fastest instead: with S a
+// multiple of 8 every KV head of a (sequence, split) then runs on the same
+// XCD, so the heads' reads of the same cells (int8: the scale lines they
+// share, the neighbouring halves of each cell's K/V run) meet in one L2.
+template <int D, bool I8, bool IDS, int NRB, int NW>
+__global__ __launch_bounds__(64 * NW, (attn_occupancy<D, I8, NRB>())) void attn_mfma(AttnArgs a) {
+  using Q = QSlots<D, NRB, NW>;
+  const int tid = threadIdx.x;
+  int id = blockIdx.x;
+  int g, s;
+  if (a.seq_fast) {
+    s = id % a.S;
+    id /= a.S;
+    g = id % a.Hk;
+    id /= a.Hk;
+  } else {
+    g = id % a.Hk;
+    id /= a.Hk;
+    s = id % a.S;
+    id /= a.S;
+  }
+  const int nu = a.nrb * (IDS ? a.T : 1);
+  const int rbl = (id % nu) % a.nrb;
+  const int tq = (id % nu) / a.nrb;
+  const int p = id / nu;
+  // The query rows are requested before anything waits on memory, so their
+  // latency overlaps the sequence-length read and the first tile's requests.
+  float4 qv[Q::N][2];
+  if constexpr (Q::QPRE) {
+#pragma unroll
+    for (int i = 0; i < Q::QPT; ++i)
+      q_load_slot<D, I8, IDS>(a, s, g, tq, rbl * 16 * NRB, tid + Q::NT * i, qv[i][0], qv[i][1]);
+  }
+  // Gather mode: the split's first NT cell ids do not depend on the
+  // sequence length, so they are requested with it and the two reads
+  // overlap.
+  int id_first = 0;
+  if constexpr (IDS) {
+    const int64_t pos = (int64_t)p * a.chunk + tid;
+    if (tid < a.chunk && pos < a.B) id_first = a.ids[((size_t)s * a.T + tq) * a.B + pos];
+  }
+  const int seq_len = a.seq_lens[s];
+  const int64_t c0l = (int64_t)p * a.chunk;
+  attn_unit<D, I8, IDS, NRB, NW>(a, g, s, rbl, tq, p, c0l, c0l + a.chunk, seq_len, id_first, qv);
+}
+
+// Balanced grid (dense windows): one workgroup per (KV head, row block,
+// piece j), KV head fastest; a.P pieces per (KV head, row block).  The
+// piece's real cells are visited sequence by sequence, each sequence's
+// segment being one split of that sequence's unit, written as partial slot
+// j - (piece of the sequence's first real cell): a sequence's partials fill
+// its slots 0 .. n-1, n = the number of pieces holding its real cells, which
+// workgroup (0, 0, 0) writes to a.flat_n for the merge.  Every wave walks
+// the lengths itself (no LDS, no barrier), so all waves agree on the
+// segments; the walk keeps its state in scalar registers (the sequence index
+// and the span start), so nothing lane-dependent stays live across units.
+template <int D, bool I8, int NRB, int NW>
+__global__ __launch_bounds__(64 * NW, (attn_occupancy<D, I8, NRB>())) void attn_mfma_flat(AttnArgs a) {
+  using Q = QSlots<D, NRB, NW>;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int pad = a.flat_pad;
+  int id = blockIdx.x;
+  const int g = id % a.Hk;
+  id /= a.Hk;
+  const int rbl = id % a.nrb;
+  const int j = id / a.nrb;
+  int W = 0;                                    // total span, 64 sequences per pass
+  for (int c = 0; c < a.S; c += 64) {
+    const int si = c + lane;
+    W += wave_sum_i(si < a.S ? flat_span(a.seq_lens[si], a.Lmax, pad) : 0);
+  }
+  const int Pe = a.P < W ? a.P : W;
+  if (blockIdx.x == 0 && tid < 64) {
+    // every sequence's slot count, for the merge
+    int base = 0;
+    for (int c = 0; c < a.S; c += 64) {
+      const int si = c + lane;
+      const int w = si < a.S ? flat_span(a.seq_lens[si], a.Lmax, pad) : 0;
+      const int end = base + wave_incl_scan_i(w);
+      if (si < a.S)
+        a.flat_n[si] = w > 0 ? flat_piece(end - 1, W, Pe) - flat_piece(end - w + pad, W, Pe) + 1 : 0;
+      base = __builtin_amdgcn_readlane(end, 63);
+    }
+  }
+  if (j >= Pe) return;                          // also W == 0: nothing visible anywhere
+  const int b0 = flat_bound(j, W, Pe), b1 = flat_bound(j + 1, W, Pe);
+  // the first sequence whose span reaches past b0, and where its span starts
+  int s = a.S, st = 0, base = 0;
+  for (int c = 0; c < a.S; c += 64) {
+    const int si = c + lane;
+    const int w = si < a.S ? flat_span(a.seq_lens[si], a.Lmax, pad) : 0;
+    const int end = base + wave_incl_scan_i(w);
+    const uint64_t m = __ballot(w > 0 && end > b0);
+    if (m) {
+      const int l = __builtin_ctzll(m);
+      s = c + l;
+      st = __builtin_amdgcn_readlane(end, l) - __builtin_amdgcn_readlane(w, l);
+      break;
+    }
+    base = __builtin_amdgcn_readlane(end, 63);
+  }
+  s = __builtin_amdgcn_readfirstlane(s);
+  st = __builtin_amdgcn_readfirstlane(st);
+  for (; s < a.S && st < b1; ++s) {
+    const int L = a.seq_lens[s];
+    const int ws = flat_window(L, a.Lmax);
+    if (ws == 0) continue;
+    const int c0 = st + pad;                    // the window's first real cell
+    const int lo = c0 > b0 ? c0 : b0;
+    const int hi = c0 + ws < b1 ? c0 + ws : b1;
+    if (lo < hi) {
+      const int p = j - flat_piece(c0, W, Pe);
+      float4 qv[Q::N][2];
+      if constexpr (Q::QPRE) {
+#pragma unroll
+        for (int i = 0; i < Q::QPT; ++i)
+          q_load_slot<D, I8, false>(a, s, g, 0, rbl * 16 * NRB, tid + Q::NT * i, qv[i][0], qv[i][1]);
+      }
+      attn_unit<D, I8, false, NRB, NW, true>(a, g, s, rbl, 0, p, lo - c0, hi - c0, L, 0, qv);
+      __syncthreads();                          // LDS is restaged by the next segment
+    }
+    st = c0 + ws;
   }
 }
 

@@ -41,13 +41,15 @@ using gqa_kern::AttnArgs;
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <int D, bool I8, bool IDS, int NRB, int NW>
+// FLAT: the balanced-partition grid (dense windows only).
+template <int D, bool I8, bool IDS, int NRB, int NW, bool FLAT = false>
 hipError_t launch_one(const AttnArgs& a, dim3 grid, hipStream_t st) {
+  static_assert(!(FLAT && IDS), "the balanced partition covers dense windows");
   using L = gqa_kern::AttnLds<D, I8, NRB, NW>;
   // gather mode: the split's ids follow the fixed part, 16-byte aligned
   const int bytes = L::BYTES + (IDS ? (a.chunk * 4 + 15) / 16 * 16 : 0);
   constexpr int most = L::BYTES + (IDS ? L::IDSB : 0);
-  auto* fn = &gqa_kern::attn_mfma<D, I8, IDS, NRB, NW>;
+  auto* fn = FLAT ? &gqa_kern::attn_mfma_flat<D, I8, NRB, NW> : &gqa_kern::attn_mfma<D, I8, IDS, NRB, NW>;
   if constexpr (most > 65536) {
     // more than 64 KB of dynamic LDS must be allowed once per device
     static std::atomic<uint64_t> attr_set{0};   // bit per device, per instance
@@ -79,6 +81,7 @@ constexpr bool fits_lds() {
 template <int D, bool I8, int NRB>
 hipError_t launch_attn_nw(const AttnArgs& a, bool ids, int nw, dim3 grid, hipStream_t st) {
   static_assert(fits_lds<D, I8, NRB, 4>() && fits_lds<D, I8, NRB, 1>(), "LDS budget");
+  if (a.flat) return launch_one<D, I8, false, NRB, 4, true>(a, grid, st);
   if (nw == 1)
     return ids ? launch_one<D, I8, true, NRB, 1>(a, grid, st)
                : launch_one<D, I8, false, NRB, 1>(a, grid, st);
@@ -114,8 +117,12 @@ int attn_common(bool i8, const float* q, const void* k, const void* v, const uin
   gqa::Shape sh{S, T, Lmax, ids ? B : 0, H, Hk, D, ids != nullptr, i8};
   int rc = gqa::check_shape(sh);
   if (rc != GQA_OK) return rc;
-  if (chunk <= 0) chunk = gqa::auto_chunk(sh);
-  if (chunk <= 0 || chunk > gqa::max_chunk(sh)) return GQA_ERR_CHUNK;
+  if (chunk == 0) chunk = gqa::auto_chunk(sh);
+  // balanced partition: a segment lies inside one window, so Lmax bounds it
+  const bool flat = chunk < 0;
+  if (flat ? (!gqa::balanced_ok(sh, chunk) || Lmax > gqa::max_chunk(sh))
+           : (chunk <= 0 || chunk > gqa::max_chunk(sh)))
+    return GQA_ERR_CHUNK;
   if (ids && (int64_t)Lmax * Hk * D * (i8 ? 1 : 2) >= ((int64_t)1 << 31)) return GQA_ERR_SHAPE;
   const size_t need = gqa::part_bytes(sh, chunk);
   const int64_t P = gqa::num_splits(sh, chunk);
@@ -130,6 +137,9 @@ int attn_common(bool i8, const float* q, const void* k, const void* v, const uin
   a.part_ml = part + gqa::part_o_floats(sh, P);
   a.S = S; a.T = T; a.Lmax = Lmax; a.B = sh.B; a.H = H; a.Hk = Hk; a.G = H / Hk;
   a.R = (int)gqa::rows_per_unit(sh); a.nrb = (int)gqa::row_blocks(sh); a.P = (int)P; a.chunk = chunk;
+  a.flat = flat ? 1 : 0;
+  a.flat_pad = gqa::flat_pad_cells(sh);
+  a.flat_n = reinterpret_cast<int*>(part + gqa::flat_n_offset_floats(sh, P));
   a.qscale = scale * kLog2e;
   a.qmant = std::frexp(a.qscale, &a.qexp);
   // int8 rows: the KV heads of a sequence share an XCD (sequence-fastest
@@ -139,7 +149,7 @@ int attn_common(bool i8, const float* q, const void* k, const void* v, const uin
   // balances uneven batches (f16 batch 62.6 us, 64.5 sequence-fastest).
   a.seq_fast = (i8 && S % 8 == 0) ? 1 : 0;
   const int nrows = gqa::block_rows(sh);
-  const int64_t nwg = P * Hk * a.nrb * (ids ? T : 1) * S;
+  const int64_t nwg = flat ? P * Hk * a.nrb : P * Hk * a.nrb * (ids ? T : 1) * S;
   if (nwg > 0x7fffffff) return GQA_ERR_SHAPE;
   dim3 grid((unsigned)nwg);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);

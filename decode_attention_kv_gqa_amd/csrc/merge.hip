@@ -136,6 +136,103 @@ __global__ __launch_bounds__(kThreads) void merge_rows(MergeArgs a) {
   }
 }
 
+// Merge after a balanced-partition attention call: row (s, t, h)'s partials
+// fill its slots 0 .. n-1, n = flat_n[s] as written by the attention call (0
+// for an empty window).  Wave w requests slot w together with n, before n
+// is known (slot w < P lies inside the workspace either way; slots at or
+// past n are dropped), so rows of up to four partials take one round trip.
+template <int D>
+__global__ __launch_bounds__(kThreads) void merge_rows_flat(MergeArgs a) {
+  constexpr int V = D / 64;
+  __shared__ float red_o[4][D];
+  __shared__ float red_ml[4][2];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int row = blockIdx.x;             // ((s * T) + t) * H + h
+  const float* ml = a.part_ml + (size_t)row * a.P * 2;
+  const float* po = a.part_o + (size_t)row * a.P * D + lane * V;
+  float gt[V];
+  const bool gated = a.gate != nullptr;
+  if (gated && wave == 0) {
+    const float* gsrc = a.gate + (size_t)row * a.gate_stride + lane * V;
+#pragma unroll
+    for (int e = 0; e < V; ++e) gt[e] = gsrc[e];
+  }
+  auto load = [&](int j, float& mj, float& lj, float (&oj)[V]) {
+    mj = ml[2 * j];
+    lj = ml[2 * j + 1];
+    const float* src = po + (size_t)j * D;
+#pragma unroll
+    for (int e = 0; e < V; ++e) oj[e] = src[e];
+  };
+  float m0 = -INFINITY, l0 = 0.f, o0[V];
+#pragma unroll
+  for (int e = 0; e < V; ++e) o0[e] = 0.f;
+  if (wave < a.P) load(wave, m0, l0, o0);
+  // (P == 0: an empty cache, for which the attention call writes nothing)
+  const int n = a.P > 0 ? a.flat_n[row / a.TH] : 0;
+
+  float M = -INFINITY, lsum = 0.f;
+  float acc[V];
+#pragma unroll
+  for (int e = 0; e < V; ++e) acc[e] = 0.f;
+  auto take = [&](float mj, float lj, const float (&oj)[V]) {
+    if (mj == -INFINITY) return;          // no visible cell of the row in that split
+    if (mj > M) {
+      const float c = (M == -INFINITY) ? 0.f : exp2f(M - mj);
+      lsum *= c;
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[e] *= c;
+      M = mj;
+    }
+    const float w = exp2f(mj - M);
+    lsum = fmaf(w, lj, lsum);
+#pragma unroll
+    for (int e = 0; e < V; ++e) acc[e] = fmaf(w, oj[e], acc[e]);
+  };
+  if (wave < n) take(m0, l0, o0);
+  for (int j = wave + 4; j < n; j += 4) {
+    float mj, lj, oj[V];
+    load(j, mj, lj, oj);
+    take(mj, lj, oj);
+  }
+#pragma unroll
+  for (int e = 0; e < V; ++e) red_o[wave][lane * V + e] = acc[e];
+  if (lane == 0) {
+    red_ml[wave][0] = M;
+    red_ml[wave][1] = lsum;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    float* out = a.out + (size_t)row * D + lane * V;
+    float Mt = red_ml[0][0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) Mt = fmaxf(Mt, red_ml[w][0]);
+    if (Mt == -INFINITY) {                  // no visible cell: zeros
+#pragma unroll
+      for (int e = 0; e < V; ++e) out[e] = 0.f;
+      return;
+    }
+    float f[4], Ls = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = red_ml[w][0];
+      f[w] = (mw == -INFINITY) ? 0.f : exp2f(mw - Mt);
+      Ls = fmaf(f[w], red_ml[w][1], Ls);
+    }
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      float x = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) x = fmaf(f[w], red_o[w][lane * V + e], x);
+      x = x / Ls;
+      if (gated) x *= 1.0f / (1.0f + __expf(-gt[e]));
+      out[e] = x;
+    }
+  }
+}
+
 template <int U>
 void launch_merge(const MergeArgs& a, int D, dim3 grid, hipStream_t st) {
   switch (D) {
@@ -157,7 +254,7 @@ static int merge_common(const float* part, const int32_t* seq_lens, const int32_
   gqa::Shape sh{S, T, Lmax, ids ? B : 0, H, H, D, ids, false};
   int rc = gqa::check_shape(sh);
   if (rc != GQA_OK) return rc;
-  if (chunk < 1) return GQA_ERR_CHUNK;
+  if (chunk == 0 || (chunk < 0 && !gqa::balanced_ok(sh, chunk))) return GQA_ERR_CHUNK;
   if (gate && gate_stride < D) return GQA_ERR_SHAPE;
   const int64_t P = gqa::num_splits(sh, chunk);
   if (P > 0 && gqa::part_bytes(sh, chunk) == 0) return GQA_ERR_SHAPE;   // no workspace could hold it
@@ -168,11 +265,20 @@ static int merge_common(const float* part, const int32_t* seq_lens, const int32_
   a.gate = gate;
   a.gate_stride = gate_stride;
   a.P = (int)P;
+  a.flat = chunk < 0;
+  a.flat_n = reinterpret_cast<const int32_t*>(part + gqa::flat_n_offset_floats(sh, P));
+  a.TH = T * H;
   const size_t rows = (size_t)S * T * H;
   if (rows > 0x7fffffffu) return GQA_ERR_SHAPE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   dim3 grid((unsigned)rows);
-  if (P <= 16)
+  if (a.flat) {
+    switch (D) {
+      case 64: hipLaunchKernelGGL(merge_rows_flat<64>, grid, dim3(kThreads), 0, st, a); break;
+      case 128: hipLaunchKernelGGL(merge_rows_flat<128>, grid, dim3(kThreads), 0, st, a); break;
+      default: hipLaunchKernelGGL(merge_rows_flat<256>, grid, dim3(kThreads), 0, st, a); break;
+    }
+  } else if (P <= 16)
     launch_merge<4>(a, D, grid, st);
   else if (P <= 32)
     launch_merge<8>(a, D, grid, st);

@@ -53,12 +53,14 @@ int auto_chunk(const Shape& s) {
 }
 
 size_t part_bytes(const Shape& s, int chunk) {
-  if (chunk < 1 || check_shape(s) != GQA_OK) return 0;
+  if (chunk == 0 || (chunk < 0 && !balanced_ok(s, chunk)) || check_shape(s) != GQA_OK) return 0;
   const int64_t P = num_splits(s, chunk);
   // rows (< 2^31) x splits (< 2^31) x (D + 2) floats: computed in 128 bits;
   // a workspace beyond half the address space is refused (0), never wrapped
-  const unsigned __int128 b = (unsigned __int128)((int64_t)s.S * s.T * s.H) * (uint64_t)P *
-                              (uint64_t)(s.D + 2) * sizeof(float);
+  unsigned __int128 b = (unsigned __int128)((int64_t)s.S * s.T * s.H) * (uint64_t)P *
+                        (uint64_t)(s.D + 2) * sizeof(float);
+  // balanced partition: the per-sequence slot counts follow, 16-byte rounded
+  if (chunk < 0) b += ((uint64_t)s.S * 4 + 15) / 16 * 16;
   if (b > (unsigned __int128)(SIZE_MAX >> 1)) return 0;
   return (size_t)b;
 }
@@ -87,7 +89,10 @@ const char* gqa_decode_strerror(int code) {
     case GQA_ERR_GROUP: return "n_heads must be a multiple of n_kv_heads";
     case GQA_ERR_HEAD_DIM: return "head_dim must be 64, 128 or 256";
     case GQA_ERR_BUDGET: return "ids given with a budget B < 1";
-    case GQA_ERR_CHUNK: return "chunk must be >= 1 (pass the resolved chunk to the merge)";
+    case GQA_ERR_CHUNK:
+      return "chunk must be >= 1 cells per split, or -P for the balanced partition (dense "
+             "windows, S * Lmax < 2^31, Lmax within a split's limit); the merge takes the "
+             "resolved chunk";
     case GQA_ERR_WORKSPACE: return "partial workspace smaller than gqa_decode_part_bytes()";
     case GQA_ERR_STATIC_LIMIT:
       return "the partials exceed the static buffer of gqa_decode_step_static "

@@ -33,9 +33,27 @@ inline int64_t width_cap(const Shape& s) {
   return s.Lmax;
 }
 
+// Most pieces per (KV head, row block) of the balanced partition.
+constexpr int kMaxPieces = 1 << 16;
+
+// A negative chunk selects the balanced partition with -chunk pieces per
+// (KV head, row block): the dense windows of all sequences, laid end to end,
+// cut into equal pieces (no ids; the total window, at most S * Lmax cells,
+// below 2^31).
+// (The total span, windows plus their pad cells, stays below 2^31: the pad
+// is at most 512 cells.)
+inline bool balanced_ok(const Shape& s, int chunk) {
+  return chunk < 0 && -(int64_t)chunk <= kMaxPieces && !s.ids && !s.tq &&
+         (int64_t)s.S * ((int64_t)s.Lmax + 1024) < ((int64_t)1 << 31);
+}
+
+// Partial slots per query row: the split count, or the piece count of the
+// balanced partition (a sequence's partials fill its first slots).
 inline int64_t num_splits(const Shape& s, int chunk) {
   int64_t w = width_cap(s);
-  return w <= 0 ? 0 : (w + chunk - 1) / chunk;
+  if (w <= 0) return 0;
+  if (chunk < 0) return -(int64_t)chunk;
+  return (w + chunk - 1) / chunk;
 }
 
 // Query rows served by one (sequence, KV head[, token]) unit.  64-bit: the
@@ -79,7 +97,7 @@ inline int64_t max_chunk(const Shape& s) {
 // splits get four waves, one per SIMD.
 inline int waves_per_block(const Shape& s, int chunk) {
   (void)s;
-  return chunk <= 64 ? 1 : 4;
+  return (chunk > 0 && chunk <= 64) ? 1 : 4;
 }
 
 int check_shape(const Shape& s);               // GQA_OK or GQA_ERR_*
@@ -91,6 +109,21 @@ size_t part_bytes(const Shape& s, int chunk);  // 0 on bad arguments
 //   ml [S][T][H][P][2]   running max (base-2 domain) and running sum
 inline size_t part_o_floats(const Shape& s, int64_t P) {
   return (size_t)s.S * s.T * s.H * (size_t)P * s.D;
+}
+// Balanced partition: after the two regions, n [S] int32, the partial slots
+// each sequence fills (written by the attention call, read by the merge).
+inline size_t flat_n_offset_floats(const Shape& s, int64_t P) {
+  return (size_t)s.S * s.T * s.H * (size_t)P * (s.D + 2);
+}
+
+// Virtual cells charged for each non-empty window in the balanced
+// partition: the cost of starting a sequence inside a workgroup, as the
+// cells that stream in that time.  kFlatPadBytes of K + V rows of one KV
+// head per sequence start.
+constexpr int64_t kFlatPadBytes = 64 * 1024;
+inline int flat_pad_cells(const Shape& s) {
+  const int64_t cell = 2 * (int64_t)s.D * (s.i8 ? 1 : 2);   // K + V bytes of one KV head
+  return (int)(kFlatPadBytes / cell);
 }
 
 }  // namespace gqa

@@ -60,7 +60,7 @@ extern "C" int gqa_decode_step_static(const float* q, const void* k, const void*
   if (Lmax > 0 && (!k || !v || (kv_kind == 1 && (!k_scales || !v_scales)))) return GQA_ERR_NULL;
   if (ids && B < 1) return GQA_ERR_BUDGET;
   const int Bx = ids ? B : 0;
-  if (chunk <= 0) {
+  if (chunk == 0) {
     chunk = gqa_decode_auto_chunk(S, T, Lmax, Bx, H, Hk, D, kv_kind);
     if (chunk <= 0) return chunk;
   }

@@ -86,8 +86,11 @@ enum {
   GQA_ERR_GROUP = -3,      /* H % Hk != 0                                        */
   GQA_ERR_HEAD_DIM = -4,   /* D not in {64, 128, 256}                            */
   GQA_ERR_BUDGET = -5,     /* ids given with B < 1                               */
-  GQA_ERR_CHUNK = -6,      /* chunk < 1 in the merge, or a split wider than 2^31
-                              bytes of K rows (chunk * Hk * D * elem >= 2^31)    */
+  GQA_ERR_CHUNK = -6,      /* chunk 0 in the merge, a split wider than 2^31
+                              bytes of K rows (chunk * Hk * D * elem >= 2^31),
+                              or a balanced partition (chunk < 0) outside its
+                              limits (ids, P > 65536, S * (Lmax + 1024) >= 2^31,
+                              Lmax * Hk * D * elem >= 2^31)                      */
   GQA_ERR_WORKSPACE = -7,  /* part_bytes < gqa_decode_part_bytes(...)            */
   GQA_ERR_STATIC_LIMIT = -8 /* gqa_decode_step_static: the partials need more than
                               GQA_STATIC_PART_BYTES                              */
@@ -99,11 +102,13 @@ enum {
 /* Partial workspace size in bytes for one attention call: one partial
  * (D unnormalised output floats + running max + running sum) per query row
  * and split, splits = ceil(min(B or Lmax, Lmax) / chunk).  `B` is the budget
- * (0 when no ids are used); `chunk` is the resolved cells-per-split (> 0).
- * Returns 0 for invalid arguments.  Pure host function. */
+ * (0 when no ids are used); `chunk` is the resolved cells-per-split (> 0),
+ * or -P for the balanced partition (see the attention calls): P partial
+ * slots per query row, followed by S int32 slot counts rounded up to 16
+ * bytes.  Returns 0 for invalid arguments.  Pure host function. */
 size_t gqa_decode_part_bytes(int S, int T, int Lmax, int B, int H, int D, int chunk);
 
-/* The split size the attention calls use when passed chunk <= 0.  A pure,
+/* The split size the attention calls use when passed chunk == 0.  A pure,
  * deterministic host function of the shapes: it picks the cells per split so
  * that the grid gives every one of the 256 compute units several
  * workgroups, while the partials stay a small fraction of the KV bytes.
@@ -122,8 +127,23 @@ int gqa_decode_auto_chunk(int S, int T, int Lmax, int B, int H, int Hk, int D, i
  *   part      workspace of part_bytes >= gqa_decode_part_bytes(S,T,Lmax,B,H,D,chunk')
  *             where chunk' is the resolved chunk; contents are overwritten
  *   scale     score scale (typically 1/sqrt(D))
- *   chunk     cells per split; <= 0 selects gqa_decode_auto_chunk(...);
+ *   chunk     cells per split (> 0): each (sequence, KV head) window is cut
+ *             into splits of `chunk` cells, one workgroup each;
+ *             0 selects gqa_decode_auto_chunk(...);
+ *             -P (dense windows only) selects the balanced partition for
+ *             batches of uneven lengths: the windows of all S sequences are
+ *             laid end to end, each non-empty one preceded by a fixed number
+ *             of virtual cells that stand for the cost of starting a
+ *             sequence (64 KB of its K + V rows: 128 cells for f16 head_dim
+ *             128), and the total is cut into P near-equal pieces per KV head
+ *             (and row block), one workgroup each, that may cross sequence
+ *             boundaries; a piece writes one partial per sequence it
+ *             touches.  Needs ids == NULL, P <= 65536 and
+ *             S * (Lmax + 1024) < 2^31.  (qsa2.metal's chunk partials and
+ *             log-sum-exp merge do not depend on where the chunks start, so
+ *             any cut of a window gives the same result up to rounding.)
  *             chunk * Hk * D * (bytes per element) must stay below 2^31
+ *             (balanced: Lmax in its place).
  * Errors: GQA_ERR_NULL, _SHAPE, _GROUP, _HEAD_DIM, _BUDGET, _CHUNK, _WORKSPACE. */
 int gqa_decode_attn_f16(const float *q, const uint16_t *k, const uint16_t *v,
                         const int32_t *ids, const int32_t *seq_lens,
@@ -144,7 +164,9 @@ int gqa_decode_attn_i8(const float *q, const int8_t *k, const int8_t *v,
                        float scale, int chunk, void *stream);
 
 /* Log-sum-exp merge of the partials written by the attention call with the
- * same S, T, Lmax, B, H, D and the same RESOLVED chunk (> 0):
+ * same S, T, Lmax, B, H, D and the same RESOLVED chunk (> 0, or the same -P
+ * for the balanced partition, where each row's slot count is read from the
+ * workspace):
  *   M = max_j m_j,  out = sum_j e^(m_j - M) o_j / sum_j e^(m_j - M) l_j
  * (qsa2.metal, qsa_merge2).  The attention call writes every (row, split)
  * slot of the workspace; a split holding no visible cell of a row carries
@@ -273,7 +295,8 @@ int gqa_decode_append_i8(const float *k_new, const float *v_new, const int32_t *
  *   kv_kind   0: k, v are f16 bit patterns (k_scales, v_scales unused)
  *             1: k, v are int8 codes with f16 k_scales, v_scales
  *   out       [S][T][H][D] float32, as gqa_decode_merge
- *   chunk     <= 0 selects gqa_decode_auto_chunk(..., kv_kind)
+ *   chunk     0 selects gqa_decode_auto_chunk(..., kv_kind); -P the
+ *             balanced partition, as the attention calls
  * Other arguments as gqa_decode_attn_f16 / _i8.  Every call on one GPU uses
  * that GPU's one buffer: calls that overlap on a GPU (other streams, other
  * threads, without ordering between them) race and give wrong results.

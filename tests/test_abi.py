@@ -67,6 +67,12 @@ def attn_f16(**kw):
     (dict(ids=FAKE, B=0), _lib.GQA_ERR_BUDGET),
     (dict(part_bytes=16), _lib.GQA_ERR_WORKSPACE),
     (dict(chunk=1, part_bytes=8 * 16 * 66 * 4 - 1), _lib.GQA_ERR_WORKSPACE),
+    # balanced partition (negative chunk): dense windows only, a bounded
+    # piece count and total window, a workspace holding the slot counts too
+    (dict(chunk=-4, ids=FAKE, B=8), _lib.GQA_ERR_CHUNK),
+    (dict(chunk=-(1 << 16) - 1), _lib.GQA_ERR_CHUNK),
+    (dict(chunk=-4, S=1 << 16, Lmax=1 << 15), _lib.GQA_ERR_CHUNK),
+    (dict(chunk=-4, part_bytes=8 * 4 * 66 * 4 + 15), _lib.GQA_ERR_WORKSPACE),
 ])
 def test_attn_f16_rejects(kw, code):
     assert attn_f16(**kw) == code
@@ -84,6 +90,8 @@ def test_merge_rejects():
     assert m(FAKE, FAKE, None, FAKE, 1, 1, 16, 0, 8, 64, 0, 0) == _lib.GQA_ERR_CHUNK
     assert m(FAKE, FAKE, None, FAKE, 1, 1, 16, 0, 8, 96, 32, 0) == _lib.GQA_ERR_HEAD_DIM
     assert m(FAKE, FAKE, FAKE, FAKE, 1, 1, 16, 0, 8, 64, 32, 0) == _lib.GQA_ERR_BUDGET
+    # the balanced partition has no ids form
+    assert m(FAKE, FAKE, FAKE, FAKE, 1, 1, 16, 8, 8, 64, -4, 0) == _lib.GQA_ERR_CHUNK
 
 
 def test_merge_gated_rejects():
@@ -123,6 +131,13 @@ def test_part_bytes_formula():
     assert gq.gqa_decode_part_bytes(1, 1, 100, 0, 8, 64, 32) == 8 * 4 * 66 * 4
     assert gq.gqa_decode_part_bytes(1, 1, 0, 0, 8, 64, 32) == 0
     assert gq.gqa_decode_part_bytes(1, 1, 100, 0, 8, 64, 0) == 0
+    # balanced partition: P slots per row, then S int32 slot counts rounded
+    # up to 16 bytes; no ids form
+    assert gq.gqa_decode_part_bytes(32, 1, 4096, 0, 32, 128, -32) == 32 * 32 * 32 * 130 * 4 + 128
+    assert gq.gqa_decode_part_bytes(3, 2, 100, 0, 8, 64, -5) == 3 * 2 * 8 * 5 * 66 * 4 + 16
+    assert gq.gqa_decode_part_bytes(3, 1, 0, 0, 8, 64, -5) == 16
+    assert gq.gqa_decode_part_bytes(3, 1, 100, 8, 8, 64, -5) == 0
+    assert gq.gqa_decode_part_bytes(3, 1, 100, 0, 8, 64, -(1 << 17)) == 0
 
 
 def test_auto_chunk_plan():

@@ -46,7 +46,7 @@ class Workload:
     Lmax: int
     kv: str               # "f16" or "i8"
     scale: float
-    chunk: int            # cells per split; 0 = library's automatic choice
+    chunk: int            # cells per split; 0 = library's automatic choice; -P = balanced partition
     lens: str             # "full" (every sequence at Lmax) or "uniform:lo:hi" (inclusive)
     budget: int = 0       # B; 0 = dense (no ids)
     description: str = ""
@@ -58,8 +58,9 @@ WORKLOADS = {
                  scale=1.0 / 8.0, chunk=32, lens="full",
                  description="tiny f16 decode: 1 seq, 8 heads / 2 KV heads, hd 64, 256 cells, 32-cell chunks"),
         Workload("f16_batch", 1, S=32, T=1, H=32, Hk=8, D=128, Lmax=4096, kv="f16",
-                 scale=1.0 / math.sqrt(128.0), chunk=0, lens="uniform:512:4096",
-                 description="f16 GQA decode batch: 32 seqs, lengths U[512,4096], 32/8 heads, hd 128"),
+                 scale=1.0 / math.sqrt(128.0), chunk=-32, lens="uniform:512:4096",
+                 description="f16 GQA decode batch: 32 seqs, lengths U[512,4096], 32/8 heads, hd 128; "
+                             "balanced partition, 32 pieces per KV head"),
         Workload("i8_32k", 2, S=8, T=1, H=24, Hk=2, D=256, Lmax=32768, kv="i8",
                  scale=1.0 / 16.0, chunk=0, lens="full",
                  description="int8 KV decode: 8 seqs at context 32768, 24/2 heads (group 12), hd 256"),
