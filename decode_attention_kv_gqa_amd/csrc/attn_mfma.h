@@ -238,8 +238,21 @@ __device__ __forceinline__ void attn_unit(const AttnArgs& a, int g, int s, int r
   int tid = threadIdx.x;
   // Called in a loop: the lane index is made opaque at each call, so the
   // compiler cannot hoist the body's lane-dependent addressing out of the
-  // loop and hold it in registers across the whole body.
-  if constexpr (IN_LOOP) asm volatile("" : "+v"(tid));
+  // loop and hold it in registers across the whole body; and the unit's
+  // coordinates, uniform by construction, are read from the first lane, so
+  // that the buffer resources built from them sit in scalar registers (a
+  // resource in vector registers costs a loop over the lanes at every load:
+  // balanced int8 32K 63.3 -> 53.2 us).
+  if constexpr (IN_LOOP) {
+    asm volatile("" : "+v"(tid));
+    g = __builtin_amdgcn_readfirstlane(g);
+    s = __builtin_amdgcn_readfirstlane(s);
+    rbl = __builtin_amdgcn_readfirstlane(rbl);
+    p = __builtin_amdgcn_readfirstlane(p);
+    c0l = __builtin_amdgcn_readfirstlane((int)c0l);
+    cap_end = __builtin_amdgcn_readfirstlane((int)cap_end);
+    seq_len = __builtin_amdgcn_readfirstlane(seq_len);
+  }
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int lr = lane & 15, lb = lane >> 4;

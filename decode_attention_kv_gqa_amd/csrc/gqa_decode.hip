@@ -49,7 +49,8 @@ hipError_t launch_one(const AttnArgs& a, dim3 grid, hipStream_t st) {
   // gather mode: the split's ids follow the fixed part, 16-byte aligned
   const int bytes = L::BYTES + (IDS ? (a.chunk * 4 + 15) / 16 * 16 : 0);
   constexpr int most = L::BYTES + (IDS ? L::IDSB : 0);
-  auto* fn = FLAT ? &gqa_kern::attn_mfma_flat<D, I8, NRB, NW> : &gqa_kern::attn_mfma<D, I8, IDS, NRB, NW>;
+  auto* fn = &gqa_kern::attn_mfma<D, I8, IDS, NRB, NW>;
+  if constexpr (FLAT) fn = &gqa_kern::attn_mfma_flat<D, I8, NRB, NW>;
   if constexpr (most > 65536) {
     // more than 64 KB of dynamic LDS must be allowed once per device
     static std::atomic<uint64_t> attr_set{0};   // bit per device, per instance
