@@ -221,7 +221,9 @@ __device__ __forceinline__ void q_load_slot(const AttnArgs& a, int s, int g, int
 // caller; qv the block's query slots when QSlots::QPRE (requested by the
 // caller).  Called by every thread of the workgroup; returns with the
 // partial written (LDS may be reused after a barrier).
-template <int D, bool I8, bool IDS, int NRB, int NW, bool IN_LOOP = false>
+// IDS: 0 dense windows, 1 gather through cell ids, 2 gather through cell ids
+// over a plane of 2 GiB or more (64-bit row addresses).
+template <int D, bool I8, int IDS, int NRB, int NW, bool IN_LOOP = false>
 __device__ __forceinline__ void attn_unit(const AttnArgs& a, int g, int s, int rbl, int tq, int p,
                                           int64_t c0l, int64_t cap_end, int seq_len,
                                           int id_first,
@@ -265,7 +267,7 @@ __device__ __forceinline__ void attn_unit(const AttnArgs& a, int g, int s, int r
   constexpr int QPT = Q::QPT;
   constexpr bool QPRE = Q::QPRE;
   auto q_load = [&](int slot, float4& u0, float4& u1) {
-    q_load_slot<D, I8, IDS>(a, s, g, tq, r0, slot, u0, u1);
+    q_load_slot<D, I8, (IDS != 0)>(a, s, g, tq, r0, slot, u0, u1);
   };
   // Per-row max |q| of the block.  A lane's slots all belong to its rows
   // 16k + lr; each wave reduces its slots in registers (qmx).  A one-wave
@@ -365,7 +367,11 @@ __device__ __forceinline__ void attn_unit(const AttnArgs& a, int g, int s, int r
   // a lane adds its cell's row offset (the split's ids are staged in LDS)
   // and list positions past the split map to kOut, past every resource.
   // Loads are therefore issued unconditionally, which keeps the compiler's
-  // wait counts exact. ----
+  // wait counts exact.  Wide gather (IDS 2: the sequence's rows of all KV
+  // heads span 2^31 bytes or more, past a 32-bit offset): plain 64-bit
+  // addresses, and a list position at or past the split's end reads the
+  // split's last row again, a row this split attends anyway, whose weight
+  // the softmax's edge mask sets to 0. ----
   const uint32_t rowstride = (uint32_t)a.Hk * RBY;           // bytes between cells of a KV head
   const uint32_t srow = (uint32_t)a.Hk * G::NG * 2;           // scale bytes between cells
   const size_t first_row = ((size_t)s * a.Lmax + (IDS ? 0 : c0)) * a.Hk + g;
@@ -377,6 +383,11 @@ __device__ __forceinline__ void attn_unit(const AttnArgs& a, int g, int s, int r
   const __amdgpu_buffer_rsrc_t rks = make_rsrc(I8 ? a.ksc + first_row * G::NG : nullptr, ncells * srow);
   const __amdgpu_buffer_rsrc_t rvs = make_rsrc(I8 ? a.vsc + first_row * G::NG : nullptr, ncells * srow);
   constexpr uint32_t kOut = 0x80000000u;                     // past every resource (< 2^31 bytes)
+  constexpr bool WIDE = IDS == 2;
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k) + first_row * RBY;
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v) + first_row * RBY;
+  const uint8_t* ksbase = reinterpret_cast<const uint8_t*>(I8 ? a.ksc + first_row * G::NG : nullptr);
+  const uint8_t* vsbase = reinterpret_cast<const uint8_t*>(I8 ? a.vsc + first_row * G::NG : nullptr);
   int32_t* idl = reinterpret_cast<int32_t*>(smem + L::BYTES);  // gather mode: ids of [c0, cend)
   if constexpr (IDS) {
     const int32_t* idrow = a.ids + ((size_t)s * a.T + tq) * a.B;
@@ -395,6 +406,15 @@ __device__ __forceinline__ void attn_unit(const AttnArgs& a, int g, int s, int r
     } else {
       return (uint32_t)(pos - c0) * stride;
     }
+  };
+  // Wide gather: byte offset of list position pos's row (the split's last
+  // row for positions at or past cend).
+  auto cell_off64 = [&](int pos, uint32_t stride) -> size_t {
+    const int i = (pos < cend ? pos : cend - 1) - c0;
+    return (size_t)(uint32_t)idl[i] * stride;
+  };
+  auto ld16 = [](const uint8_t* p) -> u32x4 {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   };
 
   struct KRegs {
@@ -435,16 +455,26 @@ __device__ __forceinline__ void attn_unit(const AttnArgs& a, int g, int s, int r
 #pragma unroll
       for (int u = 0; u < G::VLD; ++u) {
         const int rr = u * G::RPI + lane / G::CH;
-        const uint32_t vo = cell_off(ts + rr, rowstride) + 16 * (lane % G::CH);
-        R.k[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, vo, 0, kNT);
+        if constexpr (WIDE) {
+          R.k[u] = ld16(kbase + cell_off64(ts + rr, rowstride) + 16 * (lane % G::CH));
+        } else {
+          const uint32_t vo = cell_off(ts + rr, rowstride) + 16 * (lane % G::CH);
+          R.k[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, vo, 0, kNT);
+        }
       }
     } else {                     // the lane's MFMA operand fragments
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
-        const uint32_t vo = cell_off(ts + 16 * cb + lr, rowstride) + 16 * lb;
+        if constexpr (WIDE) {
+          const uint8_t* row = kbase + cell_off64(ts + 16 * cb + lr, rowstride) + 16 * lb;
 #pragma unroll
-        for (int j = 0; j < G::KLD; ++j)
-          R.k[cb * G::KLD + j] = __builtin_amdgcn_raw_buffer_load_b128(rk, vo + 64 * j, 0, kNT);
+          for (int j = 0; j < G::KLD; ++j) R.k[cb * G::KLD + j] = ld16(row + 64 * j);
+        } else {
+          const uint32_t vo = cell_off(ts + 16 * cb + lr, rowstride) + 16 * lb;
+#pragma unroll
+          for (int j = 0; j < G::KLD; ++j)
+            R.k[cb * G::KLD + j] = __builtin_amdgcn_raw_buffer_load_b128(rk, vo + 64 * j, 0, kNT);
+        }
       }
     }
   };
@@ -453,10 +483,26 @@ __device__ __forceinline__ void attn_unit(const AttnArgs& a, int g, int s, int r
 #pragma unroll
     for (int u = 0; u < G::VLD; ++u) {
       const int rr = u * G::RPI + lane / G::CH;
-      const uint32_t vo = cell_off(ts + rr, rowstride) + 16 * (lane % G::CH);
-      R.v[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, vo, 0, kNT);
+      if constexpr (WIDE) {
+        R.v[u] = ld16(vbase + cell_off64(ts + rr, rowstride) + 16 * (lane % G::CH));
+      } else {
+        const uint32_t vo = cell_off(ts + rr, rowstride) + 16 * (lane % G::CH);
+        R.v[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, vo, 0, kNT);
+      }
     }
-    if constexpr (I8) {
+    if constexpr (I8 && WIDE) {
+      const size_t so = cell_off64(ts + (lane & 31), srow);
+      if constexpr (G::NG == 4) {
+        R.ks = *reinterpret_cast<const u32x2*>(ksbase + so);
+        R.vs = *reinterpret_cast<const u32x2*>(vsbase + so);
+      } else if constexpr (G::NG == 2) {
+        R.ks[0] = *reinterpret_cast<const uint32_t*>(ksbase + so);
+        R.vs[0] = *reinterpret_cast<const uint32_t*>(vsbase + so);
+      } else {
+        R.ks[0] = *reinterpret_cast<const uint16_t*>(ksbase + so);
+        R.vs[0] = *reinterpret_cast<const uint16_t*>(vsbase + so);
+      }
+    } else if constexpr (I8) {
       const uint32_t vo = cell_off(ts + (lane & 31), srow);
       if constexpr (G::NG == 4) {
         R.ks = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rks, vo, 0, 0));
@@ -962,7 +1008,7 @@ __device__ __forceinline__ void attn_unit(const AttnArgs& a, int g, int s, int r
 // multiple of 8 every KV head of a (sequence, split) then runs on the same
 // XCD, so the heads' reads of the same cells (int8: the scale lines they
 // share, the neighbouring halves of each cell's K/V run) meet in one L2.
-template <int D, bool I8, bool IDS, int NRB, int NW>
+template <int D, bool I8, int IDS, int NRB, int NW>
 __global__ __launch_bounds__(64 * NW, (attn_occupancy<D, I8, NRB>())) void attn_mfma(AttnArgs a) {
   using Q = QSlots<D, NRB, NW>;
   const int tid = threadIdx.x;
@@ -989,7 +1035,7 @@ __global__ __launch_bounds__(64 * NW, (attn_occupancy<D, I8, NRB>())) void attn_
   if constexpr (Q::QPRE) {
 #pragma unroll
     for (int i = 0; i < Q::QPT; ++i)
-      q_load_slot<D, I8, IDS>(a, s, g, tq, rbl * 16 * NRB, tid + Q::NT * i, qv[i][0], qv[i][1]);
+      q_load_slot<D, I8, (IDS != 0)>(a, s, g, tq, rbl * 16 * NRB, tid + Q::NT * i, qv[i][0], qv[i][1]);
   }
   // Gather mode: the split's first NT cell ids do not depend on the
   // sequence length, so they are requested with it and the two reads
@@ -1077,7 +1123,7 @@ __global__ __launch_bounds__(64 * NW, (attn_occupancy<D, I8, NRB>())) void attn_
         for (int i = 0; i < Q::QPT; ++i)
           q_load_slot<D, I8, false>(a, s, g, 0, rbl * 16 * NRB, tid + Q::NT * i, qv[i][0], qv[i][1]);
       }
-      attn_unit<D, I8, false, NRB, NW, true>(a, g, s, rbl, 0, p, lo - c0, hi - c0, L, 0, qv);
+      attn_unit<D, I8, 0, NRB, NW, true>(a, g, s, rbl, 0, p, lo - c0, hi - c0, L, 0, qv);
       __syncthreads();                          // LDS is restaged by the next segment
     }
     st = c0 + ws;

@@ -85,6 +85,7 @@ struct AttnArgs {
   int S, T, Lmax, B, H, Hk, G, R, nrb, P, chunk;
   int seq_fast;      // 1: grid order with the sequence varying fastest, else the KV head
   int flat;          // 1: balanced partition, P pieces per (KV head, row block)
+  int wide;          // gather mode: 1 when a sequence's rows of all KV heads span >= 2^31 bytes
   int flat_pad;      // balanced partition: virtual cells before each non-empty window
   int* flat_n;       // balanced partition: [S] partial slots each sequence fills
   float qscale;      // scale * log2(e)

@@ -41,10 +41,11 @@ using gqa_kern::AttnArgs;
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// FLAT: the balanced-partition grid (dense windows only).
-template <int D, bool I8, bool IDS, int NRB, int NW, bool FLAT = false>
+// IDS: 0 dense, 1 gather, 2 gather over a plane of 2 GiB or more.  FLAT:
+// the balanced-partition grid (dense windows only).
+template <int D, bool I8, int IDS, int NRB, int NW, bool FLAT = false>
 hipError_t launch_one(const AttnArgs& a, dim3 grid, hipStream_t st) {
-  static_assert(!(FLAT && IDS), "the balanced partition covers dense windows");
+  static_assert(!(FLAT && IDS != 0), "the balanced partition covers dense windows");
   using L = gqa_kern::AttnLds<D, I8, NRB, NW>;
   // gather mode: the split's ids follow the fixed part, 16-byte aligned
   const int bytes = L::BYTES + (IDS ? (a.chunk * 4 + 15) / 16 * 16 : 0);
@@ -82,11 +83,13 @@ constexpr bool fits_lds() {
 template <int D, bool I8, int NRB>
 hipError_t launch_attn_nw(const AttnArgs& a, bool ids, int nw, dim3 grid, hipStream_t st) {
   static_assert(fits_lds<D, I8, NRB, 4>() && fits_lds<D, I8, NRB, 1>(), "LDS budget");
-  if (a.flat) return launch_one<D, I8, false, NRB, 4, true>(a, grid, st);
-  if (nw == 1)
-    return ids ? launch_one<D, I8, true, NRB, 1>(a, grid, st)
-               : launch_one<D, I8, false, NRB, 1>(a, grid, st);
-  return ids ? launch_one<D, I8, true, NRB, 4>(a, grid, st) : launch_one<D, I8, false, NRB, 4>(a, grid, st);
+  if (a.flat) return launch_one<D, I8, 0, NRB, 4, true>(a, grid, st);
+  if (nw == 1) {
+    if (!ids) return launch_one<D, I8, 0, NRB, 1>(a, grid, st);
+    return a.wide ? launch_one<D, I8, 2, NRB, 1>(a, grid, st) : launch_one<D, I8, 1, NRB, 1>(a, grid, st);
+  }
+  if (!ids) return launch_one<D, I8, 0, NRB, 4>(a, grid, st);
+  return a.wide ? launch_one<D, I8, 2, NRB, 4>(a, grid, st) : launch_one<D, I8, 1, NRB, 4>(a, grid, st);
 }
 
 template <int D, bool I8>
@@ -124,7 +127,6 @@ int attn_common(bool i8, const float* q, const void* k, const void* v, const uin
   if (flat ? (!gqa::balanced_ok(sh, chunk) || Lmax > gqa::max_chunk(sh))
            : (chunk <= 0 || chunk > gqa::max_chunk(sh)))
     return GQA_ERR_CHUNK;
-  if (ids && (int64_t)Lmax * Hk * D * (i8 ? 1 : 2) >= ((int64_t)1 << 31)) return GQA_ERR_SHAPE;
   const size_t need = gqa::part_bytes(sh, chunk);
   const int64_t P = gqa::num_splits(sh, chunk);
   if (P > 0 && need == 0) return GQA_ERR_SHAPE;   // the partials would not fit any address space
@@ -139,6 +141,9 @@ int attn_common(bool i8, const float* q, const void* k, const void* v, const uin
   a.S = S; a.T = T; a.Lmax = Lmax; a.B = sh.B; a.H = H; a.Hk = Hk; a.G = H / Hk;
   a.R = (int)gqa::rows_per_unit(sh); a.nrb = (int)gqa::row_blocks(sh); a.P = (int)P; a.chunk = chunk;
   a.flat = flat ? 1 : 0;
+  // gather over a sequence whose rows of all KV heads span 2^31 bytes or
+  // more: 64-bit row addresses instead of 32-bit buffer offsets
+  a.wide = (ids && (int64_t)Lmax * Hk * D * (i8 ? 1 : 2) >= ((int64_t)1 << 31)) ? 1 : 0;
   a.flat_pad = gqa::flat_pad_cells(sh);
   a.flat_n = reinterpret_cast<int*>(part + gqa::flat_n_offset_floats(sh, P));
   a.qscale = scale * kLog2e;

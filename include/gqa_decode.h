@@ -51,6 +51,9 @@
  *    distinct cells of the token's window [0, L_t).  An id outside [0, Lmax)
  *    is clamped into range, so a bad id yields a wrong row, never an
  *    out-of-bounds read.
+ *  - Size limits: any Lmax with ids (a sequence whose rows span 2^31 bytes
+ *    or more is addressed with 64-bit row pointers); a dense split's K rows
+ *    must span less than 2^31 bytes (see `chunk`).
  *  - K/V traffic: one workgroup serves every query row of a KV head (the
  *    H / Hk heads of the group, times the T tokens of a dense window), so
  *    each K/V row is read once per split, up to 64 rows per KV head for
