@@ -1071,19 +1071,26 @@ __global__ __launch_bounds__(64 * NW, (attn_occupancy<D, I8, NRB>())) void attn_
   id /= a.Hk;
   const int rbl = id % a.nrb;
   const int j = id / a.nrb;
-  int W = 0;                                    // total span, 64 sequences per pass
-  for (int c = 0; c < a.S; c += 64) {
+  // The first 64 lengths stay in registers (one per lane) for the whole
+  // walk: the plan needs one round trip to memory before the first unit's
+  // requests, and the walk reads them with lane reads.  Batches of more
+  // than 64 sequences read the rest in passes of 64.
+  const int L0 = lane < a.S ? a.seq_lens[lane] : 0;
+  const int w0 = lane < a.S ? flat_span(L0, a.Lmax, pad) : 0;
+  int W = wave_sum_i(w0);                       // total span
+  for (int c = 64; c < a.S; c += 64) {
     const int si = c + lane;
     W += wave_sum_i(si < a.S ? flat_span(a.seq_lens[si], a.Lmax, pad) : 0);
   }
   const int Pe = a.P < W ? a.P : W;
+  const int end0 = wave_incl_scan_i(w0);        // span ends of sequences 0..63
   if (blockIdx.x == 0 && tid < 64) {
     // every sequence's slot count, for the merge
     int base = 0;
     for (int c = 0; c < a.S; c += 64) {
       const int si = c + lane;
-      const int w = si < a.S ? flat_span(a.seq_lens[si], a.Lmax, pad) : 0;
-      const int end = base + wave_incl_scan_i(w);
+      const int w = c == 0 ? w0 : (si < a.S ? flat_span(a.seq_lens[si], a.Lmax, pad) : 0);
+      const int end = c == 0 ? end0 : base + wave_incl_scan_i(w);
       if (si < a.S)
         a.flat_n[si] = w > 0 ? flat_piece(end - 1, W, Pe) - flat_piece(end - w + pad, W, Pe) + 1 : 0;
       base = __builtin_amdgcn_readlane(end, 63);
@@ -1092,24 +1099,34 @@ __global__ __launch_bounds__(64 * NW, (attn_occupancy<D, I8, NRB>())) void attn_
   if (j >= Pe) return;                          // also W == 0: nothing visible anywhere
   const int b0 = flat_bound(j, W, Pe), b1 = flat_bound(j + 1, W, Pe);
   // the first sequence whose span reaches past b0, and where its span starts
-  int s = a.S, st = 0, base = 0;
-  for (int c = 0; c < a.S; c += 64) {
-    const int si = c + lane;
-    const int w = si < a.S ? flat_span(a.seq_lens[si], a.Lmax, pad) : 0;
-    const int end = base + wave_incl_scan_i(w);
-    const uint64_t m = __ballot(w > 0 && end > b0);
+  int s = a.S, st = 0;
+  {
+    const uint64_t m = __ballot(w0 > 0 && end0 > b0);
     if (m) {
       const int l = __builtin_ctzll(m);
-      s = c + l;
-      st = __builtin_amdgcn_readlane(end, l) - __builtin_amdgcn_readlane(w, l);
-      break;
+      s = l;
+      st = __builtin_amdgcn_readlane(end0, l) - __builtin_amdgcn_readlane(w0, l);
+    } else {
+      int base = __builtin_amdgcn_readlane(end0, 63);
+      for (int c = 64; c < a.S; c += 64) {
+        const int si = c + lane;
+        const int w = si < a.S ? flat_span(a.seq_lens[si], a.Lmax, pad) : 0;
+        const int end = base + wave_incl_scan_i(w);
+        const uint64_t mc = __ballot(w > 0 && end > b0);
+        if (mc) {
+          const int l = __builtin_ctzll(mc);
+          s = c + l;
+          st = __builtin_amdgcn_readlane(end, l) - __builtin_amdgcn_readlane(w, l);
+          break;
+        }
+        base = __builtin_amdgcn_readlane(end, 63);
+      }
     }
-    base = __builtin_amdgcn_readlane(end, 63);
   }
   s = __builtin_amdgcn_readfirstlane(s);
   st = __builtin_amdgcn_readfirstlane(st);
   for (; s < a.S && st < b1; ++s) {
-    const int L = a.seq_lens[s];
+    const int L = s < 64 ? __builtin_amdgcn_readlane(L0, s) : a.seq_lens[s];
     const int ws = flat_window(L, a.Lmax);
     if (ws == 0) continue;
     const int c0 = st + pad;                    // the window's first real cell
