@@ -14,7 +14,8 @@ from . import _lib
 from ._lib import (GqaDecodeError, gqa_decode_attn_f16, gqa_decode_attn_i8, gqa_decode_merge,
                    gqa_decode_merge_gated, gqa_decode_attn_tq, gqa_decode_merge_tq,
                    gqa_decode_select_ids, gqa_decode_append_i8,
-                   gqa_decode_part_bytes, gqa_decode_auto_chunk, gqa_decode_step_static,
+                   gqa_decode_part_bytes, gqa_decode_auto_chunk, gqa_decode_auto_pieces,
+                   gqa_decode_step_static,
                    gqa_bench_stream_read, strerror)
 
 __all__ = ["decode_attention", "DecodeAttention", "GqaDecodeError", "gqa_decode_attn_f16",
@@ -23,7 +24,8 @@ __all__ = ["decode_attention", "DecodeAttention", "GqaDecodeError", "gqa_decode_
            "gqa_decode_select_ids", "select_ids",
            "gqa_decode_append_i8", "append_i8",
            "gqa_decode_part_bytes", "gqa_decode_step_static",
-           "gqa_decode_auto_chunk", "gqa_bench_stream_read", "strerror"]
+           "gqa_decode_auto_chunk", "gqa_decode_auto_pieces", "gqa_bench_stream_read",
+           "strerror"]
 
 
 def _raw_stream_getter():
@@ -41,14 +43,19 @@ class DecodeAttention:
     the current torch stream at each call (or on `stream`, a raw
     hipStream_t).  The per-call path is argument marshalling only."""
 
-    def __init__(self, S, T, H, Hk, D, Lmax, kv: str, B: int = 0, chunk: int = 0, device="cuda"):
+    def __init__(self, S, T, H, Hk, D, Lmax, kv: str, B: int = 0, chunk=0, device="cuda"):
         """chunk: cells per split; 0 picks one (gqa_decode_auto_chunk); -P
         cuts the dense windows of the whole batch, laid end to end, into P
-        equal pieces per KV head (the balanced partition)."""
+        equal pieces per KV head (the balanced partition, for batches of
+        uneven lengths); "balanced" picks P (gqa_decode_auto_pieces)."""
         import torch
         self.S, self.T, self.H, self.Hk, self.D, self.Lmax, self.B = S, T, H, Hk, D, Lmax, B
         self.kv = kv
-        if chunk == 0:
+        if chunk == "balanced":
+            chunk = gqa_decode_auto_pieces(S, T, Lmax, H, Hk, D, kv == "i8")
+            if chunk >= 0 or B:
+                raise GqaDecodeError("gqa_decode_auto_pieces", chunk if chunk < 0 else _lib.GQA_ERR_CHUNK)
+        elif chunk == 0:
             chunk = gqa_decode_auto_chunk(S, T, Lmax, B, H, Hk, D, kv == "i8")
             if chunk <= 0:
                 raise GqaDecodeError("gqa_decode_auto_chunk", chunk)
@@ -155,10 +162,12 @@ def _validate(q, k, v, seq_lens, k_scales, v_scales, ids):
 
 
 def decode_attention(q, k, v, seq_lens, scale: Optional[float] = None, *, k_scales=None,
-                     v_scales=None, ids=None, chunk: int = 0, gate=None):
+                     v_scales=None, ids=None, chunk=0, gate=None):
     """One decode step.  q [S][T][H][D] float32; k, v [S][Lmax][Hk][D]
     float16, or int8 with k_scales / v_scales [S][Lmax][Hk][D/64] float16;
     seq_lens [S] int32 (cells visible to each sequence's last query token);
+    chunk: cells per split, 0 for the library's choice, -P or "balanced" for
+    the balanced partition of a batch of uneven lengths (dense only);
     ids None or [S][T][B] int32; gate None or float32 [S][T][H][D], possibly
     the gate half of [query | gate] rows (a view whose last dim is contiguous
     and whose head rows are evenly strided).  Returns out [S][T][H][D]
@@ -196,7 +205,7 @@ _PLANS_MAX = 16
 
 
 def _planned_step(S, T, H, Hk, D, Lmax, kv, B, chunk, device):
-    key = (S, T, H, Hk, D, Lmax, kv, B, int(chunk), str(device))
+    key = (S, T, H, Hk, D, Lmax, kv, B, chunk if chunk == "balanced" else int(chunk), str(device))
     step = _PLANS.get(key)
     if step is None:
         if len(_PLANS) >= _PLANS_MAX:

@@ -26,7 +26,7 @@ GQA_STATIC_PART_BYTES = 16 << 20
 EXPORTED = ["gqa_decode_attn_f16", "gqa_decode_attn_i8", "gqa_decode_merge",
             "gqa_decode_merge_gated", "gqa_decode_attn_tq", "gqa_decode_merge_tq",
             "gqa_decode_select_ids", "gqa_decode_append_i8", "gqa_decode_part_bytes",
-            "gqa_decode_auto_chunk", "gqa_decode_step_static",
+            "gqa_decode_auto_chunk", "gqa_decode_auto_pieces", "gqa_decode_step_static",
             "gqa_decode_strerror", "gqa_bench_stream_read"]
 
 _lib = None
@@ -69,6 +69,8 @@ def load() -> ctypes.CDLL:
     lib.gqa_decode_part_bytes.restype = sz
     lib.gqa_decode_auto_chunk.argtypes = [i32] * 8
     lib.gqa_decode_auto_chunk.restype = i32
+    lib.gqa_decode_auto_pieces.argtypes = [i32] * 7
+    lib.gqa_decode_auto_pieces.restype = i32
     lib.gqa_decode_step_static.argtypes = [vp] * 8 + [i32] * 7 + [f32, i32, i32, vp]
     lib.gqa_decode_step_static.restype = i32
     lib.gqa_decode_strerror.argtypes = [i32]
@@ -133,6 +135,11 @@ def gqa_decode_part_bytes(S, T, Lmax, B, H, D, chunk) -> int:
 def gqa_decode_auto_chunk(S, T, Lmax, B, H, Hk, D, kv_kind) -> int:
     """kv_kind: 0 (or False) f16, 1 (or True) int8, 2 TurboQuant."""
     return load().gqa_decode_auto_chunk(S, T, Lmax, B, H, Hk, D, int(kv_kind))
+
+
+def gqa_decode_auto_pieces(S, T, Lmax, H, Hk, D, kv_kind) -> int:
+    """The balanced partition's chunk argument (-P); kv_kind 0 f16, 1 int8."""
+    return load().gqa_decode_auto_pieces(S, T, Lmax, H, Hk, D, int(kv_kind))
 
 
 def gqa_decode_step_static(q, k, v, k_scales, v_scales, ids, seq_lens, out, S, T, Lmax, B, H, Hk,

@@ -1066,11 +1066,26 @@ __global__ __launch_bounds__(64 * NW, (attn_occupancy<D, I8, NRB>())) void attn_
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int pad = a.flat_pad;
+  // int8 rows with a piece count divisible by the 8 XCDs: pieces vary
+  // fastest within groups of eight, so every KV head (and row block) of a
+  // piece runs on the same XCD and the int8 scale lines the heads share
+  // (both heads' scales of a cell sit in one 16-byte run) meet in one L2,
+  // as the split grid's sequence-fastest order does; otherwise the KV head
+  // varies fastest.
   int id = blockIdx.x;
-  const int g = id % a.Hk;
-  id /= a.Hk;
-  const int rbl = id % a.nrb;
-  const int j = id / a.nrb;
+  int g, rbl, j;
+  if (I8 && a.P % 8 == 0) {
+    const int per = 8 * a.Hk * a.nrb;
+    const int rem = id % per;
+    j = id / per * 8 + rem % 8;
+    g = rem / 8 % a.Hk;
+    rbl = rem / 8 / a.Hk;
+  } else {
+    g = id % a.Hk;
+    id /= a.Hk;
+    rbl = id % a.nrb;
+    j = id / a.nrb;
+  }
   // The first 64 lengths stay in registers (one per lane) for the whole
   // walk: the plan needs one round trip to memory before the first unit's
   // requests, and the walk reads them with lane reads.  Batches of more

@@ -52,6 +52,24 @@ int auto_chunk(const Shape& s) {
   return (int)chunk;
 }
 
+// Pieces per (KV head, row block) of the balanced partition: one four-wave
+// workgroup per compute unit (256 of them), measured best on uneven batches
+// (f16 batch at 32 pieces per KV head: 57.5 us against 60.1 at 64 and
+// 61.7 at 28), rounded down to a multiple of the 8 XCDs when that is at
+// least 8.  Returned negated, as the chunk argument that selects it.
+int auto_pieces(const Shape& s) {
+  int rc = check_shape(s);
+  if (rc != GQA_OK) return rc;
+  if (s.ids || s.tq) return GQA_ERR_CHUNK;       // the partition covers dense windows
+  const int64_t units = (int64_t)s.Hk * row_blocks(s);
+  int64_t P = 256 / units;
+  if (P >= 8) P = P / 8 * 8;
+  if (P < 1) P = 1;
+  if (P > kMaxPieces) P = kMaxPieces;
+  if (!balanced_ok(s, (int)-P)) return GQA_ERR_CHUNK;
+  return (int)-P;
+}
+
 size_t part_bytes(const Shape& s, int chunk) {
   if (chunk == 0 || (chunk < 0 && !balanced_ok(s, chunk)) || check_shape(s) != GQA_OK) return 0;
   const int64_t P = num_splits(s, chunk);
@@ -79,6 +97,12 @@ int gqa_decode_auto_chunk(int S, int T, int Lmax, int B, int H, int Hk, int D, i
   if (kv_kind < 0 || kv_kind > 2) return GQA_ERR_SHAPE;
   gqa::Shape s{S, T, Lmax, B, H, Hk, D, B > 0, kv_kind != 0, kv_kind == 2};
   return gqa::auto_chunk(s);
+}
+
+int gqa_decode_auto_pieces(int S, int T, int Lmax, int H, int Hk, int D, int kv_kind) {
+  if (kv_kind < 0 || kv_kind > 1) return GQA_ERR_SHAPE;
+  gqa::Shape s{S, T, Lmax, 0, H, Hk, D, false, kv_kind == 1, false};
+  return gqa::auto_pieces(s);
 }
 
 const char* gqa_decode_strerror(int code) {

@@ -102,6 +102,7 @@ inline int waves_per_block(const Shape& s, int chunk) {
 
 int check_shape(const Shape& s);               // GQA_OK or GQA_ERR_*
 int auto_chunk(const Shape& s);                // > 0, or GQA_ERR_*
+int auto_pieces(const Shape& s);               // -P (balanced partition), or GQA_ERR_*
 size_t part_bytes(const Shape& s, int chunk);  // 0 on bad arguments
 
 // Offsets (in floats) of the two regions of the partial workspace:

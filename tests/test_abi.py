@@ -161,6 +161,25 @@ def test_auto_chunk_plan():
     assert ac(4, 1, 131072, 0, 32, 8, 128, 3) == _lib.GQA_ERR_SHAPE
 
 
+def test_auto_pieces_plan():
+    ap = gq.gqa_decode_auto_pieces
+    # one workgroup per compute unit: 256 / (KV heads x row blocks), a
+    # multiple of 8 when at least 8, returned as the chunk argument (-P)
+    assert ap(32, 1, 4096, 32, 8, 128, 0) == -32         # the f16 batch
+    assert ap(8, 1, 32768, 24, 2, 256, 1) == -128        # int8, 2 KV heads
+    assert ap(4, 4, 260, 32, 2, 256, 1) == -64           # two row blocks (64 rows at hd 256)
+    assert ap(1, 1, 256, 24, 3, 64, 0) == -80            # 256 / 3 = 85 -> 80
+    assert ap(1, 1, 256, 512, 512, 64, 0) == -1
+    assert ap(1, 1, 256, 8, 2, 64, 2) == _lib.GQA_ERR_SHAPE          # no TurboQuant form
+    assert ap(1 << 20, 1, 1 << 20, 8, 2, 64, 0) == _lib.GQA_ERR_CHUNK  # total window past 2^31
+    assert ap(1, 1, 256, 9, 2, 64, 0) == _lib.GQA_ERR_GROUP
+    for args in [(32, 1, 4096, 32, 8, 128, 0), (8, 1, 32768, 24, 2, 256, 1)]:
+        P = -ap(*args)
+        S, T, Lmax, H, Hk, D, _ = args
+        assert gq.gqa_decode_part_bytes(S, T, Lmax, 0, H, D, -P) == \
+            S * T * H * P * (D + 2) * 4 + (S * 4 + 15) // 16 * 16
+
+
 def test_python_wrapper_refuses_cpu_tensors():
     import torch
     q = torch.zeros(1, 1, 8, 64)

@@ -175,9 +175,34 @@ def test_static_step_takes_the_balanced_partition():
         assert_parity(out.cpu().numpy(), oracle(inp), f"static balanced P={P}")
 
 
+@pytest.mark.parametrize("kv,H,Hk,D", [("i8", 24, 2, 256), ("f16", 32, 8, 128), ("i8", 16, 4, 64)])
+def test_balanced_keyword_on_uneven_batches(kv, H, Hk, D):
+    # chunk="balanced": the piece count the library picks (256 workgroups;
+    # int8 with a piece count divisible by 8 puts a piece's KV heads on one
+    # XCD)
+    rng = np.random.default_rng(91)
+    lens = rng.integers(0, 3000, size=24)
+    lens[[2, 9]] = 0
+    lens[5] = 3000
+    inp = make_case(24, 1, H, Hk, D, 3000, lens, kv=kv, seed=93)
+    assert_parity(run_gpu(inp, "balanced"), oracle(inp), f"balanced keyword kv={kv} D={D}")
+
+
 @pytest.mark.parametrize("P", [32, 64])
 def test_full_size_f16_batch(P):
     inp = make_inputs("f16_batch")
     print("[gpu] full-size f16_batch: oracle", flush=True)
     ref = oracle(inp)
     assert_parity(run_gpu(inp, -P), ref, f"f16_batch P={P}")
+
+
+def test_full_size_int8_batch():
+    # the int8 batch of uneven lengths the bench times, in its launch
+    # configuration (128 pieces per KV head) and with the automatic split
+    from workloads import WORKLOADS
+    inp = make_inputs("i8_batch")
+    print("[gpu] full-size i8_batch: oracle", flush=True)
+    ref = oracle(inp)
+    dev = to_dev(inp)
+    for chunk in (WORKLOADS["i8_batch"].chunk, 0):
+        assert_parity(run_gpu(inp, chunk, dev=dev), ref, f"i8_batch chunk={chunk}")

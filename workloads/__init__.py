@@ -71,6 +71,12 @@ WORKLOADS = {
         Workload("f16_mq_causal", 4, S=4, T=8, H=32, Hk=8, D=128, Lmax=131072, kv="f16",
                  scale=1.0 / math.sqrt(128.0), chunk=0, lens="full",
                  description="multi-query causal chunk: 4 seqs x 8 tokens at start 131064, context 131072, 32/8 heads, hd 128"),
+        # not one of the pages' configurations: the int8 32K model's heads over
+        # a batch of uneven lengths, where the balanced partition pays most
+        Workload("i8_batch", 8, S=32, T=1, H=24, Hk=2, D=256, Lmax=16384, kv="i8",
+                 scale=1.0 / 16.0, chunk=-128, lens="uniform:2048:16384",
+                 description="int8 decode batch of uneven lengths: 32 seqs, lengths U[2048,16384], 24/2 heads, "
+                             "hd 256; balanced partition, 128 pieces per KV head"),
     ]
 }
 WORKLOAD_ORDER = sorted(WORKLOADS, key=lambda n: WORKLOADS[n].index)
