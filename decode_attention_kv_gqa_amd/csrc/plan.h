@@ -41,7 +41,7 @@ constexpr int kMaxPieces = 1 << 16;
 // cut into equal pieces (no ids; the total window, at most S * Lmax cells,
 // below 2^31).
 // (The total span, windows plus their pad cells, stays below 2^31: the pad
-// is at most 512 cells.)
+// is at most 1024 cells.)
 inline bool balanced_ok(const Shape& s, int chunk) {
   return chunk < 0 && -(int64_t)chunk <= kMaxPieces && !s.ids && !s.tq &&
          (int64_t)s.S * ((int64_t)s.Lmax + 1024) < ((int64_t)1 << 31);
@@ -119,12 +119,15 @@ inline size_t flat_n_offset_floats(const Shape& s, int64_t P) {
 
 // Virtual cells charged for each non-empty window in the balanced
 // partition: the cost of starting a sequence inside a workgroup, as the
-// cells that stream in that time.  kFlatPadBytes of K + V rows of one KV
-// head per sequence start.
+// cells that stream in that time.  64 KB of K + V rows of one KV head per
+// sequence start for f16 rows, 128 KB for int8 rows, whose tiles cost more
+// arithmetic to drain and refill (measured best: f16 batch 32 KB 58.2-58.5,
+// 64 KB 57.5-57.6, 128 KB 57.6-57.7 us; int8 uneven batch 32 KB 57.0,
+// 64 KB 56.1, 128 KB 54.8-55.0, 256 KB 56.0 us).
 constexpr int64_t kFlatPadBytes = 64 * 1024;
 inline int flat_pad_cells(const Shape& s) {
   const int64_t cell = 2 * (int64_t)s.D * (s.i8 ? 1 : 2);   // K + V bytes of one KV head
-  return (int)(kFlatPadBytes / cell);
+  return (int)((s.i8 ? 2 : 1) * kFlatPadBytes / cell);
 }
 
 }  // namespace gqa
