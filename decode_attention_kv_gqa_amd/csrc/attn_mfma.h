@@ -1097,17 +1097,21 @@ __global__ __launch_bounds__(64 * NW, (attn_occupancy<D, I8, NRB>())) void attn_
     const int si = c + lane;
     W += wave_sum_i(si < a.S ? flat_span(a.seq_lens[si], a.Lmax, pad) : 0);
   }
-  const int Pe = a.P < W ? a.P : W;
+  const int Pe = a.P < W / kFlatQ ? a.P : W / kFlatQ;
   const int end0 = wave_incl_scan_i(w0);        // span ends of sequences 0..63
   if (blockIdx.x == 0 && tid < 64) {
     // every sequence's slot count, for the merge
     int base = 0;
     for (int c = 0; c < a.S; c += 64) {
       const int si = c + lane;
-      const int w = c == 0 ? w0 : (si < a.S ? flat_span(a.seq_lens[si], a.Lmax, pad) : 0);
+      const int Ls = c == 0 ? L0 : (si < a.S ? a.seq_lens[si] : 0);
+      const int w = c == 0 ? w0 : (si < a.S ? flat_span(Ls, a.Lmax, pad) : 0);
       const int end = c == 0 ? end0 : base + wave_incl_scan_i(w);
+      const int first = end - w + pad;         // the window's first real cell
       if (si < a.S)
-        a.flat_n[si] = w > 0 ? flat_piece(end - 1, W, Pe) - flat_piece(end - w + pad, W, Pe) + 1 : 0;
+        a.flat_n[si] = w > 0 ? flat_piece(first + flat_window(Ls, a.Lmax) - 1, W, Pe) -
+                                   flat_piece(first, W, Pe) + 1
+                             : 0;
       base = __builtin_amdgcn_readlane(end, 63);
     }
   }
@@ -1158,7 +1162,7 @@ __global__ __launch_bounds__(64 * NW, (attn_occupancy<D, I8, NRB>())) void attn_
       attn_unit<D, I8, 0, NRB, NW, true>(a, g, s, rbl, 0, p, lo - c0, hi - c0, L, 0, qv);
       __syncthreads();                          // LDS is restaged by the next segment
     }
-    st = c0 + ws;
+    st = c0 + (ws + kFlatQ - 1) / kFlatQ * kFlatQ;
   }
 }
 

@@ -55,18 +55,26 @@ __device__ __forceinline__ int wave_incl_scan_i(int x) {
 __device__ __forceinline__ int flat_window(int seq_len, int Lmax) {
   return seq_len < 0 ? 0 : (seq_len > Lmax ? Lmax : seq_len);
 }
-// Cells a window takes in the concatenation: its pad and its cells, or none.
+// The concatenation is cut in units of kFlatQ cells (a round of 32-cell
+// tiles over four waves): pads are whole units and windows are rounded up to
+// whole units, so sequences start on unit boundaries and a piece boundary
+// inside a sequence never splits a round of tiles.
+constexpr int kFlatQ = 128;
+// Cells a window takes in the concatenation: its pad and its cells rounded
+// up to whole units, or none.
 __device__ __forceinline__ int flat_span(int seq_len, int Lmax, int pad) {
   const int w = flat_window(seq_len, Lmax);
-  return w > 0 ? w + pad : 0;
+  return w > 0 ? (w + kFlatQ - 1) / kFlatQ * kFlatQ + pad : 0;
 }
+// Piece j of Pe over a span of W cells (both in whole units).
 __device__ __forceinline__ int flat_bound(int j, int W, int Pe) {
-  return (int)((int64_t)j * W / Pe);
+  return (int)((int64_t)j * (W / kFlatQ) / Pe) * kFlatQ;
 }
 // The piece holding position x in [0, W): the largest j with flat_bound(j)
-// <= x, i.e. ceil((x + 1) Pe / W) - 1.
+// <= x.
 __device__ __forceinline__ int flat_piece(int x, int W, int Pe) {
-  return (int)(((int64_t)(x + 1) * Pe + W - 1) / W) - 1;
+  const int64_t Wu = W / kFlatQ;
+  return (int)(((int64_t)(x / kFlatQ + 1) * Pe + Wu - 1) / Wu) - 1;
 }
 
 // Arguments of the chunk kernel.  Query rows of a unit (one sequence, one KV

@@ -40,11 +40,11 @@ constexpr int kMaxPieces = 1 << 16;
 // (KV head, row block): the dense windows of all sequences, laid end to end,
 // cut into equal pieces (no ids; the total window, at most S * Lmax cells,
 // below 2^31).
-// (The total span, windows plus their pad cells, stays below 2^31: the pad
-// is at most 1024 cells.)
+// (The total span, windows rounded up to 128-cell units plus their pad
+// cells, stays below 2^31: the pad is at most 1024 cells.)
 inline bool balanced_ok(const Shape& s, int chunk) {
   return chunk < 0 && -(int64_t)chunk <= kMaxPieces && !s.ids && !s.tq &&
-         (int64_t)s.S * ((int64_t)s.Lmax + 1024) < ((int64_t)1 << 31);
+         (int64_t)s.S * ((int64_t)s.Lmax + 1152) < ((int64_t)1 << 31);
 }
 
 // Partial slots per query row: the split count, or the piece count of the
@@ -127,7 +127,8 @@ inline size_t flat_n_offset_floats(const Shape& s, int64_t P) {
 constexpr int64_t kFlatPadBytes = 64 * 1024;
 inline int flat_pad_cells(const Shape& s) {
   const int64_t cell = 2 * (int64_t)s.D * (s.i8 ? 1 : 2);   // K + V bytes of one KV head
-  return (int)((s.i8 ? 2 : 1) * kFlatPadBytes / cell);
+  const int64_t pad = (s.i8 ? 2 : 1) * kFlatPadBytes / cell;
+  return (int)((pad + 127) / 128 * 128);      // whole 128-cell units
 }
 
 }  // namespace gqa

@@ -92,7 +92,7 @@ enum {
   GQA_ERR_CHUNK = -6,      /* chunk 0 in the merge, a split wider than 2^31
                               bytes of K rows (chunk * Hk * D * elem >= 2^31),
                               or a balanced partition (chunk < 0) outside its
-                              limits (ids, P > 65536, S * (Lmax + 1024) >= 2^31,
+                              limits (ids, P > 65536, S * (Lmax + 1152) >= 2^31,
                               Lmax * Hk * D * elem >= 2^31)                      */
   GQA_ERR_WORKSPACE = -7,  /* part_bytes < gqa_decode_part_bytes(...)            */
   GQA_ERR_STATIC_LIMIT = -8 /* gqa_decode_step_static: the partials need more than
@@ -153,8 +153,10 @@ int gqa_decode_auto_pieces(int S, int T, int Lmax, int H, int Hk, int D, int kv_
  *             and the total is cut into P near-equal pieces per KV head
  *             (and row block), one workgroup each, that may cross sequence
  *             boundaries; a piece writes one partial per sequence it
- *             touches.  Needs ids == NULL, P <= 65536 and
- *             S * (Lmax + 1024) < 2^31.  (qsa2.metal's chunk partials and
+ *             touches.  The windows are rounded up, and the pieces cut, in
+ *             whole units of 128 cells (a round of 32-cell tiles over a
+ *             workgroup's four waves).  Needs ids == NULL, P <= 65536 and
+ *             S * (Lmax + 1152) < 2^31.  (qsa2.metal's chunk partials and
  *             log-sum-exp merge do not depend on where the chunks start, so
  *             any cut of a window gives the same result up to rounding.)
  *             chunk * Hk * D * (bytes per element) must stay below 2^31

@@ -58,10 +58,10 @@ static void check_shape_case(int S, int T, int Lmax, int B, int H, int Hk, int D
     if (ofl < ((i128)1 << 62)) CHECK((i128)gqa::part_o_floats(s, P) == ofl, "part_o_floats");
   }
   // balanced partition (negative chunk): dense windows only, at most 65536
-  // pieces, S * (Lmax + 1024) below 2^31; P slots per row, then S int32
+  // pieces, S * (Lmax + 1152) below 2^31; P slots per row, then S int32
   // slot counts rounded up to 16 bytes
   for (int c : {-1, -7, -32, -65536, -65537, -2147483647 - 1}) {
-    const bool ok = !ids && (i128)-(i128)c <= 65536 && (i128)S * ((i128)Lmax + 1024) < ((i128)1 << 31);
+    const bool ok = !ids && (i128)-(i128)c <= 65536 && (i128)S * ((i128)Lmax + 1152) < ((i128)1 << 31);
     CHECK(gqa::balanced_ok(s, c) == ok, "balanced_ok S=%d Lmax=%d c=%d ids=%d", S, Lmax, c, (int)ids);
     const size_t got = gqa::part_bytes(s, c);
     if (!ok) {
@@ -74,7 +74,8 @@ static void check_shape_case(int S, int T, int Lmax, int B, int H, int Hk, int D
     if (bytes < ((i128)1 << 62)) CHECK((i128)got == bytes, "balanced part_bytes %zu vs %lld", got, (long long)bytes);
     const i128 off = (i128)S * T * H * P * (D + 2);
     if (off < ((i128)1 << 62)) CHECK((i128)gqa::flat_n_offset_floats(s, P) == off, "flat_n_offset_floats");
-    CHECK(gqa::flat_pad_cells(s) == (i8 ? 131072 / (2 * D) : 65536 / (4 * D)), "flat_pad_cells");
+    const int pad = i8 ? 131072 / (2 * D) : 65536 / (4 * D);
+    CHECK(gqa::flat_pad_cells(s) == (pad + 127) / 128 * 128, "flat_pad_cells");
   }
   CHECK(gqa_decode_part_bytes(S, T, Lmax, ids ? B : 0, H, D, chunk) ==
             gqa::part_bytes(gqa::Shape{S, T, Lmax, ids ? B : 0, H, H, D, ids, false}, chunk),
