@@ -1065,7 +1065,6 @@ __global__ __launch_bounds__(64 * NW, (attn_occupancy<D, I8, NRB>())) void attn_
   using Q = QSlots<D, NRB, NW>;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int pad = a.flat_pad;
   // int8 rows with a piece count divisible by the 8 XCDs: pieces vary
   // fastest within groups of eight, so every KV head (and row block) of a
   // piece runs on the same XCD and the int8 scale lines the heads share
@@ -1091,6 +1090,22 @@ __global__ __launch_bounds__(64 * NW, (attn_occupancy<D, I8, NRB>())) void attn_
   // requests, and the walk reads them with lane reads.  Batches of more
   // than 64 sequences read the rest in passes of 64.
   const int L0 = lane < a.S ? a.seq_lens[lane] : 0;
+  // Windows all of one length (empty ones aside): pieces can align with the
+  // sequences, and a pad would only shift them off, so none is charged.
+  int wlo, whi;
+  {
+    const int x = flat_window(L0, a.Lmax);
+    wlo = x > 0 ? x : 0x7fffffff;
+    whi = x;
+    for (int c = 64; c < a.S; c += 64) {
+      const int y = c + lane < a.S ? flat_window(a.seq_lens[c + lane], a.Lmax) : 0;
+      wlo = y > 0 && y < wlo ? y : wlo;
+      whi = y > whi ? y : whi;
+    }
+    wlo = wave_min_i(wlo);
+    whi = wave_max_i(whi);
+  }
+  const int pad = wlo >= whi ? 0 : a.flat_pad;
   const int w0 = lane < a.S ? flat_span(L0, a.Lmax, pad) : 0;
   int W = wave_sum_i(w0);                       // total span
   for (int c = 64; c < a.S; c += 64) {

@@ -30,6 +30,24 @@ __device__ __forceinline__ int wave_sum_i(int x) {
   return x;
 }
 
+__device__ __forceinline__ int wave_min_i(int x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const int y = __shfl_xor(x, o, 64);
+    x = y < x ? y : x;
+  }
+  return x;
+}
+
+__device__ __forceinline__ int wave_max_i(int x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const int y = __shfl_xor(x, o, 64);
+    x = y > x ? y : x;
+  }
+  return x;
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ int wave_incl_scan_i(int x) {
   const int lane = threadIdx.x & 63;

@@ -138,10 +138,13 @@ __global__ __launch_bounds__(kThreads) void merge_rows(MergeArgs a) {
 
 // Merge after a balanced-partition attention call: row (s, t, h)'s partials
 // fill its slots 0 .. n-1, n = flat_n[s] as written by the attention call (0
-// for an empty window).  Wave w requests slot w together with n, before n
-// is known (slot w < P lies inside the workspace either way; slots at or
-// past n are dropped), so rows of up to four partials take one round trip.
-template <int D>
+// for an empty window).  Wave w requests slots w, w+4, .., w+4(U-1)
+// together with n, before n is known (slots below P lie inside the
+// workspace either way; those at or past n are dropped), so rows of up to
+// 4U partials take one round trip.  The host sizes U from the partials a
+// sequence of the batch's mean window gets (P / S): one for batches of
+// about a piece per sequence, four for sixteen pieces per sequence.
+template <int D, int U>
 __global__ __launch_bounds__(kThreads) void merge_rows_flat(MergeArgs a) {
   constexpr int V = D / 64;
   __shared__ float red_o[4][D];
@@ -166,10 +169,15 @@ __global__ __launch_bounds__(kThreads) void merge_rows_flat(MergeArgs a) {
 #pragma unroll
     for (int e = 0; e < V; ++e) oj[e] = src[e];
   };
-  float m0 = -INFINITY, l0 = 0.f, o0[V];
+  float m0[U], l0[U], o0[U][V];
 #pragma unroll
-  for (int e = 0; e < V; ++e) o0[e] = 0.f;
-  if (wave < a.P) load(wave, m0, l0, o0);
+  for (int u = 0; u < U; ++u) {
+    m0[u] = -INFINITY;
+    l0[u] = 0.f;
+#pragma unroll
+    for (int e = 0; e < V; ++e) o0[u][e] = 0.f;
+    if (wave + 4 * u < a.P) load(wave + 4 * u, m0[u], l0[u], o0[u]);
+  }
   // (P == 0: an empty cache, for which the attention call writes nothing)
   const int n = a.P > 0 ? a.flat_n[row / a.TH] : 0;
 
@@ -191,8 +199,10 @@ __global__ __launch_bounds__(kThreads) void merge_rows_flat(MergeArgs a) {
 #pragma unroll
     for (int e = 0; e < V; ++e) acc[e] = fmaf(w, oj[e], acc[e]);
   };
-  if (wave < n) take(m0, l0, o0);
-  for (int j = wave + 4; j < n; j += 4) {
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (wave + 4 * u < n) take(m0[u], l0[u], o0[u]);
+  for (int j = wave + 4 * U; j < n; j += 4) {
     float mj, lj, oj[V];
     load(j, mj, lj, oj);
     take(mj, lj, oj);
@@ -230,6 +240,15 @@ __global__ __launch_bounds__(kThreads) void merge_rows_flat(MergeArgs a) {
       if (gated) x *= 1.0f / (1.0f + __expf(-gt[e]));
       out[e] = x;
     }
+  }
+}
+
+template <int U>
+void launch_merge_flat(const MergeArgs& a, int D, dim3 grid, hipStream_t st) {
+  switch (D) {
+    case 64: hipLaunchKernelGGL((merge_rows_flat<64, U>), grid, dim3(kThreads), 0, st, a); break;
+    case 128: hipLaunchKernelGGL((merge_rows_flat<128, U>), grid, dim3(kThreads), 0, st, a); break;
+    default: hipLaunchKernelGGL((merge_rows_flat<256, U>), grid, dim3(kThreads), 0, st, a); break;
   }
 }
 
@@ -273,11 +292,14 @@ static int merge_common(const float* part, const int32_t* seq_lens, const int32_
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   dim3 grid((unsigned)rows);
   if (a.flat) {
-    switch (D) {
-      case 64: hipLaunchKernelGGL(merge_rows_flat<64>, grid, dim3(kThreads), 0, st, a); break;
-      case 128: hipLaunchKernelGGL(merge_rows_flat<128>, grid, dim3(kThreads), 0, st, a); break;
-      default: hipLaunchKernelGGL(merge_rows_flat<256>, grid, dim3(kThreads), 0, st, a); break;
-    }
+    // partials of a sequence of the mean window: about P / S
+    const int64_t per = (P + S - 1) / S;
+    if (per <= 4)
+      launch_merge_flat<1>(a, D, grid, st);
+    else if (per <= 8)
+      launch_merge_flat<2>(a, D, grid, st);
+    else
+      launch_merge_flat<4>(a, D, grid, st);
   } else if (P <= 16)
     launch_merge<4>(a, D, grid, st);
   else if (P <= 32)

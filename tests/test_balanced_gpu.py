@@ -206,3 +206,15 @@ def test_full_size_int8_batch():
     dev = to_dev(inp)
     for chunk in (WORKLOADS["i8_batch"].chunk, 0):
         assert_parity(run_gpu(inp, chunk, dev=dev), ref, f"i8_batch chunk={chunk}")
+
+
+@pytest.mark.parametrize("kv", ["f16", "i8"])
+def test_equal_windows_and_merge_depths(kv):
+    # windows all of one length (empty ones aside) take no pad; piece counts
+    # from under one to 64 per sequence cover every merge prefetch depth
+    D = 128
+    for lens in ([777] * 4, [777, 0, 777, 777], [1] * 4):
+        inp = make_case(4, 2, 16, 4, D, 777, lens, kv=kv, seed=101 + lens[1])
+        ref = oracle(inp)
+        for P in (1, 3, 4, 13, 24, 40, 256):
+            assert_parity(run_gpu(inp, -P), ref, f"equal windows kv={kv} lens={lens} P={P}")
