@@ -422,13 +422,15 @@ def measure_tq(workload, chunk, steps, warmup, dev, copies_arg=0):
 
 
 def measure_attention(name, chunk, steps, warmup, dev, gate=False, copies=0, cold=20,
-                      with_stream_read=True):
+                      with_stream_read=True, sort_ids=True):
     """One attention workload on the GPU: seeded inputs resident in HBM (as
     many copies as keep successive steps out of the last-level cache), K
     steps of attention + merge back to back (wall clock bracketed by device
     synchronisation), the chunk kernel alone from HIP events around bursts of
     back-to-back launches on its stream, single steps between their own
-    events, cold steps, and a plain streaming read of the same bytes.
+    events, cold steps, and a plain streaming read of the same bytes.  With
+    sort_ids False a gathered workload's ids keep the order they were drawn
+    in (no counter record applies then: traffic is None).
     Returns (result dict, inputs)."""
     import numpy as np
     import torch
@@ -438,7 +440,7 @@ def measure_attention(name, chunk, steps, warmup, dev, gate=False, copies=0, col
     w = WORKLOADS[name]
     chunk = w.chunk if chunk is None else chunk
     t_gen = time.perf_counter()
-    inp = make_inputs(name)
+    inp = make_inputs(name, sort_ids=sort_ids)
     step_bytes = kv_bytes(inp)
     sh = inp.shape
     print(f"[bench] {name}: inputs drawn in {time.perf_counter() - t_gen:.1f} s, "
@@ -556,7 +558,7 @@ def measure_attention(name, chunk, steps, warmup, dev, gate=False, copies=0, col
         del scratch
 
     achieved = step_bytes / attn_mean_s / 1e9
-    traffic = load_traffic(name)
+    traffic = load_traffic(name) if sort_ids or inp.ids is None else None
     res = {
         "value": round(step_bytes / (wall / K) / 1e9, 2),
         "ms_per_step": round(wall / K * 1e3, 5),
@@ -673,6 +675,8 @@ def main():
     ap.add_argument("--gate", action="store_true",
                     help="merge with the output gate (gate rows interleaved with the query)")
     ap.add_argument("--copies", type=int, default=0, help="input replicas to rotate through")
+    ap.add_argument("--unsorted-ids", action="store_true",
+                    help="gathered workloads: ids in the order drawn instead of ascending")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (HBM counter calibration)")
     ap.add_argument("--launch-floor", action="store_true",
@@ -711,7 +715,8 @@ def main():
     w = WORKLOADS[args.workload]
     chunk = -args.pieces if args.pieces > 0 else args.chunk
     m, inp = measure_attention(args.workload, chunk, args.steps, args.warmup, dev,
-                               gate=args.gate, copies=args.copies)
+                               gate=args.gate, copies=args.copies,
+                               sort_ids=not args.unsorted_ids)
     sh = inp.shape
     res = {
         "metric": "decode-attention effective KV HBM GB/s (% of peak) and us/step, 1 MI355X",
@@ -737,7 +742,8 @@ def main():
                    "Hk": sh["Hk"], "D": sh["D"], "Lmax": sh["Lmax"], "budget": sh["B"],
                    "kv": inp.kv, "chunk": m["chunk"], "kv_bytes_per_step": m["kv_bytes_per_step"],
                    "input_copies_rotated": m["input_copies_rotated"],
-                   "output_gate": bool(args.gate), "description": w.description},
+                   "output_gate": bool(args.gate), "ids_sorted": not args.unsorted_ids,
+                   "description": w.description},
         "roofline": m["roofline"],
     }
     if not args.no_cpu_baseline:
@@ -748,14 +754,21 @@ def main():
         # every other configuration, measured the same way with fewer steps
         # (no CPU baseline); the line's value stays the named workload's
         res["workloads"] = {}
-        for name in WORKLOAD_ORDER:
-            if name == args.workload:
+        # gathered workloads once more with their ids in the order drawn
+        # (the selection emits them ascending, which the named line uses)
+        runs = [(n, True) for n in WORKLOAD_ORDER]
+        runs += [(n, False) for n in WORKLOAD_ORDER if WORKLOADS[n].budget > 0]
+        for name, sort_ids in runs:
+            if name == args.workload and sort_ids != args.unsorted_ids:
                 continue
             o, _ = measure_attention(name, None, min(args.steps, 100), min(args.warmup, 10), dev,
-                                     cold=10)
+                                     cold=10, sort_ids=sort_ids)
             r = o["roofline"]
-            res["workloads"][name] = {
-                "description": WORKLOADS[name].description, "chunk": o["chunk"],
+            key = name if sort_ids else name + "_unsorted_ids"
+            res["workloads"][key] = {
+                "description": WORKLOADS[name].description +
+                               ("" if sort_ids else "; ids in the order drawn"),
+                "chunk": o["chunk"],
                 "kv_bytes_per_step": o["kv_bytes_per_step"], "us_per_step": o["us_per_step"],
                 "step_us_p10_p50_p90": o["step_us_p10_p50_p90"],
                 "cold_step_us_p10_p50_p90": o["cold_step_us_p10_p50_p90"],

@@ -301,6 +301,18 @@ def test_full_size_workload(name):
         assert_parity(got, ref, f"{name} chunk={chunk}")
 
 
+def test_full_size_budgeted_ids_in_drawn_order():
+    # the budgeted workload with its ids in the order drawn (not ascending),
+    # in the bench's launch configuration, every output element
+    w = WORKLOADS["i8_budget"]
+    inp = make_inputs("i8_budget", sort_ids=False)
+    assert not all(np.all(np.diff(inp.ids[s, t]) > 0) for s in range(inp.ids.shape[0])
+                   for t in range(inp.ids.shape[1]))
+    print("[gpu] full-size i8_budget, ids unsorted: oracle", flush=True)
+    ref = oracle(inp)
+    assert_parity(run_gpu(inp, chunk=w.chunk), ref, "i8_budget unsorted ids")
+
+
 @pytest.mark.parametrize("kv", ["f16", "i8"])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("G,T", [(8, 8), (10, 4), (16, 5)])
