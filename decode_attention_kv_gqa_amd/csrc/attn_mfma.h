@@ -1065,20 +1065,21 @@ __global__ __launch_bounds__(64 * NW, (attn_occupancy<D, I8, NRB>())) void attn_
   using Q = QSlots<D, NRB, NW>;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  // int8 rows with a piece count divisible by the 8 XCDs: pieces vary
-  // fastest within groups of eight, so every KV head (and row block) of a
-  // piece runs on the same XCD and the int8 scale lines the heads share
-  // (both heads' scales of a cell sit in one 16-byte run) meet in one L2,
-  // as the split grid's sequence-fastest order does; otherwise the KV head
-  // varies fastest.
+  // Piece order.  With a piece count divisible by the 8 XCDs, for int8 rows
+  // or fewer than 8 (KV head, row block) pairs: XCD x (workgroup id mod 8)
+  // takes the contiguous pieces [x P/8, (x+1) P/8) with every KV head and
+  // row block of each (their ids differ by multiples of 8), so the scale
+  // lines the heads of a cell share (int8) and the rows around a piece
+  // boundary meet in one L2.  Otherwise (f16 with 8 or more pairs, or P not
+  // a multiple of 8) the KV head varies fastest: XCD x streams the same
+  // heads of every piece.
   int id = blockIdx.x;
   int g, rbl, j;
-  if (I8 && a.P % 8 == 0) {
-    const int per = 8 * a.Hk * a.nrb;
-    const int rem = id % per;
-    j = id / per * 8 + rem % 8;
-    g = rem / 8 % a.Hk;
-    rbl = rem / 8 / a.Hk;
+  if (a.P % 8 == 0 && (I8 || a.Hk * a.nrb < 8)) {
+    const int li = id / 8;
+    g = li % a.Hk;
+    rbl = li / a.Hk % a.nrb;
+    j = (id % 8) * (a.P / 8) + li / (a.Hk * a.nrb);
   } else {
     g = id % a.Hk;
     id /= a.Hk;

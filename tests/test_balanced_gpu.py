@@ -175,11 +175,12 @@ def test_static_step_takes_the_balanced_partition():
         assert_parity(out.cpu().numpy(), oracle(inp), f"static balanced P={P}")
 
 
-@pytest.mark.parametrize("kv,H,Hk,D", [("i8", 24, 2, 256), ("f16", 32, 8, 128), ("i8", 16, 4, 64)])
+@pytest.mark.parametrize("kv,H,Hk,D", [("i8", 24, 2, 256), ("f16", 32, 8, 128), ("i8", 16, 4, 64),
+                                        ("f16", 24, 2, 256), ("i8", 32, 8, 128)])
 def test_balanced_keyword_on_uneven_batches(kv, H, Hk, D):
     # chunk="balanced": the piece count the library picks (256 workgroups;
-    # int8 with a piece count divisible by 8 puts a piece's KV heads on one
-    # XCD)
+    # int8 with a piece count divisible by 8 gives each XCD a contiguous
+    # eighth of the pieces, every KV head of each)
     rng = np.random.default_rng(91)
     lens = rng.integers(0, 3000, size=24)
     lens[[2, 9]] = 0
