@@ -3,6 +3,9 @@ grid-style tests do not pin one by one (sequence counts that are and are not
 multiples of 8, 1-4 KV heads, groups of 1-20 heads, 1-4 causal query tokens,
 head dims 64/128/256, f16 and int8 rows, dense or gathered through a budget
 of ids, automatic or odd split sizes, lengths from 0 to past the capacity).
+A second sweep covers the balanced partition (a negative chunk, or
+"balanced"): batches of up to 70 sequences, some with every window of one
+length, piece counts that are and are not multiples of 8.
 Each case compares every output element with the fp64 oracle to the same
 bar as the other parity tests (tests/conftest.py)."""
 import numpy as np
@@ -18,6 +21,7 @@ torch = pytest.importorskip("torch")
 
 N_CASES = 128
 N_LONG = 32
+N_BALANCED = 48
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -46,6 +50,29 @@ def draw_case(i, long=False):
                 budget=budget, chunk=chunk, seed=seed)
 
 
+def draw_balanced(i):
+    """Case i of the balanced-partition sweep (dense windows only)."""
+    seed = 33000 + i
+    rng = np.random.default_rng(seed)
+    S = int(rng.choice([1, 2, 3, 5, 8, 13, 32, 70]))
+    T = int(rng.integers(1, 5))
+    Hk = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.integers(1, 17))
+    D = int(rng.choice([64, 128, 256]))
+    kv = "i8" if rng.random() < 0.5 else "f16"
+    Lmax = int(rng.integers(1, 801 if S >= 32 else 3001))
+    if rng.random() < 0.25:                          # one window length (no pad)
+        lens = np.full(S, int(rng.integers(1, Lmax + 1)))
+        lens[rng.random(S) < 0.2] = 0
+    else:
+        lens = rng.integers(0, Lmax + 4, size=S)
+    u = rng.random()
+    chunk = ("balanced" if u < 0.25 else -8 * int(rng.integers(1, 33)) if u < 0.55
+             else -int(rng.integers(1, 401)))
+    return dict(S=S, T=T, Hk=Hk, G=G, D=D, kv=kv, Lmax=Lmax, lens=[int(x) for x in lens],
+                budget=0, chunk=chunk, seed=seed)
+
+
 def run_case(c, i):
     import decode_attention_kv_gqa_amd as gq
     inp = make_case(c["S"], c["T"], c["G"] * c["Hk"], c["Hk"], c["D"], c["Lmax"], c["lens"],
@@ -71,3 +98,10 @@ def test_random_long_window(i):
     """Windows of 700-4000 cells: several tiles per wave, the last one
     requesting nothing past the split."""
     run_case(draw_case(i, long=True), i)
+
+
+@pytest.mark.parametrize("i", range(N_BALANCED))
+def test_random_balanced(i):
+    """Balanced partition: pieces crossing sequence boundaries, empty and
+    equal windows, row blocks, both piece orders."""
+    run_case(draw_balanced(i), i)
