@@ -119,15 +119,18 @@ inline size_t flat_n_offset_floats(const Shape& s, int64_t P) {
 
 // Virtual cells charged for each non-empty window in the balanced
 // partition: the cost of starting a sequence inside a workgroup, as the
-// cells that stream in that time.  64 KB of K + V rows of one KV head per
-// sequence start for f16 rows, 128 KB for int8 rows, whose tiles cost more
-// arithmetic to drain and refill (measured best: f16 batch 32 KB 58.2-58.5,
-// 64 KB 57.5-57.6, 128 KB 57.6-57.7 us; int8 uneven batch 32 KB 57.0,
-// 64 KB 56.1, 128 KB 54.8-55.0, 256 KB 56.0 us).
+// cells that stream in that time.  f16 rows: 64 KB of K + V rows of one KV
+// head per sequence start (f16 batch, head_dim 128: 32 KB 58.2-58.5, 64 KB
+// 57.5-57.6, 128 KB 57.6-57.7 us).  int8 rows, whose tiles cost more
+// arithmetic to drain and refill: 256 cells whatever the head_dim (int8
+// batch, head_dim 256: 128 cells 54.9, 256 cells 53.3-53.6, 384 cells
+// 53.3-53.8 us; head_dim 128: 256 cells 43.2, 512 cells 45.0-45.2, 768
+// cells 47.8-47.9 us).
 constexpr int64_t kFlatPadBytes = 64 * 1024;
+constexpr int64_t kFlatPadCellsI8 = 256;
 inline int flat_pad_cells(const Shape& s) {
-  const int64_t cell = 2 * (int64_t)s.D * (s.i8 ? 1 : 2);   // K + V bytes of one KV head
-  const int64_t pad = (s.i8 ? 2 : 1) * kFlatPadBytes / cell;
+  const int64_t cell = 4 * (int64_t)s.D;      // K + V bytes of one KV head, f16
+  const int64_t pad = s.i8 ? kFlatPadCellsI8 : kFlatPadBytes / cell;
   return (int)((pad + 127) / 128 * 128);      // whole 128-cell units
 }
 

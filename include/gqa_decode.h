@@ -149,9 +149,9 @@ int gqa_decode_auto_pieces(int S, int T, int Lmax, int H, int Hk, int D, int kv_
  *             batches of uneven lengths: the windows of all S sequences are
  *             laid end to end, each non-empty one preceded by a fixed number
  *             of virtual cells that stand for the cost of starting a
- *             sequence (64 KB of its K + V rows for f16, 128 KB for int8:
- *             128 cells for f16 head_dim 128, 256 for int8 head_dim 256;
- *             none when every non-empty window has the same length),
+ *             sequence (f16: 64 KB of its K + V rows, 128 cells at
+ *             head_dim 128; int8: 256 cells; none when every non-empty
+ *             window has the same length),
  *             and the total is cut into P near-equal pieces per KV head
  *             (and row block), one workgroup each, that may cross sequence
  *             boundaries; a piece writes one partial per sequence it

@@ -74,7 +74,7 @@ static void check_shape_case(int S, int T, int Lmax, int B, int H, int Hk, int D
     if (bytes < ((i128)1 << 62)) CHECK((i128)got == bytes, "balanced part_bytes %zu vs %lld", got, (long long)bytes);
     const i128 off = (i128)S * T * H * P * (D + 2);
     if (off < ((i128)1 << 62)) CHECK((i128)gqa::flat_n_offset_floats(s, P) == off, "flat_n_offset_floats");
-    const int pad = i8 ? 131072 / (2 * D) : 65536 / (4 * D);
+    const int pad = i8 ? 256 : 65536 / (4 * D);
     CHECK(gqa::flat_pad_cells(s) == (pad + 127) / 128 * 128, "flat_pad_cells");
   }
   CHECK(gqa_decode_part_bytes(S, T, Lmax, ids ? B : 0, H, D, chunk) ==
