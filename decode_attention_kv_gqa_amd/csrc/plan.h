@@ -121,9 +121,7 @@ inline size_t flat_n_offset_floats(const Shape& s, int64_t P) {
 // partition: the cost of starting a sequence inside a workgroup, as the
 // cells that stream in that time.  f16 rows: 64 KB of K + V rows of one KV
 // head per sequence start (f16 batch, head_dim 128: 32 KB 58.2-58.5, 64 KB
-// 57.5-57.6, 128 KB 57.6-57.7 us; head_dim 64: 256 cells 33.1, 128 cells
-// 33.7-33.8 us; head_dim 256: 128 cells 101.1-101.2, 256 cells 102.9-103.1
-// us).  int8 rows, whose tiles cost more
+// 57.5-57.6, 128 KB 57.6-57.7 us).  int8 rows, whose tiles cost more
 // arithmetic to drain and refill: 256 cells whatever the head_dim (int8
 // batch, head_dim 256: 128 cells 54.9, 256 cells 53.3-53.6, 384 cells
 // 53.3-53.8 us; head_dim 128: 256 cells 43.2, 512 cells 45.0-45.2, 768
